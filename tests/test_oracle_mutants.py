@@ -1,0 +1,110 @@
+"""Plant plausible mistakes in the oracle (on the CPU) and check that the
+pins of ``test_oracle.py`` catch every one of them.
+
+A pin suite that still passes on a broken oracle would not be evidence of
+anything; each mutant below is one small, realistic slip (a dropped term, a
+wrong sign, an off-by-one, a transposed operand, a swapped axis)."""
+import numpy as np
+import pytest
+
+from oracle import lla_oracle as O
+from tests import test_oracle as P
+
+
+def _decode_head_variant(mask_extra=0, scale_pow=-0.5, rotate_q=True, key_shift=0,
+                         v_uses_k=False, no_max=False):
+    def decode_head(c_k, c_v, q, W_up_k_t, W_up_v_t, mu_k_t, mu_v_t, pos,
+                    scale=None, base=O.ROPE_BASE, check_latent_v=True):
+        d = q.shape[-1]
+        if scale is None:
+            scale = float(d) ** scale_pow
+        n = max(pos + 1 + mask_extra, 1)
+        k_hat = O.reconstruct(c_k[:n], W_up_k_t, mu_k_t)
+        k_rot = O.rope(k_hat, np.arange(n) + key_shift, base)
+        q_rot = O.rope(q, pos, base) if rotate_q else np.asarray(q, np.float64)
+        s = scale * (k_rot @ q_rot)
+        e = np.exp(s) if no_max else np.exp(s - s.max())
+        p = e / e.sum()
+        if v_uses_k:
+            return p @ O.reconstruct(c_k[:n], W_up_k_t, mu_k_t)
+        return p @ O.reconstruct(c_v[:n], W_up_v_t, mu_v_t)
+    return decode_head
+
+
+def _rope_variant(sign=1.0, interleaved=False, freq_div=1.0):
+    def rope(x, pos, base=O.ROPE_BASE):
+        x = np.asarray(x, np.float64)
+        d = x.shape[-1]
+        theta = base ** (-2.0 * np.arange(d // 2) / d / freq_div)
+        ang = sign * np.asarray(pos, np.float64)[..., None] * theta
+        c, s = np.cos(ang), np.sin(ang)
+        if interleaved:
+            a, b = x[..., 0::2], x[..., 1::2]
+            out = np.empty_like(x)
+            out[..., 0::2], out[..., 1::2] = a * c - b * s, a * s + b * c
+            return out
+        a, b = x[..., : d // 2], x[..., d // 2:]
+        return np.concatenate([a * c - b * s, a * s + b * c], axis=-1)
+    return rope
+
+
+def _decode_2d_interleaved_heads(c_k, c_v, q, W_up_k_t, W_up_v_t, mu_k_t, mu_v_t, pos,
+                                 scale=None, base=O.ROPE_BASE):
+    H, d = q.shape
+    return np.stack([O.decode_head(c_k, c_v, q[h], W_up_k_t[h::H], W_up_v_t[h::H],
+                                   mu_k_t[h::H], mu_v_t[h::H], pos, scale, base)
+                     for h in range(H)])
+
+
+MUTANTS = {
+    "reconstruct_drops_mu": ("reconstruct", lambda c, W, mu: np.asarray(c) @ np.asarray(W).T),
+    "encode_uncentred": ("encode", lambda x, mu, W: np.asarray(x) @ np.asarray(W)),
+    "encode_adds_mu": ("encode", lambda x, mu, W: (np.asarray(x) + mu) @ np.asarray(W)),
+    "rope_negative_angle": ("rope", _rope_variant(sign=-1.0)),
+    "rope_interleaved_pairs": ("rope", _rope_variant(interleaved=True)),
+    "rope_wrong_frequencies": ("rope", _rope_variant(freq_div=2.0)),
+    "mask_one_slot_short": ("decode_head", _decode_head_variant(mask_extra=-1)),
+    "mask_one_slot_long": ("decode_head", _decode_head_variant(mask_extra=1)),
+    "scale_sqrt_d": ("decode_head", _decode_head_variant(scale_pow=0.5)),
+    "query_not_rotated": ("decode_head", _decode_head_variant(rotate_q=False)),
+    "keys_rotated_one_late": ("decode_head", _decode_head_variant(key_shift=1)),
+    "values_from_key_codec": ("decode_head", _decode_head_variant(v_uses_k=True)),
+    "loop_slice_reversed": ("loop_slice",
+                            lambda v, t, width: np.asarray(v, np.float64)[
+                                ..., (np.shape(v)[-1] // width - 1 - t) * width:
+                                (np.shape(v)[-1] // width - t) * width]),
+    "ratio_missing_factor_two": ("compression_ratio",
+                                 lambda T, d, rk, rv, heads=1, variant="per_head":
+                                 P.Fraction(T * d * (heads if variant == "2d" else 1), rk + rv)),
+    "teacher_cache_one_axis": ("teacher_cache_scalars",
+                               lambda T, L, H, d, n: T * L * H * d * n),
+    "offset_slot_head_swapped": ("store_offset",
+                                 lambda shape, b, l, j, h, k:
+                                 (((b * shape[1] + l) * shape[3] + h) * shape[2] + j) * shape[4] + k),
+    "2d_heads_interleaved": ("decode_2d", _decode_2d_interleaved_heads),
+    "bf16_truncates": ("bf16_round",
+                       lambda x: np.sign(x) * np.ldexp(np.floor(np.ldexp(np.abs(x), 8 - np.frexp(x)[1])),
+                                                      np.frexp(x)[1] - 8)),
+}
+
+
+def _pins_fail():
+    failed = []
+    for pin in P.PINS:
+        try:
+            pin()
+        except Exception:  # an assertion or a crash both reveal the mutant
+            failed.append(pin.__name__)
+    return failed
+
+
+def test_unmutated_oracle_passes_all_pins():
+    assert _pins_fail() == []
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS))
+def test_mutant_is_caught(name, monkeypatch):
+    attr, fn = MUTANTS[name]
+    monkeypatch.setattr(O, attr, fn)
+    failed = _pins_fail()
+    assert failed, f"mutant {name} passed every pin"
