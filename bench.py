@@ -1,0 +1,244 @@
+"""Decode-attention throughput of the LLA hot path on one MI355X.
+
+One step = what one generated token costs every sequence in the store:
+D*T decode-attention calls in loop-major order (for t: for layer), each
+reading that layer's whole latent slab for all B sequences, then D encode
+appends writing the new token's latents (slot N-1, overwritten in steady
+state).  Inputs are synthetic and resident in HBM before timing starts.
+
+Prints one JSON line (rank 0, N = 1 GPU):
+  value      = B / step time  (tokens/s, all sequences)
+  roofline   = algorithmic bytes of one decode call / its average duration,
+               HIP events on the launch stream over the timed region,
+               against 8 TB/s
+  cpu_baseline = the fp64 oracle timed on a bounded sample on host cores
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "LLA decode-attn tokens/s at B=768, 4k ctx, ρ=21.3 + % of HBM roofline"
+HBM_PEAK_GBS = 8000.0
+KERNEL_SRC = os.path.join(ROOT, "looped_transformer_decode_amd", "csrc", "decode_mfma.hip")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_mfma_extreme_batch_traffic.json")
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=5)
+    ap.add_argument("--warmup", type=int, default=2)
+    ap.add_argument("--workload", default="extreme_batch_b768_ctx4k")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0,
+                    help="budget of the oracle timing sample (0 disables it)")
+    ap.add_argument("--no-encode", action="store_true", help=argparse.SUPPRESS)
+    return ap.parse_args()
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def algorithmic_bytes(w, pos_plus_one: int) -> int:
+    """Bytes one decode call must move: the latent slab slots 0..pos of
+    every sequence, the queries and outputs, and W_up,t / mu_t."""
+    store = w.B * pos_plus_one * w.store_heads * w.R * w.elt_bytes
+    q_out = 2 * w.B * w.H * w.d * 4
+    rows = w.H * w.d
+    codec = rows * w.R * w.elt_bytes + 2 * rows * 4
+    return store + q_out + codec
+
+
+def traffic_for_current_kernel():
+    """HBM bytes per launch from the committed rocprofv3 counter summary,
+    or None when absent or taken on a different kernel source."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            t = json.load(f)
+        src = hashlib.sha256(open(KERNEL_SRC, "rb").read()).hexdigest()
+        if t.get("kernel_sha256") != src:
+            return None
+        return t.get("hbm_bytes_per_launch")
+    except (OSError, ValueError):
+        return None
+
+
+def cpu_baseline(w, codec, budget_s: float):
+    """Oracle decode of the (layer 0, loop 0) call, one sequence at a time
+    until the time budget is spent; scaled to tokens/s of the whole step."""
+    from threadpoolctl import threadpool_info
+
+    from oracle import lla_oracle as O
+    from synth.workloads import store_slab
+    layer, t = 0, 0
+    q = codec.q(layer, t, 4)
+    wk, wv = codec.w_up("k", layer, t), codec.w_up("v", layer, t)
+    mk = O.loop_slice(codec.mu("k", layer), t, w.width)
+    mv = O.loop_slice(codec.mu("v", layer), t, w.width)
+    done, spent = 0, 0.0
+    while spent < budget_s and done < w.B:
+        b = done % 4
+        slab = store_slab(w, b, layer)
+        t0 = time.perf_counter()
+        if w.variant == "2d":
+            O.decode_2d(slab[:, 0, :w.r_k], slab[:, 0, w.r_k:], q[b], wk[0], wv[0], mk[0], mv[0],
+                        w.N - 1)
+        else:
+            O.decode(slab[..., :w.r_k], slab[..., w.r_k:], q[b], wk, wv, mk, mv, w.N - 1)
+        spent += time.perf_counter() - t0
+        done += 1
+    per_seq = spent / done
+    t_step = per_seq * w.B * w.D * w.T
+    threads = max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
+    return {"value": w.B / t_step, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "sample": f"{done} sequence(s) x {w.H} heads of the (layer 0, loop 0) call at pos "
+                      f"{w.N - 1}, {spent:.1f} s; scaled x{w.B}/{done} sequences x "
+                      f"{w.D * w.T} calls per step"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py measures one GPU: this build has no multi-GPU path "
+              "(the hot path shards by sequence with no exchange; see DESIGN.md).",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import looped_transformer_decode_amd as L
+    from synth import gen
+    from synth.device import fill_hash_normal
+    from synth.workloads import TID_Q, TID_X_K, TID_X_V, WORKLOADS, Codec, store_key
+
+    w = WORKLOADS[args.workload]
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    log(f"[bench] workload {w.name}: B={w.B} D={w.D} N={w.N} H={w.H} d={w.d} T={w.T} "
+        f"r_k={w.r_k} r_v={w.r_v} {w.variant} {w.dtype}; store {w.store_bytes / 1e9:.2f} GB")
+
+    store = L.LatentStore(w.variant, w.dtype, batch=w.B, layers=w.D, max_ctx=w.N, heads=w.H,
+                          d_head=w.d, loops=w.T, r_k=w.r_k, r_v=w.r_v, device=dev)
+    t0 = time.time()
+    fill_hash_normal(store.tensor, store_key(w))
+    torch.cuda.synchronize()
+    log(f"[bench] store filled in {time.time() - t0:.1f} s")
+    rope = L.rope_table(store, dev)
+    codec = Codec(w)
+    tdt = store.torch_dtype
+    is2d = w.variant == "2d"
+    width = w.width
+
+    def up(x, dtype):
+        x32 = np.asarray(x, np.float32)
+        if dtype == torch.float32:
+            return torch.from_numpy(x32).to(dev)
+        return torch.from_numpy(gen.f32_to_bf16_bits(x32).view(np.int16)).to(dev).view(tdt)
+
+    # codec tensors of every (layer, loop)
+    wk, wv, mk, mv = {}, {}, {}, {}
+    wdk, wdv, muk, muv = [], [], [], []
+    for l in range(w.D):
+        for t in range(w.T):
+            a, b_ = codec.w_up("k", l, t), codec.w_up("v", l, t)
+            wk[l, t] = up(a.reshape(-1, w.r_k) if is2d else a, tdt)
+            wv[l, t] = up(b_.reshape(-1, w.r_v) if is2d else b_, tdt)
+            m1 = codec.mu("k", l)[:, t * width:(t + 1) * width]   # mu_t: loop-t block
+            m2 = codec.mu("v", l)[:, t * width:(t + 1) * width]
+            mk[l, t] = up(m1.reshape(-1) if is2d else m1, torch.float32)
+            mv[l, t] = up(m2.reshape(-1) if is2d else m2, torch.float32)
+        wdk.append(up(codec.w_down("k", l)[0] if is2d else codec.w_down("k", l), tdt))
+        wdv.append(up(codec.w_down("v", l)[0] if is2d else codec.w_down("v", l), tdt))
+        muk.append(up(codec.mu("k", l)[0] if is2d else codec.mu("k", l), torch.float32))
+        muv.append(up(codec.mu("v", l)[0] if is2d else codec.mu("v", l), torch.float32))
+    q = torch.empty((w.D, w.T, w.B, w.H, w.d), dtype=torch.float32, device=dev)
+    fill_hash_normal(q, gen.stream_key(w.seed, TID_Q))
+    K = w.T * width
+    xshape = (w.D, w.B, w.n_new, K) if is2d else (w.D, w.B, w.n_new, w.H, K)
+    xk = torch.empty(xshape, dtype=tdt, device=dev)
+    xv = torch.empty(xshape, dtype=tdt, device=dev)
+    fill_hash_normal(xk, gen.stream_key(w.seed, TID_X_K))
+    fill_hash_normal(xv, gen.stream_key(w.seed, TID_X_V))
+    pos = torch.full((w.B,), w.N - 1, dtype=torch.int32, device=dev)
+    start = torch.full((w.B,), w.N - w.n_new, dtype=torch.int32, device=dev)
+    out = torch.empty((w.B, w.H, w.d), dtype=torch.float32, device=dev)
+    ws = L.workspace(store)
+    decode = L.lla2d_decode_attn if is2d else L.lla_decode_attn
+    encode = L.lla2d_encode_append if is2d else L.lla_encode_append
+    stream = torch.cuda.current_stream()
+    log(f"[bench] path={L.lla_decode_path(store)} splits={L.lla_decode_auto_splits(store)}")
+
+    def step(events=None):
+        for t in range(w.T):
+            for l in range(w.D):
+                if events is not None:
+                    events[0].append(torch.cuda.Event(enable_timing=True))
+                    events[0][-1].record(stream)
+                decode(store, l, t, q[l, t], wk[l, t], wv[l, t], mk[l, t], mv[l, t], pos, rope,
+                       out, ws)
+                if events is not None:
+                    events[1].append(torch.cuda.Event(enable_timing=True))
+                    events[1][-1].record(stream)
+        if not args.no_encode:
+            for l in range(w.D):
+                encode(store, l, xk[l], xv[l], muk[l], muv[l], wdk[l], wdv[l], start)
+
+    for i in range(args.warmup):
+        step()
+        torch.cuda.synchronize()
+        log(f"[bench] warmup step {i + 1}/{args.warmup} done")
+    ev = ([], [])
+    torch.cuda.synchronize()
+    t_start = torch.cuda.Event(enable_timing=True)
+    t_end = torch.cuda.Event(enable_timing=True)
+    t_start.record(stream)
+    for i in range(args.steps):
+        step(ev)
+    t_end.record(stream)
+    torch.cuda.synchronize()
+    ms_step = t_start.elapsed_time(t_end) / args.steps
+    call_ms = np.array([a.elapsed_time(b) for a, b in zip(*ev)])
+    log(f"[bench] {args.steps} steps: {ms_step:.3f} ms/step; decode call mean "
+        f"{call_ms.mean() * 1e3:.1f} us (min {call_ms.min() * 1e3:.1f}, "
+        f"max {call_ms.max() * 1e3:.1f})")
+    value = w.B / (ms_step / 1e3)
+    bytes_call = algorithmic_bytes(w, w.N)
+    achieved = bytes_call / (call_ms.mean() / 1e3) / 1e9
+    res = {
+        "metric": METRIC, "value": round(value, 2), "unit": "tokens/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16"
+        if w.dtype == "bf16" else "f32", "data": "synthetic",
+        "config": {"workload": w.name, "variant": w.variant, "B": w.B, "layers": w.D,
+                   "ctx": w.N, "heads": w.H, "d_head": w.d, "loops": w.T, "r_k": w.r_k,
+                   "r_v": w.r_v, "rho": str(L.lla_compression_ratio(store)),
+                   "calls_per_step": w.D * w.T, "encode_appends_per_step": 0 if args.no_encode
+                   else w.D, "splits": L.lla_decode_auto_splits(store),
+                   "path": L.lla_decode_path(store)},
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "traffic": traffic_for_current_kernel(),
+                     "kernel": "decode_mfma_split + decode_merge (one lla_decode_attn call)",
+                     "bytes_per_launch": bytes_call, "launch_us": round(call_ms.mean() * 1e3, 2)},
+    }
+    if args.cpu_seconds > 0:
+        del store, q, xk, xv
+        torch.cuda.empty_cache()
+        res["cpu_baseline"] = cpu_baseline(w, codec, args.cpu_seconds)
+    else:
+        res["cpu_baseline"] = None
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,196 @@
+/*
+ * lla.h -- C ABI of the Looped Latent Attention (LLA) decode hot path,
+ * built for AMD Instinct MI355X (gfx950).
+ *
+ * Method: "Looped Latent Attention: Cross-Loop KV Compression for Looped
+ * Transformers" (arXiv 2607.15456), Section 3.  For every token, layer and
+ * head the loop-indexed K (and V) vectors x = [x_1; ...; x_T] (Eq. 1) are
+ * stored as one latent c = (x - mu) W_down (Eq. 2).  Decode-time attention
+ * at loop t rebuilds x_hat_t = c W_up,t^T + mu_t (Eq. 3) only as it reads a
+ * slot, applies RoPE after reconstruction at the slot's position (the
+ * rotary phase is shared by all loops; "RoPE and reconstruction"), and
+ * attends causally exactly like the uncompressed model.  LLA-2D ("LLA-2D
+ * variant") keeps one latent per token and layer that decodes all H heads.
+ *
+ * Conventions shared by every entry point
+ *  - Every pointer argument named "device" is device memory owned by the
+ *    caller; the library allocates no device memory, keeps no global
+ *    mutable state and may be called from several host threads.
+ *  - Launching calls are asynchronous on the given stream (0 = the null
+ *    stream).  Nothing on the decode / encode path synchronises the host.
+ *  - All arguments are validated on the host before any launch; an invalid
+ *    call returns a non-zero lla_status_t and launches nothing.  A failed
+ *    launch returns LLA_E_HIP.  No C++ exception crosses this boundary.
+ *  - Store layout (element type = store->dtype):
+ *        store[b][layer][slot][h'][k],  shape [B, D, N, H', r_k + r_v]
+ *    row-major, H' = H (per-head) or 1 (LLA-2D).  Components k in [0, r_k)
+ *    are the K latent, [r_k, r_k + r_v) the V latent.  Slot j holds the
+ *    token at absolute position j.  Offsets are 64-bit (lla_store_offset).
+ *  - RoPE: rotate-half pairs (i, i + d/2), theta_i = rope_base^(-2i/d).
+ *  - Softmax scale: softmax_scale > 0 is used as given; <= 0 selects
+ *    1/sqrt(d_head).
+ */
+#ifndef LLA_H
+#define LLA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  LLA_OK = 0,
+  LLA_E_NULL = 1,        /* a required pointer is NULL                       */
+  LLA_E_SHAPE = 2,       /* a size is non-positive or sizes are inconsistent */
+  LLA_E_DTYPE = 3,       /* unknown element type                             */
+  LLA_E_RANGE = 4,       /* layer / loop / n_new / scale out of range        */
+  LLA_E_WORKSPACE = 5,   /* workspace NULL or smaller than required          */
+  LLA_E_UNSUPPORTED = 6, /* valid request that no kernel here implements    */
+  LLA_E_VARIANT = 7,     /* per-head call on an LLA-2D store or vice versa   */
+  LLA_E_HIP = 8,         /* a HIP runtime call or kernel launch failed       */
+  LLA_E_OVERFLOW = 9     /* a byte count does not fit in size_t / int64      */
+} lla_status_t;
+
+typedef enum { LLA_DT_F32 = 0, LLA_DT_BF16 = 1 } lla_dtype_t;
+typedef enum { LLA_PER_HEAD = 0, LLA_2D = 1 } lla_variant_t;
+
+/* Descriptor of one latent store.  Plain data; the library never keeps it. */
+typedef struct {
+  int32_t variant;   /* lla_variant_t                                          */
+  int32_t dtype;     /* lla_dtype_t of the store and of x, W_down, W_up        */
+  int32_t batch;     /* B sequences                                            */
+  int32_t layers;    /* D layers                                               */
+  int32_t max_ctx;   /* N slots per (sequence, layer)                          */
+  int32_t heads;     /* H attention heads (queries and K/V heads alike)        */
+  int32_t d_head;    /* d, even                                                */
+  int32_t loops;     /* T recurrence steps                                     */
+  int32_t r_k;       /* K latent rank                                          */
+  int32_t r_v;       /* V latent rank                                          */
+  float rope_base;   /* RoPE base, e.g. 10000                                  */
+  void *data;        /* device: the store, lla_store_bytes() bytes, caller-owned */
+} lla_store_t;
+
+/* Human-readable name of a status code (static string, never NULL). */
+const char *lla_status_string(lla_status_t status);
+
+/* Checks a descriptor's fields (not its data pointer).  LLA_OK or the
+ * first error found. */
+lla_status_t lla_store_check(const lla_store_t *store);
+
+/* Bytes of the latent store: B*D*N*H'*(r_k+r_v)*sizeof(dtype).
+ * Returns 0 for an invalid descriptor or when the count overflows. */
+size_t lla_store_bytes(const lla_store_t *store);
+
+/* Element offset of store[b][layer][pos][head][comp] (64-bit).  head is
+ * the stored head (must be 0 for LLA-2D).  Returns -1 when any index is
+ * out of range or the descriptor is invalid.  Host-only, no device access. */
+int64_t lla_store_offset(const lla_store_t *store, int32_t b, int32_t layer,
+                         int32_t pos, int32_t head, int32_t comp);
+
+/* Exact compression ratio of the store as a reduced fraction num/den
+ * (paper Sec. 3 Eq. 4): per-head 2*T*d/(r_k+r_v); LLA-2D 2*T*H*d/(r_k+r_v). */
+lla_status_t lla_compression_ratio(const lla_store_t *store, int64_t *num,
+                                   int64_t *den);
+
+/* Size of the RoPE table the decode calls read, for store's (N, d, base). */
+size_t lla_rope_table_bytes(const lla_store_t *store);
+
+/* Fills a HOST buffer of lla_rope_table_bytes() bytes with the RoPE table
+ * (computed in double precision, rounded once); the caller copies it to
+ * device memory and passes that copy to the decode calls.  The contents are
+ * opaque: cos/sin of pos*theta_i for every slot, in the element orders the
+ * decode kernels read.  Error if bytes is smaller than required. */
+lla_status_t lla_rope_table_fill(const lla_store_t *store, void *host_table,
+                                 size_t bytes);
+
+/* ---------------------------------------------------------------------------
+ * Append-time encoder (paper Sec. 3 Eq. 2): for every new token
+ *     c = (x - mu) W_down
+ * for the K and V axes separately, rounded to the store type (nearest,
+ * ties even) and written to store[b][layer][start_pos[b] + j][h][...].
+ * Call it once a token has finished all T loops (Eq. 2 needs the whole
+ * T-loop stack).  n_new == 0 is a no-op.
+ *
+ * Per-head (lla_encode_append):
+ *   x_k, x_v     device, store dtype, [B, n_new, H, T*d]  (x_1..x_T stacked, Eq. 1)
+ *   mu_k, mu_v   device, float32,     [H, T*d]
+ *   w_down_k     device, store dtype, [H, T*d, r_k]
+ *   w_down_v     device, store dtype, [H, T*d, r_v]
+ * LLA-2D (lla2d_encode_append): H' = 1 and the stack is [t][h][d]:
+ *   x_k, x_v     [B, n_new, T*H*d];  mu_* [T*H*d];  w_down_* [T*H*d, r]
+ *   start_pos    device, int32, [B]; slots outside [0, N) are not written.
+ * ------------------------------------------------------------------------- */
+lla_status_t lla_encode_append(const lla_store_t *store, int32_t layer,
+                               const void *x_k, const void *x_v,
+                               const float *mu_k, const float *mu_v,
+                               const void *w_down_k, const void *w_down_v,
+                               const int32_t *start_pos, int32_t n_new,
+                               hipStream_t stream);
+lla_status_t lla2d_encode_append(const lla_store_t *store, int32_t layer,
+                                 const void *x_k, const void *x_v,
+                                 const float *mu_k, const float *mu_v,
+                                 const void *w_down_k, const void *w_down_v,
+                                 const int32_t *start_pos, int32_t n_new,
+                                 hipStream_t stream);
+
+/* Workspace bytes a decode call needs for n_splits context splits
+ * (0 = the automatic choice lla_decode_attn would make). */
+size_t lla_decode_workspace_bytes(const lla_store_t *store, int32_t n_splits);
+
+/* The split count lla_decode_attn uses when n_splits == 0. */
+int32_t lla_decode_auto_splits(const lla_store_t *store);
+
+/* ---------------------------------------------------------------------------
+ * Decode-time attention at (layer, loop t) over the latent store
+ * (paper Sec. 3 Eq. 3, "RoPE and reconstruction"): for every sequence b
+ * and head h, the query at position pos[b] attends slots 0..pos[b]:
+ *   k_j = RoPE(c_k,j W_up,k,t^T + mu_k,t, j),  v_j = c_v,j W_up,v,t^T + mu_v,t
+ *   out[b][h] = sum_j softmax_j(scale * RoPE(q[b][h], pos[b]) . k_j) v_j
+ * The current token's own K/V must already be in the store (slot pos[b]).
+ *
+ * Per-head (lla_decode_attn):
+ *   q            device, float32, [B, H, d], before RoPE
+ *   w_up_k_t     device, store dtype, [H, d, r_k]   (W_up,k,t of every head)
+ *   w_up_v_t     device, store dtype, [H, d, r_v]
+ *   mu_k_t       device, float32, [H, d]  (loop-t slice of mu_k)
+ *   mu_v_t       device, float32, [H, d]
+ * LLA-2D (lla2d_decode_attn): w_up_*_t [H*d, r] with rows [h][d];
+ *   mu_*_t [H*d].
+ *   pos          device, int32, [B]; values are clamped into [0, N-1].
+ *   rope_table   device copy of lla_rope_table_fill()'s output.
+ *   out          device, float32, [B, H, d].
+ *   workspace    device, >= lla_decode_workspace_bytes(store, n_splits).
+ *   loop         0 <= loop < T.  Validated; the RoPE phase does not depend
+ *                on it -- W_up,t and mu_t carry the loop.
+ * ------------------------------------------------------------------------- */
+lla_status_t lla_decode_attn(const lla_store_t *store, int32_t layer,
+                             int32_t loop, const float *q,
+                             const void *w_up_k_t, const void *w_up_v_t,
+                             const float *mu_k_t, const float *mu_v_t,
+                             const int32_t *pos, const void *rope_table,
+                             float softmax_scale, float *out, void *workspace,
+                             size_t ws_bytes, int32_t n_splits,
+                             hipStream_t stream);
+lla_status_t lla2d_decode_attn(const lla_store_t *store, int32_t layer,
+                               int32_t loop, const float *q,
+                               const void *w_up_k_t, const void *w_up_v_t,
+                               const float *mu_k_t, const float *mu_v_t,
+                               const int32_t *pos, const void *rope_table,
+                               float softmax_scale, float *out,
+                               void *workspace, size_t ws_bytes,
+                               int32_t n_splits, hipStream_t stream);
+
+/* Name of the kernel family lla_decode_attn / lla2d_decode_attn would
+ * launch for this store ("mfma" fast path or "valu" generic path), or NULL
+ * for an invalid descriptor.  Host-only. */
+const char *lla_decode_path(const lla_store_t *store);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* LLA_H */

@@ -1,0 +1,411 @@
+// Per-head LLA decode for bf16 latent stores on gfx950 (the fast path).
+//
+// What it computes ("Looped Latent Attention: Cross-Loop KV Compression for
+// Looped Transformers", Sec. 3 Eq. 3 and "RoPE and reconstruction"): for
+// sequence b, head h, loop t and every slot j <= pos[b]
+//     s_j = scale * RoPE(q, pos) . RoPE(W_up,k,t c_k,j + mu_k,t, j)
+// followed by an online softmax and the latent-space value average
+// sum_j p_j c_v,j (the merge kernel applies W_up,v,t and mu_v,t once).
+//
+// How.  RoPE is a rotation by j*theta_i of each pair (i, i + d/2), so with
+// phi_j = [cos(j theta); sin(j theta)] in R^d the score is bilinear in the
+// rotary row phi_j and the stored latent c_j:
+//     s_j = phi_j^T G c_j + phi_j^T g0,
+//     G[i, k]       = q'_i W[i, k] + q'_{i+d/2} W[i+d/2, k]
+//     G[i+d/2, k]   = q'_{i+d/2} W[i, k] - q'_i W[i+d/2, k]      (i < d/2)
+// with q' the rotated, scaled query and g0 the same expression with mu_k,t
+// in place of W[:, k].  G is built once per workgroup; per tile of 32 slots
+// one MFMA chain U = G^T Phi^T (rows (head, k), columns = slots, K = d)
+// yields phi_j^T G[:, k] for every slot, and the score is the rank-r_k dot
+// product of U's column with the slot's latent.  Reconstruction, RoPE and
+// the q.k product thereby run on the matrix cores (the K-side work is the
+// same tokens x d x r_k contraction as reconstructing K), leaving the
+// vector ALUs an r_k-term dot, the softmax and the r_v-term value update
+// per (slot, head).  Row order of G^T is chosen so that lane l of a 32x32
+// MFMA output holds all r_k values of slot l%32 for one head: lanes 0-31
+// serve the first head of a pair, lanes 32-63 the second, so no cross-lane
+// reduction is needed anywhere in the slot loop.
+//
+// Data movement.  A workgroup owns (b, head group, context split).  Slot
+// records of the head group are contiguous in HBM; tiles of 32 slots are
+// streamed with buffer loads that write LDS directly (no VGPR staging),
+// three or two tiles deep, plus the matching 8 KB tile of bf16 phi rows.
+// 16-byte chunks are XOR-swizzled by (slot & 7) inside each slot record so
+// that the per-lane record reads (lanes = consecutive slots) hit distinct
+// LDS banks.  Buffer loads past the slab return zeros, so partial tiles
+// never read outside the store.
+#include "lla_device.h"
+#include "lla_internal.h"
+
+namespace lla {
+namespace detail {
+
+typedef __attribute__((__vector_size__(8 * sizeof(short)))) short bf16x8_t;
+typedef __attribute__((__vector_size__(16 * sizeof(float)))) float f32x16_t;
+typedef __attribute__((__vector_size__(4 * sizeof(uint32_t)))) uint32_t u32x4_t;
+#define LDS_AS __attribute__((address_space(3)))
+
+constexpr int kD = 128;             // d_head served by this path
+constexpr int kKSteps = kD / 16;    // k-steps of v_mfma_f32_32x32x16_bf16
+constexpr int kTile = 32;           // slots per tile (MFMA column count)
+constexpr int kPhiTileBytes = kTile * kD * 2;
+constexpr int kLdsMax = 160 * 1024;
+constexpr float kRescaleGap = 8.0f; // log2-domain headroom before rescaling
+
+template <int RK, int RV, int HPW, int NW>
+struct Cfg {
+  static constexpr int HG = HPW * NW;           // heads per workgroup
+  static constexpr int NT = NW * 64;            // threads per workgroup
+  static constexpr int REC = (RK + RV) * 2;     // bytes per (slot, head)
+  static constexpr int CPH = REC / 16;          // 16-byte chunks per head record
+  static constexpr int CPT = HG * CPH;          // chunks per slot of the group
+  static constexpr int TILE_BYTES = kTile * CPT * 16;
+  static constexpr int STAGE_BYTES = TILE_BYTES + kPhiTileBytes;
+  static constexpr int NSTAGE = (kLdsMax / STAGE_BYTES) > 3 ? 3 : (kLdsMax / STAGE_BYTES);
+  static constexpr int LDS_BYTES = NSTAGE * STAGE_BYTES;
+  static constexpr int LOADS_STORE = kTile * CPT / NT;
+  static constexpr int LOADS_PHI = (kPhiTileBytes / 16) / NT;
+  static constexpr int LOADS = LOADS_STORE + LOADS_PHI;
+  static constexpr int PAIRS = HPW / 2;
+  static constexpr int KT = RK / 16;            // 32-row MFMA tiles per head pair
+  static constexpr int CK_CHUNKS = RK / 8;
+  static constexpr int CV_CHUNKS = RV / 8;
+  static_assert(HPW % 2 == 0 && HPW <= 4, "heads per wave: 2 or 4");
+  static_assert(RK % 16 == 0 && RV % 8 == 0, "rank granularity");
+  static_assert(CPT % 8 == 0, "swizzle works on groups of 8 chunks");
+  static_assert((kTile * CPT) % NT == 0 && (kPhiTileBytes / 16) % NT == 0, "load split");
+  static_assert(NSTAGE >= 2, "two LDS stages must fit");
+  static_assert(NSTAGE * LOADS <= 63, "vmcnt range");
+  // LDS used before the pipeline starts: rotated queries + W_up,k,t of the group
+  static_assert(HG * kD * 4 + HG * kD * RK * 2 <= LDS_BYTES, "setup staging");
+  // LDS used by the final cross-lane reduction
+  static_assert(NW * PAIRS * 64 * (RV + 2) * 4 <= LDS_BYTES, "reduction staging");
+};
+
+__device__ __forceinline__ void wait_vm(int n_outstanding_tiles, int loads) {
+  // Constant immediates only: n_outstanding_tiles is 0, 1 or 2.
+  if (n_outstanding_tiles <= 0) {
+    __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
+  } else if (n_outstanding_tiles == 1) {
+    switch (loads) {
+#define LLA_W(n) case n: __builtin_amdgcn_s_waitcnt(waitcnt_vm(n)); break;
+      LLA_W(2) LLA_W(3) LLA_W(4) LLA_W(5) LLA_W(6) LLA_W(7) LLA_W(8) LLA_W(9) LLA_W(10)
+      LLA_W(11) LLA_W(12) LLA_W(13) LLA_W(14) LLA_W(15) LLA_W(16) LLA_W(17) LLA_W(18)
+      LLA_W(19) LLA_W(20) LLA_W(21) LLA_W(22) LLA_W(23) LLA_W(24) LLA_W(25) LLA_W(26)
+      LLA_W(27) LLA_W(28) LLA_W(29) LLA_W(30) LLA_W(31)
+      default: __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
+    }
+  } else {
+    switch (2 * loads) {
+      LLA_W(4) LLA_W(6) LLA_W(8) LLA_W(10) LLA_W(12) LLA_W(14) LLA_W(16) LLA_W(18) LLA_W(20)
+      LLA_W(22) LLA_W(24) LLA_W(26) LLA_W(28) LLA_W(30) LLA_W(32) LLA_W(34) LLA_W(36)
+      LLA_W(38) LLA_W(40) LLA_W(42) LLA_W(44) LLA_W(46) LLA_W(48) LLA_W(50) LLA_W(52)
+      LLA_W(54) LLA_W(56) LLA_W(58) LLA_W(60) LLA_W(62)
+#undef LLA_W
+      default: __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
+    }
+  }
+}
+
+// lgkmcnt(0), other counters untouched.
+constexpr int kWaitLgkm0 = 15 | (7 << 4) | (0 << 8) | (3 << 14);
+
+template <int RK, int RV, int HPW, int NW>
+__global__ __launch_bounds__(NW * 64, 1) void decode_mfma_split(DecodeParams p) {
+#if defined(__HIP_DEVICE_COMPILE__)  // the body uses device-only builtin types
+  using C = Cfg<RK, RV, HPW, NW>;
+  extern __shared__ __attribute__((aligned(16))) char lds[];
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+
+  const int groups = p.H / C::HG;
+  int bid = blockIdx.x;
+  const int s = bid % p.S;
+  bid /= p.S;
+  const int g = bid % groups;
+  const int b = bid / groups;
+  const int h0 = g * C::HG;
+
+  const int pos = min(max(p.pos[b], 0), p.N - 1);
+  const int t0 = s * p.split_len;
+  const int t1 = min(t0 + p.split_len, pos + 1);
+  if (t0 >= t1) {  // split entirely after the query: empty partials
+    for (int i = tid; i < C::HG * (RV + 2); i += C::NT) {
+      const int hl = i / (RV + 2), r = i % (RV + 2);
+      p.ws[((int64_t)(b * p.H + h0 + hl) * p.S + s) * (RV + 2) + r] = (r == 0) ? -INFINITY : 0.f;
+    }
+    return;
+  }
+  const int ntiles = (t1 - t0 + kTile - 1) / kTile;
+
+  // ---- setup: rotated + scaled queries and W_up,k,t of the group in LDS ----
+  float *qr = reinterpret_cast<float *>(lds);                          // [HG][kD]
+  uint16_t *wl = reinterpret_cast<uint16_t *>(lds + C::HG * kD * 4);   // [HG][kD][RK]
+  {
+    const float *rq = p.rope_f32 + (int64_t)pos * kD;  // [kD/2][2] at pos
+    for (int i = tid; i < C::HG * (kD / 2); i += C::NT) {
+      const int hl = i / (kD / 2), ii = i % (kD / 2);
+      const float *qb = p.q + ((int64_t)b * p.H + h0 + hl) * kD;
+      const float c = rq[2 * ii], sn = rq[2 * ii + 1];
+      const float a = qb[ii], bb = qb[ii + kD / 2];
+      qr[hl * kD + ii] = (a * c - bb * sn) * p.scale_log2;
+      qr[hl * kD + ii + kD / 2] = (a * sn + bb * c) * p.scale_log2;
+    }
+    const u32x4_t *wsrc =
+        reinterpret_cast<const u32x4_t *>(reinterpret_cast<const uint16_t *>(p.wk) +
+                                          (int64_t)h0 * kD * RK);
+    u32x4_t *wdst = reinterpret_cast<u32x4_t *>(wl);
+    for (int i = tid; i < C::HG * kD * RK / 8; i += C::NT) wdst[i] = wsrc[i];
+  }
+  __syncthreads();
+
+  // ---- A operands: G^T rows (per head pair) and the mu row block ----
+  const int row = lane & 31, khalf = lane >> 5;
+  bf16x8_t Ak[C::PAIRS][C::KT][kKSteps];
+  bf16x8_t Amu[kKSteps];
+#pragma unroll
+  for (int pp = 0; pp < C::PAIRS; ++pp) {
+#pragma unroll
+    for (int ti = 0; ti < C::KT; ++ti) {
+      const int hip = (row >> 2) & 1;
+      const int k = ti * 16 + ((row >> 3) << 2) + (row & 3);
+      const int hl = wave * HPW + 2 * pp + hip;
+      const float *qh = qr + hl * kD;
+      const uint16_t *wh = wl + hl * kD * RK;
+#pragma unroll
+      for (int st = 0; st < kKSteps; ++st) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const int i = 16 * st + 8 * khalf + e;
+          float gv;
+          if (i < kD / 2) {
+            gv = qh[i] * bf16_bits_to_f32(wh[i * RK + k]) +
+                 qh[i + kD / 2] * bf16_bits_to_f32(wh[(i + kD / 2) * RK + k]);
+          } else {
+            gv = qh[i] * bf16_bits_to_f32(wh[(i - kD / 2) * RK + k]) -
+                 qh[i - kD / 2] * bf16_bits_to_f32(wh[i * RK + k]);
+          }
+          Ak[pp][ti][st][e] = (short)f32_to_bf16_bits(gv);
+        }
+      }
+    }
+  }
+  {
+    // mu rows: row 8*pp + 4*hip (pp < PAIRS) carries head wave*HPW + 2*pp + hip;
+    // an output lane l then finds its head's mu term in accumulator 4*pp.
+    const bool used = ((row & 3) == 0) && ((row >> 3) < C::PAIRS);
+    const int hl = wave * HPW + 2 * (row >> 3) + ((row >> 2) & 1);
+    const float *qh = qr + (used ? hl : 0) * kD;
+    const float *mu = p.muk + (int64_t)(h0 + (used ? hl : 0)) * kD;
+#pragma unroll
+    for (int st = 0; st < kKSteps; ++st) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const int i = 16 * st + 8 * khalf + e;
+        float gv = 0.f;
+        if (used) {
+          gv = (i < kD / 2) ? qh[i] * mu[i] + qh[i + kD / 2] * mu[i + kD / 2]
+                            : qh[i] * mu[i - kD / 2] - qh[i - kD / 2] * mu[i];
+        }
+        Amu[st][e] = (short)f32_to_bf16_bits(gv);
+      }
+    }
+  }
+  __syncthreads();  // the setup LDS area is reused by the pipeline stages
+
+  // ---- tile streaming setup ----
+  const int64_t slab_elems = (int64_t)p.N * p.Hs * p.R;
+  const uint16_t *slab = reinterpret_cast<const uint16_t *>(p.store) +
+                         ((int64_t)b * p.D + p.layer) * slab_elems;
+  const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint16_t *>(slab), (short)0, (int)(slab_elems * 2), 0x00020000);
+  const int phi_tiles = (p.N + kTile - 1) / kTile;
+  const __amdgpu_buffer_rsrc_t rphi = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint16_t *>(p.rope_bf16), (short)0, phi_tiles * kPhiTileBytes, 0x00020000);
+  const uint32_t tok_stride = (uint32_t)p.Hs * p.R * 2;  // bytes per slot in the slab
+  const uint32_t grp_off = (uint32_t)h0 * C::REC;
+  uint32_t voff[C::LOADS_STORE];
+#pragma unroll
+  for (int n = 0; n < C::LOADS_STORE; ++n) {
+    const int P = n * C::NT + tid;           // LDS chunk this lane fills
+    const int tj = P / C::CPT, qq = P % C::CPT;
+    voff[n] = tj * tok_stride + grp_off + (uint32_t)((qq ^ (tj & 7)) * 16);
+  }
+  auto issue = [&](int it, int buf) {
+    char *sb = lds + buf * C::STAGE_BYTES;
+    const uint32_t tile_off = (uint32_t)(t0 + it * kTile) * tok_stride;
+#pragma unroll
+    for (int n = 0; n < C::LOADS_STORE; ++n)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          rs, (LDS_AS void *)(sb + (n * C::NT + wave * 64) * 16), 16, voff[n] + tile_off, 0, 0, 0);
+    const uint32_t phi_off = (uint32_t)(t0 / kTile + it) * kPhiTileBytes;
+#pragma unroll
+    for (int n = 0; n < C::LOADS_PHI; ++n)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          rphi, (LDS_AS void *)(sb + C::TILE_BYTES + (n * C::NT + wave * 64) * 16), 16,
+          phi_off + (uint32_t)(n * C::NT + tid) * 16, 0, 0, 0);
+  };
+
+  // ---- online-softmax state: per lane (slot residue l%32, head of the pair) ----
+  float m[C::PAIRS], l[C::PAIRS], acc[C::PAIRS][RV];
+#pragma unroll
+  for (int pp = 0; pp < C::PAIRS; ++pp) {
+    m[pp] = -INFINITY;
+    l[pp] = 0.f;
+#pragma unroll
+    for (int r = 0; r < RV; ++r) acc[pp][r] = 0.f;
+  }
+
+  for (int st = 0; st < C::NSTAGE - 1; ++st)
+    if (st < ntiles) issue(st, st);
+
+  const int tj = lane & 31;
+  const int swz = tj & 7;
+  for (int it = 0; it < ntiles; ++it) {
+    const int buf = it % C::NSTAGE;
+    if (it + C::NSTAGE - 1 < ntiles) issue(it + C::NSTAGE - 1, (it + C::NSTAGE - 1) % C::NSTAGE);
+    wait_vm(min(C::NSTAGE - 1, ntiles - 1 - it), C::LOADS);
+    __builtin_amdgcn_s_barrier();
+
+    const char *sb = lds + buf * C::STAGE_BYTES;
+    const char *phb = sb + C::TILE_BYTES;
+    bf16x8_t bphi[kKSteps];
+#pragma unroll
+    for (int st = 0; st < kKSteps; ++st)
+      bphi[st] = *reinterpret_cast<const bf16x8_t *>(phb + (st * 64 + lane) * 16);
+
+    f32x16_t umu = {};
+#pragma unroll
+    for (int st = 0; st < kKSteps; ++st)
+      umu = __builtin_amdgcn_mfma_f32_32x32x16_bf16(Amu[st], bphi[st], umu, 0, 0, 0);
+
+    const bool valid = (t0 + it * kTile + tj) < t1;
+    const char *rec = sb + tj * C::CPT * 16;
+#pragma unroll
+    for (int pp = 0; pp < C::PAIRS; ++pp) {
+      f32x16_t u[C::KT];
+#pragma unroll
+      for (int ti = 0; ti < C::KT; ++ti) {
+        u[ti] = f32x16_t{};
+#pragma unroll
+        for (int st = 0; st < kKSteps; ++st)
+          u[ti] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(Ak[pp][ti][st], bphi[st], u[ti], 0, 0, 0);
+      }
+      const int hl = wave * HPW + 2 * pp + (lane >> 5);
+      const int q0 = hl * C::CPH;
+      u32x4_t ck[C::CK_CHUNKS];
+#pragma unroll
+      for (int c = 0; c < C::CK_CHUNKS; ++c)
+        ck[c] = *reinterpret_cast<const u32x4_t *>(rec + ((q0 + c) ^ swz) * 16);
+      float sc = umu[4 * pp];
+#pragma unroll
+      for (int ti = 0; ti < C::KT; ++ti) {
+#pragma unroll
+        for (int gg = 0; gg < 4; ++gg) {
+          // k = ti*16 + 4*gg + e, e = 0..3: chunk k/8, dwords (k%8)/2
+          const u32x4_t cc = ck[(ti * 16 + 4 * gg) / 8];
+          const int dw = ((4 * gg) % 8) / 2;
+          sc = fmaf(u[ti][4 * gg + 0], bf16_lo(cc[dw]), sc);
+          sc = fmaf(u[ti][4 * gg + 1], bf16_hi(cc[dw]), sc);
+          sc = fmaf(u[ti][4 * gg + 2], bf16_lo(cc[dw + 1]), sc);
+          sc = fmaf(u[ti][4 * gg + 3], bf16_hi(cc[dw + 1]), sc);
+        }
+      }
+      if (valid) {
+        if (sc > m[pp] + kRescaleGap) {
+          const float f = exp2f(m[pp] - sc);
+          l[pp] *= f;
+#pragma unroll
+          for (int r = 0; r < RV; ++r) acc[pp][r] *= f;
+          m[pp] = sc;
+        }
+        const float pe = exp2f(sc - m[pp]);
+        l[pp] += pe;
+#pragma unroll
+        for (int c = 0; c < C::CV_CHUNKS; ++c) {
+          const u32x4_t cv =
+              *reinterpret_cast<const u32x4_t *>(rec + ((q0 + C::CK_CHUNKS + c) ^ swz) * 16);
+#pragma unroll
+          for (int w = 0; w < 4; ++w) {
+            acc[pp][8 * c + 2 * w] = fmaf(pe, bf16_lo(cv[w]), acc[pp][8 * c + 2 * w]);
+            acc[pp][8 * c + 2 * w + 1] = fmaf(pe, bf16_hi(cv[w]), acc[pp][8 * c + 2 * w + 1]);
+          }
+        }
+      }
+    }
+    __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
+    __builtin_amdgcn_s_barrier();
+  }
+
+  // ---- combine the 32 lane states of every head and write the partial ----
+  float *red = reinterpret_cast<float *>(lds);  // [NW][PAIRS][64][RV + 2]
+#pragma unroll
+  for (int pp = 0; pp < C::PAIRS; ++pp) {
+    float *dst = red + ((wave * C::PAIRS + pp) * 64 + lane) * (RV + 2);
+    dst[0] = m[pp];
+    dst[1] = l[pp];
+#pragma unroll
+    for (int r = 0; r < RV; ++r) dst[2 + r] = acc[pp][r];
+  }
+  __syncthreads();
+  for (int o = tid; o < C::HG * (RV + 2); o += C::NT) {
+    const int hl = o / (RV + 2), r = o % (RV + 2);
+    const int w = hl / HPW, pp = (hl % HPW) / 2, half = hl & 1;
+    const float *src = red + ((w * C::PAIRS + pp) * 64 + half * 32) * (RV + 2);
+    float M = -INFINITY;
+    for (int i = 0; i < 32; ++i) M = fmaxf(M, src[i * (RV + 2)]);
+    float v;
+    if (r == 0) {
+      v = M;
+    } else {
+      v = 0.f;
+      for (int i = 0; i < 32; ++i) {
+        const float mi = src[i * (RV + 2)];
+        if (mi != -INFINITY) v = fmaf(src[i * (RV + 2) + r], exp2f(mi - M), v);
+      }
+    }
+    p.ws[((int64_t)(b * p.H + h0 + hl) * p.S + s) * (RV + 2) + r] = v;
+  }
+#endif
+}
+
+template <int RK, int RV, int HPW, int NW>
+hipError_t launch(const DecodeParams &p, hipStream_t st) {
+  using C = Cfg<RK, RV, HPW, NW>;
+  const int groups = p.H / C::HG;
+  const dim3 grid(p.B * groups * p.S);
+  const hipError_t e = hipFuncSetAttribute(
+      reinterpret_cast<const void *>(&decode_mfma_split<RK, RV, HPW, NW>),
+      hipFuncAttributeMaxDynamicSharedMemorySize, C::LDS_BYTES);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL((decode_mfma_split<RK, RV, HPW, NW>), grid, dim3(C::NT), C::LDS_BYTES, st, p);
+  return hipGetLastError();
+}
+
+}  // namespace detail
+
+using namespace detail;
+
+// Shapes served by the fast path and the template instance for each.
+bool decode_mfma_supported(int32_t H, int32_t d, int32_t rk, int32_t rv, int32_t Hs) {
+  if (d != kD || Hs != H) return false;
+  const int32_t hg = decode_mfma_group_heads(rk, rv);
+  return hg > 0 && H % hg == 0;
+}
+
+int32_t decode_mfma_group_heads(int32_t rk, int32_t rv) {
+  if (rk == 16 && rv == 32) return Cfg<16, 32, 4, 4>::HG;
+  if (rk == 32 && rv == 64) return Cfg<32, 64, 2, 4>::HG;
+  if (rk == 48 && rv == 80) return Cfg<48, 80, 2, 4>::HG;
+  return 0;
+}
+
+hipError_t launch_decode_mfma(const DecodeParams &p, hipStream_t st) {
+  if (p.rk == 16 && p.rv == 32) return launch<16, 32, 4, 4>(p, st);
+  if (p.rk == 32 && p.rv == 64) return launch<32, 64, 2, 4>(p, st);
+  if (p.rk == 48 && p.rv == 80) return launch<48, 80, 2, 4>(p, st);
+  return hipErrorInvalidValue;
+}
+
+}  // namespace lla

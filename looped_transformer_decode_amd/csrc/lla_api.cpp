@@ -1,0 +1,348 @@
+// Host side of the LLA C ABI: argument validation, sizes, the exact
+// compression ratio, the RoPE table, and dispatch to the HIP kernels.
+// Every check runs before any launch; nothing here allocates device memory
+// or synchronises the device.
+#include <algorithm>
+#include <climits>
+#include <cmath>
+#include <cstdint>
+#include <cstring>
+#include <numeric>
+
+#include "lla.h"
+#include "lla_internal.h"
+
+namespace lla {
+
+RopeLayout rope_layout(int32_t n_ctx, int32_t d_head) {
+  RopeLayout L{};
+  L.f32_bytes = (size_t)n_ctx * (size_t)d_head * sizeof(float);
+  L.bf16_off = (L.f32_bytes + 255) / 256 * 256;
+  const size_t tiles = ((size_t)n_ctx + 31) / 32;
+  L.bf16_bytes = (d_head % 16 == 0) ? tiles * 32 * (size_t)d_head * 2 : 0;
+  L.total = L.bf16_off + L.bf16_bytes;
+  return L;
+}
+
+}  // namespace lla
+
+namespace {
+
+using lla::DecodeParams;
+using lla::EncodeParams;
+
+bool mul_ok(size_t a, size_t b, size_t *out) {
+  if (a != 0 && b > SIZE_MAX / a) return false;
+  *out = a * b;
+  return true;
+}
+
+size_t elt_size(int32_t dtype) { return dtype == LLA_DT_F32 ? 4 : 2; }
+
+int32_t store_heads(const lla_store_t *s) { return s->variant == LLA_2D ? 1 : s->heads; }
+
+// Element count of the store, or 0 on overflow.
+size_t store_elems(const lla_store_t *s) {
+  size_t n = 1;
+  const size_t dims[5] = {(size_t)s->batch, (size_t)s->layers, (size_t)s->max_ctx,
+                          (size_t)store_heads(s), (size_t)s->r_k + (size_t)s->r_v};
+  for (size_t v : dims)
+    if (!mul_ok(n, v, &n)) return 0;
+  return n;
+}
+
+// float64 -> bfloat16 bits, round to nearest, ties to even, in one step.
+uint16_t f64_to_bf16(double v) {
+  if (std::isnan(v)) return 0x7FC0;
+  if (v == 0.0) return std::signbit(v) ? 0x8000 : 0x0000;
+  int e = 0;
+  std::frexp(v, &e);
+  if (e < -125) e = -125;
+  const double q = std::ldexp(1.0, e - 8);
+  const double r = std::nearbyint(v / q) * q;  // default rounding mode: ties to even
+  const float f = (float)r;                    // exact: r has at most 8 significant bits
+  uint32_t u;
+  std::memcpy(&u, &f, 4);
+  return (uint16_t)(u >> 16);
+}
+
+int32_t auto_splits(const lla_store_t *s, bool mfma) {
+  // Enough workgroups to cover 256 CUs several times, each split at least
+  // 256 slots long so that the per-workgroup setup stays amortised.
+  const int64_t per_split =
+      mfma ? (int64_t)s->batch * (s->heads / lla::decode_mfma_group_heads(s->r_k, s->r_v))
+           : (int64_t)s->batch * s->heads;
+  const int64_t target = mfma ? 1024 : 2048;
+  int64_t S = (target + per_split - 1) / per_split;
+  const int64_t max_s = std::max<int64_t>(1, s->max_ctx / 256);
+  if (S > max_s) S = max_s;
+  if (S < 1) S = 1;
+  return (int32_t)S;
+}
+
+bool use_mfma(const lla_store_t *s) {
+  return s->dtype == LLA_DT_BF16 &&
+         lla::decode_mfma_supported(s->heads, s->d_head, s->r_k, s->r_v, store_heads(s));
+}
+
+bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
+
+lla_status_t decode_impl(const lla_store_t *st, int32_t want_variant, int32_t layer,
+                         int32_t loop, const float *q, const void *wk, const void *wv,
+                         const float *muk, const float *muv, const int32_t *pos,
+                         const void *rope, float scale, float *out, void *ws, size_t ws_bytes,
+                         int32_t n_splits, hipStream_t stream) {
+  lla_status_t e = lla_store_check(st);
+  if (e != LLA_OK) return e;
+  if (st->variant != want_variant) return LLA_E_VARIANT;
+  if (!st->data || !q || !wk || !wv || !muk || !muv || !pos || !rope || !out) return LLA_E_NULL;
+  if (layer < 0 || layer >= st->layers || loop < 0 || loop >= st->loops) return LLA_E_RANGE;
+  if (n_splits < 0 || n_splits > st->max_ctx) return LLA_E_RANGE;
+  if (std::isnan(scale) || std::isinf(scale)) return LLA_E_RANGE;
+  const bool mfma = use_mfma(st) && aligned16(st->data) && aligned16(wk) && aligned16(rope);
+  if (!mfma) {
+    if (st->d_head > 256 || st->r_k > 128 || st->r_v > 256 ||
+        (size_t)st->d_head * st->r_k > 8192)
+      return LLA_E_UNSUPPORTED;
+  } else {
+    // 32-bit buffer offsets address one (sequence, layer) slab
+    const uint64_t slab = (uint64_t)st->max_ctx * store_heads(st) * (st->r_k + st->r_v) * 2;
+    if (slab >= (1ull << 31)) return LLA_E_UNSUPPORTED;
+  }
+  const int32_t S = n_splits ? n_splits : auto_splits(st, mfma);
+  const size_t need = lla_decode_workspace_bytes(st, S);
+  if (!ws) return LLA_E_WORKSPACE;
+  if (need == 0 || ws_bytes < need) return LLA_E_WORKSPACE;
+
+  DecodeParams p{};
+  p.store = st->data;
+  p.B = st->batch;
+  p.D = st->layers;
+  p.N = st->max_ctx;
+  p.H = st->heads;
+  p.Hs = store_heads(st);
+  p.rk = st->r_k;
+  p.rv = st->r_v;
+  p.R = st->r_k + st->r_v;
+  p.d = st->d_head;
+  p.layer = layer;
+  p.q = q;
+  p.wk = wk;
+  p.wv = wv;
+  p.muk = muk;
+  p.muv = muv;
+  p.pos = pos;
+  const lla::RopeLayout rl = lla::rope_layout(st->max_ctx, st->d_head);
+  p.rope_f32 = reinterpret_cast<const float *>(rope);
+  p.rope_bf16 = reinterpret_cast<const uint16_t *>(reinterpret_cast<const char *>(rope) + rl.bf16_off);
+  const float sc = scale > 0.f ? scale : (float)(1.0 / std::sqrt((double)st->d_head));
+  p.scale_log2 = (float)((double)sc * 1.4426950408889634);
+  p.ws = reinterpret_cast<float *>(ws);
+  p.S = S;
+  const int32_t per = (st->max_ctx + S - 1) / S;
+  p.split_len = (per + 31) / 32 * 32;
+  p.out = out;
+
+  hipError_t he = mfma ? lla::launch_decode_mfma(p, stream)
+                       : lla::launch_decode_valu(p, st->dtype, stream);
+  if (he != hipSuccess) return LLA_E_HIP;
+  he = lla::launch_decode_merge(p, st->dtype, stream);
+  return he == hipSuccess ? LLA_OK : LLA_E_HIP;
+}
+
+lla_status_t encode_impl(const lla_store_t *st, int32_t want_variant, int32_t layer,
+                         const void *xk, const void *xv, const float *muk, const float *muv,
+                         const void *wdk, const void *wdv, const int32_t *start, int32_t n_new,
+                         hipStream_t stream) {
+  lla_status_t e = lla_store_check(st);
+  if (e != LLA_OK) return e;
+  if (st->variant != want_variant) return LLA_E_VARIANT;
+  if (layer < 0 || layer >= st->layers) return LLA_E_RANGE;
+  if (n_new < 0 || n_new > st->max_ctx) return LLA_E_RANGE;
+  if (n_new == 0) return LLA_OK;
+  if (!st->data || !xk || !xv || !muk || !muv || !wdk || !wdv || !start) return LLA_E_NULL;
+  if (st->r_k > 128 || st->r_v > 128) return LLA_E_UNSUPPORTED;
+  const int64_t width = (int64_t)st->d_head * (st->variant == LLA_2D ? st->heads : 1);
+  const int64_t K = width * st->loops;
+  if (K > INT32_MAX || (int64_t)st->batch * n_new > INT32_MAX) return LLA_E_OVERFLOW;
+  EncodeParams p{};
+  p.store = st->data;
+  p.B = st->batch;
+  p.D = st->layers;
+  p.N = st->max_ctx;
+  p.Hs = store_heads(st);
+  p.rk = st->r_k;
+  p.rv = st->r_v;
+  p.R = st->r_k + st->r_v;
+  p.layer = layer;
+  p.K = (int32_t)K;
+  p.n_new = n_new;
+  p.x[0] = xk;
+  p.x[1] = xv;
+  p.mu[0] = muk;
+  p.mu[1] = muv;
+  p.wd[0] = wdk;
+  p.wd[1] = wdv;
+  p.start = start;
+  const hipError_t he = lla::launch_encode_valu(p, st->dtype, stream);
+  return he == hipSuccess ? LLA_OK : LLA_E_HIP;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char *lla_status_string(lla_status_t s) {
+  switch (s) {
+    case LLA_OK: return "LLA_OK";
+    case LLA_E_NULL: return "LLA_E_NULL: a required pointer is NULL";
+    case LLA_E_SHAPE: return "LLA_E_SHAPE: invalid or inconsistent sizes";
+    case LLA_E_DTYPE: return "LLA_E_DTYPE: unknown element type";
+    case LLA_E_RANGE: return "LLA_E_RANGE: index or value out of range";
+    case LLA_E_WORKSPACE: return "LLA_E_WORKSPACE: workspace missing or too small";
+    case LLA_E_UNSUPPORTED: return "LLA_E_UNSUPPORTED: no kernel for this shape";
+    case LLA_E_VARIANT: return "LLA_E_VARIANT: store variant does not match the call";
+    case LLA_E_HIP: return "LLA_E_HIP: HIP launch or runtime error";
+    case LLA_E_OVERFLOW: return "LLA_E_OVERFLOW: size does not fit";
+  }
+  return "LLA_E_UNKNOWN";
+}
+
+lla_status_t lla_store_check(const lla_store_t *s) {
+  if (!s) return LLA_E_NULL;
+  if (s->variant != LLA_PER_HEAD && s->variant != LLA_2D) return LLA_E_VARIANT;
+  if (s->dtype != LLA_DT_F32 && s->dtype != LLA_DT_BF16) return LLA_E_DTYPE;
+  if (s->batch <= 0 || s->layers <= 0 || s->max_ctx <= 0 || s->heads <= 0 || s->d_head <= 0 ||
+      s->loops <= 0 || s->r_k <= 0 || s->r_v <= 0)
+    return LLA_E_SHAPE;
+  if (s->d_head % 2 != 0) return LLA_E_SHAPE;
+  if (!(s->rope_base > 1.0f) || std::isinf(s->rope_base)) return LLA_E_RANGE;
+  size_t bytes;
+  const size_t n = store_elems(s);
+  if (n == 0 || !mul_ok(n, elt_size(s->dtype), &bytes) || bytes > (size_t)INT64_MAX)
+    return LLA_E_OVERFLOW;
+  return LLA_OK;
+}
+
+size_t lla_store_bytes(const lla_store_t *s) {
+  if (lla_store_check(s) != LLA_OK) return 0;
+  return store_elems(s) * elt_size(s->dtype);
+}
+
+int64_t lla_store_offset(const lla_store_t *s, int32_t b, int32_t layer, int32_t pos,
+                         int32_t head, int32_t comp) {
+  if (lla_store_check(s) != LLA_OK) return -1;
+  const int32_t Hs = store_heads(s), R = s->r_k + s->r_v;
+  if (b < 0 || b >= s->batch || layer < 0 || layer >= s->layers || pos < 0 ||
+      pos >= s->max_ctx || head < 0 || head >= Hs || comp < 0 || comp >= R)
+    return -1;
+  return (((((int64_t)b * s->layers + layer) * s->max_ctx + pos) * Hs + head) * R) + comp;
+}
+
+lla_status_t lla_compression_ratio(const lla_store_t *s, int64_t *num, int64_t *den) {
+  const lla_status_t e = lla_store_check(s);
+  if (e != LLA_OK) return e;
+  if (!num || !den) return LLA_E_NULL;
+  int64_t n = 2LL * s->loops * s->d_head * (s->variant == LLA_2D ? s->heads : 1);
+  int64_t d = (int64_t)s->r_k + s->r_v;
+  const int64_t g = std::gcd(n, d);
+  *num = n / g;
+  *den = d / g;
+  return LLA_OK;
+}
+
+size_t lla_rope_table_bytes(const lla_store_t *s) {
+  if (lla_store_check(s) != LLA_OK) return 0;
+  return lla::rope_layout(s->max_ctx, s->d_head).total;
+}
+
+lla_status_t lla_rope_table_fill(const lla_store_t *s, void *host_table, size_t bytes) {
+  const lla_status_t e = lla_store_check(s);
+  if (e != LLA_OK) return e;
+  if (!host_table) return LLA_E_NULL;
+  const lla::RopeLayout L = lla::rope_layout(s->max_ctx, s->d_head);
+  if (bytes < L.total) return LLA_E_WORKSPACE;
+  const int32_t d = s->d_head, half = d / 2, N = s->max_ctx;
+  const double base = (double)s->rope_base;
+  float *f = reinterpret_cast<float *>(host_table);
+  for (int32_t j = 0; j < N; ++j)
+    for (int32_t i = 0; i < half; ++i) {
+      const double ang = (double)j * std::pow(base, -2.0 * i / d);
+      f[((size_t)j * half + i) * 2] = (float)std::cos(ang);
+      f[((size_t)j * half + i) * 2 + 1] = (float)std::sin(ang);
+    }
+  std::memset(reinterpret_cast<char *>(host_table) + L.f32_bytes, 0, L.bf16_off - L.f32_bytes);
+  if (L.bf16_bytes) {
+    uint16_t *h = reinterpret_cast<uint16_t *>(reinterpret_cast<char *>(host_table) + L.bf16_off);
+    const int32_t ksteps = d / 16, tiles = (N + 31) / 32;
+    for (int32_t t = 0; t < tiles; ++t)
+      for (int32_t st = 0; st < ksteps; ++st)
+        for (int32_t lane = 0; lane < 64; ++lane)
+          for (int32_t e8 = 0; e8 < 8; ++e8) {
+            const int32_t j = 32 * t + lane % 32;
+            const int32_t i = 16 * st + 8 * (lane / 32) + e8;
+            const int32_t ii = i < half ? i : i - half;
+            const double ang = (double)j * std::pow(base, -2.0 * ii / d);
+            const double v = i < half ? std::cos(ang) : std::sin(ang);
+            h[(((size_t)t * ksteps + st) * 64 + lane) * 8 + e8] = f64_to_bf16(v);
+          }
+  }
+  return LLA_OK;
+}
+
+lla_status_t lla_encode_append(const lla_store_t *store, int32_t layer, const void *x_k,
+                               const void *x_v, const float *mu_k, const float *mu_v,
+                               const void *w_down_k, const void *w_down_v,
+                               const int32_t *start_pos, int32_t n_new, hipStream_t stream) {
+  return encode_impl(store, LLA_PER_HEAD, layer, x_k, x_v, mu_k, mu_v, w_down_k, w_down_v,
+                     start_pos, n_new, stream);
+}
+
+lla_status_t lla2d_encode_append(const lla_store_t *store, int32_t layer, const void *x_k,
+                                 const void *x_v, const float *mu_k, const float *mu_v,
+                                 const void *w_down_k, const void *w_down_v,
+                                 const int32_t *start_pos, int32_t n_new, hipStream_t stream) {
+  return encode_impl(store, LLA_2D, layer, x_k, x_v, mu_k, mu_v, w_down_k, w_down_v, start_pos,
+                     n_new, stream);
+}
+
+size_t lla_decode_workspace_bytes(const lla_store_t *s, int32_t n_splits) {
+  if (lla_store_check(s) != LLA_OK || n_splits < 0) return 0;
+  const int32_t S = n_splits ? n_splits : lla_decode_auto_splits(s);
+  size_t n = (size_t)s->batch * s->heads;
+  if (!mul_ok(n, (size_t)S, &n) || !mul_ok(n, (size_t)s->r_v + 2, &n) || !mul_ok(n, 4, &n))
+    return 0;
+  return n;
+}
+
+int32_t lla_decode_auto_splits(const lla_store_t *s) {
+  if (lla_store_check(s) != LLA_OK) return 0;
+  return auto_splits(s, use_mfma(s));
+}
+
+lla_status_t lla_decode_attn(const lla_store_t *store, int32_t layer, int32_t loop,
+                             const float *q, const void *w_up_k_t, const void *w_up_v_t,
+                             const float *mu_k_t, const float *mu_v_t, const int32_t *pos,
+                             const void *rope_table, float softmax_scale, float *out,
+                             void *workspace, size_t ws_bytes, int32_t n_splits,
+                             hipStream_t stream) {
+  return decode_impl(store, LLA_PER_HEAD, layer, loop, q, w_up_k_t, w_up_v_t, mu_k_t, mu_v_t,
+                     pos, rope_table, softmax_scale, out, workspace, ws_bytes, n_splits, stream);
+}
+
+lla_status_t lla2d_decode_attn(const lla_store_t *store, int32_t layer, int32_t loop,
+                               const float *q, const void *w_up_k_t, const void *w_up_v_t,
+                               const float *mu_k_t, const float *mu_v_t, const int32_t *pos,
+                               const void *rope_table, float softmax_scale, float *out,
+                               void *workspace, size_t ws_bytes, int32_t n_splits,
+                               hipStream_t stream) {
+  return decode_impl(store, LLA_2D, layer, loop, q, w_up_k_t, w_up_v_t, mu_k_t, mu_v_t, pos,
+                     rope_table, softmax_scale, out, workspace, ws_bytes, n_splits, stream);
+}
+
+const char *lla_decode_path(const lla_store_t *s) {
+  if (lla_store_check(s) != LLA_OK) return nullptr;
+  return use_mfma(s) ? "mfma" : "valu";
+}
+
+}  // extern "C"

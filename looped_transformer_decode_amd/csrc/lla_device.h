@@ -1,0 +1,59 @@
+// Device-side helpers for the gfx950 kernels: bfloat16 conversion, wave64
+// reductions, wait-count encoding.
+#pragma once
+
+#include <cstdint>
+
+#include <hip/hip_runtime.h>
+
+namespace lla {
+
+constexpr float kLog2e = 1.4426950408889634f;
+
+// bfloat16 <-> float32.  bf16 -> f32 is exact (a 16-bit shift); f32 -> bf16
+// rounds to nearest, ties to even; NaN stays NaN.
+__device__ __forceinline__ float bf16_bits_to_f32(uint32_t bits16) {
+  return __uint_as_float(bits16 << 16);
+}
+__device__ __forceinline__ float bf16_lo(uint32_t pair) { return __uint_as_float(pair << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t pair) { return __uint_as_float(pair & 0xFFFF0000u); }
+__device__ __forceinline__ uint16_t f32_to_bf16_bits(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7F800000u) == 0x7F800000u && (u & 0x007FFFFFu)) return uint16_t((u >> 16) | 0x40u);
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return uint16_t(u >> 16);
+}
+
+// Element access for the two storage types.
+struct bf16_t {
+  uint16_t bits;
+};
+__device__ __forceinline__ float load_elem(const float *p, int64_t i) { return p[i]; }
+__device__ __forceinline__ float load_elem(const bf16_t *p, int64_t i) {
+  return bf16_bits_to_f32(p[i].bits);
+}
+__device__ __forceinline__ void store_elem(float *p, int64_t i, float v) { p[i] = v; }
+__device__ __forceinline__ void store_elem(bf16_t *p, int64_t i, float v) {
+  p[i].bits = f32_to_bf16_bits(v);
+}
+
+// wave64 butterfly reductions (every lane receives the result).
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
+  return v;
+}
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+  return v;
+}
+
+// s_waitcnt immediate that waits until at most n vector-memory operations
+// are outstanding and does not wait on the other counters (gfx9 encoding:
+// vmcnt[3:0] | expcnt[6:4] | lgkmcnt[11:8] | vmcnt[5:4] << 14).
+constexpr int waitcnt_vm(int n) {
+  return (n & 15) | (7 << 4) | (15 << 8) | ((n >> 4) << 14);
+}
+
+}  // namespace lla

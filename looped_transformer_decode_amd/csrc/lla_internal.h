@@ -1,0 +1,72 @@
+// Internal declarations shared by the host API (lla_api.cpp) and the HIP
+// kernel files.  Not part of the public ABI.
+#pragma once
+
+#include <cstddef>
+#include <cstdint>
+
+#include <hip/hip_runtime.h>
+
+#include "lla.h"
+
+namespace lla {
+
+// Byte layout of the opaque RoPE table produced by lla_rope_table_fill():
+//   [0, f32_bytes)            float32 cos/sin, [N][d/2][2]
+//   [bf16_off, +bf16_bytes)   bfloat16 phi operand tiles for the MFMA decode:
+//                             per 32-slot tile, [d/16 k-steps][64 lanes][8],
+//                             element (s, lane, e) = phi[32*tile + lane%32][i],
+//                             i = 16*s + 8*(lane/32) + e, with
+//                             phi[j][i] = cos(j*theta_i) for i < d/2 and
+//                             sin(j*theta_{i-d/2}) otherwise.
+struct RopeLayout {
+  size_t f32_bytes;
+  size_t bf16_off;
+  size_t bf16_bytes;
+  size_t total;
+};
+RopeLayout rope_layout(int32_t n_ctx, int32_t d_head);
+
+// Arguments of one decode call, resolved and validated on the host.
+struct DecodeParams {
+  const void *store;       // base of the whole store
+  int32_t B, D, N, H, Hs;  // Hs = stored heads (H or 1)
+  int32_t R, rk, rv, d;    // R = rk + rv
+  int32_t layer;
+  const float *q;          // [B, H, d]
+  const void *wk;          // [H*d, rk]  (per-head [H, d, rk] is the same memory)
+  const void *wv;          // [H*d, rv]
+  const float *muk;        // [H*d]
+  const float *muv;        // [H*d]
+  const int32_t *pos;      // [B]
+  const float *rope_f32;   // [N][d/2][2]
+  const uint16_t *rope_bf16;
+  float scale_log2;        // softmax scale * log2(e)
+  float *ws;               // partials [B, H, S, rv + 2]
+  int32_t S;               // context splits
+  int32_t split_len;       // slots per split (multiple of 32)
+  float *out;              // [B, H, d]
+};
+
+struct EncodeParams {
+  void *store;
+  int32_t B, D, N, Hs, R, rk, rv;
+  int32_t layer;
+  int32_t K;               // T * width: length of the stacked vector
+  int32_t n_new;
+  const void *x[2];        // [B, n_new, Hs, K] per axis
+  const float *mu[2];      // [Hs, K]
+  const void *wd[2];       // [Hs, K, r]
+  const int32_t *start;    // [B]
+};
+
+// Launchers (return the launch status).  dtype is lla_dtype_t.
+hipError_t launch_decode_valu(const DecodeParams &p, int dtype, hipStream_t s);
+hipError_t launch_decode_merge(const DecodeParams &p, int dtype, hipStream_t s);
+bool decode_mfma_supported(int32_t H, int32_t d, int32_t rk, int32_t rv, int32_t Hs);
+// Heads one fast-path workgroup covers (0 if the ranks have no instance).
+int32_t decode_mfma_group_heads(int32_t rk, int32_t rv);
+hipError_t launch_decode_mfma(const DecodeParams &p, hipStream_t s);
+hipError_t launch_encode_valu(const EncodeParams &p, int dtype, hipStream_t s);
+
+}  // namespace lla

@@ -1,0 +1,291 @@
+"""Thin Python binding of the LLA C ABI (include/lla.h) via ctypes.
+
+Argument marshalling only: every step of the decode / encode path runs in
+the HIP kernels of liblla.so.  torch supplies device memory and streams.
+The library must be built (``looped_transformer_decode_amd.build``); this
+module raises instead of falling back to anything else when it is missing.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from fractions import Fraction
+
+import torch
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "liblla.so")
+
+LLA_PER_HEAD, LLA_2D = 0, 1
+LLA_DT_F32, LLA_DT_BF16 = 0, 1
+STATUS = ["LLA_OK", "LLA_E_NULL", "LLA_E_SHAPE", "LLA_E_DTYPE", "LLA_E_RANGE",
+          "LLA_E_WORKSPACE", "LLA_E_UNSUPPORTED", "LLA_E_VARIANT", "LLA_E_HIP",
+          "LLA_E_OVERFLOW"]
+_TORCH_DT = {LLA_DT_F32: torch.float32, LLA_DT_BF16: torch.bfloat16}
+_DT_NAME = {"f32": LLA_DT_F32, "bf16": LLA_DT_BF16}
+_VARIANT_NAME = {"per_head": LLA_PER_HEAD, "2d": LLA_2D}
+
+
+class LlaError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__(f"{where}: {status_string(status)}")
+
+
+class StoreDesc(ctypes.Structure):
+    _fields_ = [("variant", ctypes.c_int32), ("dtype", ctypes.c_int32),
+                ("batch", ctypes.c_int32), ("layers", ctypes.c_int32),
+                ("max_ctx", ctypes.c_int32), ("heads", ctypes.c_int32),
+                ("d_head", ctypes.c_int32), ("loops", ctypes.c_int32),
+                ("r_k", ctypes.c_int32), ("r_v", ctypes.c_int32),
+                ("rope_base", ctypes.c_float), ("data", ctypes.c_void_p)]
+
+
+_lib = None
+_P, _I32, _I64, _SZ, _F = (ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64,
+                           ctypes.c_size_t, ctypes.c_float)
+_SIGS = {
+    "lla_status_string": ([_I32], ctypes.c_char_p),
+    "lla_store_check": ([_P], _I32),
+    "lla_store_bytes": ([_P], _SZ),
+    "lla_store_offset": ([_P, _I32, _I32, _I32, _I32, _I32], _I64),
+    "lla_compression_ratio": ([_P, _P, _P], _I32),
+    "lla_rope_table_bytes": ([_P], _SZ),
+    "lla_rope_table_fill": ([_P, _P, _SZ], _I32),
+    "lla_encode_append": ([_P, _I32, _P, _P, _P, _P, _P, _P, _P, _I32, _P], _I32),
+    "lla2d_encode_append": ([_P, _I32, _P, _P, _P, _P, _P, _P, _P, _I32, _P], _I32),
+    "lla_decode_workspace_bytes": ([_P, _I32], _SZ),
+    "lla_decode_auto_splits": ([_P], _I32),
+    "lla_decode_attn": ([_P, _I32, _I32, _P, _P, _P, _P, _P, _P, _P, _F, _P, _P, _SZ, _I32, _P],
+                        _I32),
+    "lla2d_decode_attn": ([_P, _I32, _I32, _P, _P, _P, _P, _P, _P, _P, _F, _P, _P, _SZ, _I32,
+                           _P], _I32),
+    "lla_decode_path": ([_P], ctypes.c_char_p),
+}
+EXPORTS = tuple(_SIGS)
+
+
+def lib():
+    """The loaded liblla.so (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it with "
+                               "`python -m looped_transformer_decode_amd.build`")
+        L = ctypes.CDLL(LIB_PATH)
+        for name, (args, res) in _SIGS.items():
+            f = getattr(L, name)
+            f.argtypes, f.restype = args, res
+        _lib = L
+    return _lib
+
+
+def status_string(status: int) -> str:
+    return lib().lla_status_string(status).decode()
+
+
+def _check(status: int, where: str):
+    if status != 0:
+        raise LlaError(status, where)
+
+
+def _ptr(t) -> int | None:
+    return None if t is None else t.data_ptr()
+
+
+def _stream(stream) -> int | None:
+    if stream is None:
+        return torch.cuda.current_stream().cuda_stream if torch.cuda.is_available() else None
+    return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+
+
+class LatentStore:
+    """A latent store: the descriptor plus the device tensor that holds it.
+
+    tensor shape [B, D, N, H', r_k + r_v] (H' = H per-head, 1 for LLA-2D),
+    torch dtype float32 or bfloat16.  ``tensor`` may be supplied (it must be
+    contiguous and of that shape) or is allocated uninitialised on
+    ``device``; ``device=None`` creates a descriptor without memory (host-only
+    queries such as sizes and offsets)."""
+
+    def __init__(self, variant="per_head", dtype="bf16", *, batch, layers, max_ctx, heads,
+                 d_head, loops, r_k, r_v, rope_base=10000.0, tensor=None, device=None):
+        self.variant = _VARIANT_NAME.get(variant, variant)
+        self.dtype = _DT_NAME.get(dtype, dtype)
+        self.batch, self.layers, self.max_ctx = batch, layers, max_ctx
+        self.heads, self.d_head, self.loops, self.r_k, self.r_v = heads, d_head, loops, r_k, r_v
+        self.rope_base = rope_base
+        self.store_heads = 1 if self.variant == LLA_2D else heads
+        self.shape = (batch, layers, max_ctx, self.store_heads, r_k + r_v)
+        if tensor is None and device is not None:
+            tensor = torch.empty(self.shape, dtype=_TORCH_DT[self.dtype], device=device)
+        if tensor is not None:
+            if tuple(tensor.shape) != self.shape or not tensor.is_contiguous():
+                raise ValueError(f"store tensor must be contiguous {self.shape}")
+            if tensor.dtype != _TORCH_DT[self.dtype]:
+                raise ValueError(f"store tensor dtype must be {_TORCH_DT[self.dtype]}")
+        self.tensor = tensor
+
+    @property
+    def torch_dtype(self):
+        return _TORCH_DT[self.dtype]
+
+    def desc(self) -> StoreDesc:
+        return StoreDesc(self.variant, self.dtype, self.batch, self.layers, self.max_ctx,
+                         self.heads, self.d_head, self.loops, self.r_k, self.r_v,
+                         self.rope_base, _ptr(self.tensor))
+
+
+# ---------------------------------------------------------------- host-only
+def lla_store_check(store: LatentStore) -> None:
+    d = store.desc()
+    _check(lib().lla_store_check(ctypes.byref(d)), "lla_store_check")
+
+
+def lla_store_bytes(store: LatentStore) -> int:
+    d = store.desc()
+    return lib().lla_store_bytes(ctypes.byref(d))
+
+
+def lla_store_offset(store: LatentStore, b, layer, pos, head, comp) -> int:
+    d = store.desc()
+    return lib().lla_store_offset(ctypes.byref(d), b, layer, pos, head, comp)
+
+
+def lla_compression_ratio(store: LatentStore) -> Fraction:
+    d = store.desc()
+    num, den = ctypes.c_int64(), ctypes.c_int64()
+    _check(lib().lla_compression_ratio(ctypes.byref(d), ctypes.byref(num), ctypes.byref(den)),
+           "lla_compression_ratio")
+    return Fraction(num.value, den.value)
+
+
+def lla_rope_table_bytes(store: LatentStore) -> int:
+    d = store.desc()
+    return lib().lla_rope_table_bytes(ctypes.byref(d))
+
+
+def lla_rope_table_fill(store: LatentStore) -> torch.Tensor:
+    """Host (CPU) uint8 tensor holding the RoPE table."""
+    d = store.desc()
+    n = lib().lla_rope_table_bytes(ctypes.byref(d))
+    if n == 0:
+        raise LlaError(lib().lla_store_check(ctypes.byref(d)) or 2, "lla_rope_table_bytes")
+    host = torch.empty(n, dtype=torch.uint8)
+    _check(lib().lla_rope_table_fill(ctypes.byref(d), host.data_ptr(), n), "lla_rope_table_fill")
+    return host
+
+
+def rope_table(store: LatentStore, device) -> torch.Tensor:
+    """The RoPE table copied to ``device``."""
+    return lla_rope_table_fill(store).to(device)
+
+
+def lla_decode_workspace_bytes(store: LatentStore, n_splits: int = 0) -> int:
+    d = store.desc()
+    return lib().lla_decode_workspace_bytes(ctypes.byref(d), n_splits)
+
+
+def lla_decode_auto_splits(store: LatentStore) -> int:
+    d = store.desc()
+    return lib().lla_decode_auto_splits(ctypes.byref(d))
+
+
+def lla_decode_path(store: LatentStore) -> str | None:
+    d = store.desc()
+    r = lib().lla_decode_path(ctypes.byref(d))
+    return None if r is None else r.decode()
+
+
+def workspace(store: LatentStore, n_splits: int = 0, device=None) -> torch.Tensor:
+    n = lla_decode_workspace_bytes(store, n_splits)
+    dev = device if device is not None else store.tensor.device
+    return torch.empty(max(n, 4), dtype=torch.uint8, device=dev)
+
+
+# ---------------------------------------------------------------- launching
+def _need(t, dtype, shape, name):
+    if t is None:
+        return
+    if t.dtype != dtype:
+        raise ValueError(f"{name}: dtype {t.dtype}, expected {dtype}")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name}: shape {tuple(t.shape)}, expected {tuple(shape)}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def _encode(fn, store, layer, x_k, x_v, mu_k, mu_v, w_down_k, w_down_v, start_pos, n_new,
+            stream):
+    s = store
+    width = s.d_head * (s.heads if s.variant == LLA_2D else 1)
+    K = s.loops * width
+    hs = s.store_heads
+    if n_new is None:
+        n_new = x_k.shape[1]
+    _need(x_k, s.torch_dtype, (s.batch, n_new, hs, K) if s.variant == LLA_PER_HEAD
+          else (s.batch, n_new, K), "x_k")
+    _need(x_v, s.torch_dtype, tuple(x_k.shape), "x_v")
+    _need(mu_k, torch.float32, (hs, K) if s.variant == LLA_PER_HEAD else (K,), "mu_k")
+    _need(mu_v, torch.float32, tuple(mu_k.shape), "mu_v")
+    _need(w_down_k, s.torch_dtype, (hs, K, s.r_k) if s.variant == LLA_PER_HEAD
+          else (K, s.r_k), "w_down_k")
+    _need(w_down_v, s.torch_dtype, (hs, K, s.r_v) if s.variant == LLA_PER_HEAD
+          else (K, s.r_v), "w_down_v")
+    _need(start_pos, torch.int32, (s.batch,), "start_pos")
+    d = s.desc()
+    _check(fn(ctypes.byref(d), layer, _ptr(x_k), _ptr(x_v), _ptr(mu_k), _ptr(mu_v),
+              _ptr(w_down_k), _ptr(w_down_v), _ptr(start_pos), n_new, _stream(stream)),
+           fn.__name__)
+
+
+def lla_encode_append(store, layer, x_k, x_v, mu_k, mu_v, w_down_k, w_down_v, start_pos,
+                      n_new=None, stream=None):
+    """c = (x - mu) W_down for n_new tokens per sequence (per-head store)."""
+    _encode(lib().lla_encode_append, store, layer, x_k, x_v, mu_k, mu_v, w_down_k, w_down_v,
+            start_pos, n_new, stream)
+
+
+def lla2d_encode_append(store, layer, x_k, x_v, mu_k, mu_v, w_down_k, w_down_v, start_pos,
+                        n_new=None, stream=None):
+    """LLA-2D encode: one latent per token over the [t][h][d] stack."""
+    _encode(lib().lla2d_encode_append, store, layer, x_k, x_v, mu_k, mu_v, w_down_k, w_down_v,
+            start_pos, n_new, stream)
+
+
+def _decode(fn, store, layer, loop, q, w_up_k_t, w_up_v_t, mu_k_t, mu_v_t, pos, rope, out,
+            ws, softmax_scale, n_splits, stream):
+    s = store
+    H, d = s.heads, s.d_head
+    _need(q, torch.float32, (s.batch, H, d), "q")
+    if s.variant == LLA_PER_HEAD:
+        _need(w_up_k_t, s.torch_dtype, (H, d, s.r_k), "w_up_k_t")
+        _need(w_up_v_t, s.torch_dtype, (H, d, s.r_v), "w_up_v_t")
+        _need(mu_k_t, torch.float32, (H, d), "mu_k_t")
+        _need(mu_v_t, torch.float32, (H, d), "mu_v_t")
+    else:
+        _need(w_up_k_t, s.torch_dtype, (H * d, s.r_k), "w_up_k_t")
+        _need(w_up_v_t, s.torch_dtype, (H * d, s.r_v), "w_up_v_t")
+        _need(mu_k_t, torch.float32, (H * d,), "mu_k_t")
+        _need(mu_v_t, torch.float32, (H * d,), "mu_v_t")
+    _need(pos, torch.int32, (s.batch,), "pos")
+    _need(out, torch.float32, (s.batch, H, d), "out")
+    dsc = s.desc()
+    _check(fn(ctypes.byref(dsc), layer, loop, _ptr(q), _ptr(w_up_k_t), _ptr(w_up_v_t),
+              _ptr(mu_k_t), _ptr(mu_v_t), _ptr(pos), _ptr(rope), float(softmax_scale), _ptr(out),
+              _ptr(ws), 0 if ws is None else ws.numel() * ws.element_size(), n_splits,
+              _stream(stream)), fn.__name__)
+    return out
+
+
+def lla_decode_attn(store, layer, loop, q, w_up_k_t, w_up_v_t, mu_k_t, mu_v_t, pos, rope_table,
+                    out, workspace, softmax_scale=0.0, n_splits=0, stream=None):
+    """Decode-time attention at (layer, loop) over a per-head latent store."""
+    return _decode(lib().lla_decode_attn, store, layer, loop, q, w_up_k_t, w_up_v_t, mu_k_t,
+                   mu_v_t, pos, rope_table, out, workspace, softmax_scale, n_splits, stream)
+
+
+def lla2d_decode_attn(store, layer, loop, q, w_up_k_t, w_up_v_t, mu_k_t, mu_v_t, pos,
+                      rope_table, out, workspace, softmax_scale=0.0, n_splits=0, stream=None):
+    """LLA-2D decode: one latent per token decodes all H heads."""
+    return _decode(lib().lla2d_decode_attn, store, layer, loop, q, w_up_k_t, w_up_v_t, mu_k_t,
+                   mu_v_t, pos, rope_table, out, workspace, softmax_scale, n_splits, stream)
