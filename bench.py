@@ -41,6 +41,11 @@ def parse():
     ap.add_argument("--workload", default="extreme_batch_b768_ctx4k")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="budget of the oracle timing sample (0 disables it)")
+    ap.add_argument("--splits", type=int, default=0,
+                    help="context splits per decode call (0 = the library's choice)")
+    ap.add_argument("--copy-calibration", type=float, default=0.0, metavar="GB",
+                    help="instead of the benchmark, copy a buffer of this size a few times "
+                         "(reference for HBM byte counters)")
     ap.add_argument("--no-encode", action="store_true", help=argparse.SUPPRESS)
     return ap.parse_args()
 
@@ -116,6 +121,23 @@ def main():
 
     import torch
 
+    if args.copy_calibration > 0:
+        n = int(args.copy_calibration * 1e9) // 4
+        src = torch.ones(n, dtype=torch.float32, device="cuda:0")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        dst.copy_(src)
+        e1.record()
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1)
+        print(json.dumps({"copy_bytes_read": n * 4, "copy_bytes_written": n * 4, "ms": ms,
+                          "GBps_read_plus_write": 2 * n * 4 / ms / 1e6}), flush=True)
+        return
+
     import looped_transformer_decode_amd as L
     from synth import gen
     from synth.device import fill_hash_normal
@@ -172,11 +194,12 @@ def main():
     pos = torch.full((w.B,), w.N - 1, dtype=torch.int32, device=dev)
     start = torch.full((w.B,), w.N - w.n_new, dtype=torch.int32, device=dev)
     out = torch.empty((w.B, w.H, w.d), dtype=torch.float32, device=dev)
-    ws = L.workspace(store)
+    ws = L.workspace(store, args.splits)
     decode = L.lla2d_decode_attn if is2d else L.lla_decode_attn
     encode = L.lla2d_encode_append if is2d else L.lla_encode_append
     stream = torch.cuda.current_stream()
-    log(f"[bench] path={L.lla_decode_path(store)} splits={L.lla_decode_auto_splits(store)}")
+    log(f"[bench] path={L.lla_decode_path(store)} "
+        f"splits={args.splits or L.lla_decode_auto_splits(store)}")
 
     def step(events=None):
         for t in range(w.T):
@@ -185,7 +208,7 @@ def main():
                     events[0].append(torch.cuda.Event(enable_timing=True))
                     events[0][-1].record(stream)
                 decode(store, l, t, q[l, t], wk[l, t], wv[l, t], mk[l, t], mv[l, t], pos, rope,
-                       out, ws)
+                       out, ws, n_splits=args.splits)
                 if events is not None:
                     events[1].append(torch.cuda.Event(enable_timing=True))
                     events[1][-1].record(stream)
@@ -223,7 +246,7 @@ def main():
                    "ctx": w.N, "heads": w.H, "d_head": w.d, "loops": w.T, "r_k": w.r_k,
                    "r_v": w.r_v, "rho": str(L.lla_compression_ratio(store)),
                    "calls_per_step": w.D * w.T, "encode_appends_per_step": 0 if args.no_encode
-                   else w.D, "splits": L.lla_decode_auto_splits(store),
+                   else w.D, "splits": args.splits or L.lla_decode_auto_splits(store),
                    "path": L.lla_decode_path(store)},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),

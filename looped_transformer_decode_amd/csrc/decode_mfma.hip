@@ -60,12 +60,14 @@ struct Cfg {
   static constexpr int CPH = REC / 16;          // 16-byte chunks per head record
   static constexpr int CPT = HG * CPH;          // chunks per slot of the group
   static constexpr int TILE_BYTES = kTile * CPT * 16;
-  static constexpr int STAGE_BYTES = TILE_BYTES + kPhiTileBytes;
-  static constexpr int NSTAGE = (kLdsMax / STAGE_BYTES) > 3 ? 3 : (kLdsMax / STAGE_BYTES);
-  static constexpr int LDS_BYTES = NSTAGE * STAGE_BYTES;
-  static constexpr int LOADS_STORE = kTile * CPT / NT;
-  static constexpr int LOADS_PHI = (kPhiTileBytes / 16) / NT;
-  static constexpr int LOADS = LOADS_STORE + LOADS_PHI;
+  // Store tiles are prefetched NS-1 tiles ahead; the (L2-resident) phi
+  // tiles one tile ahead in two buffers of their own.
+  static constexpr int NS_FIT = (kLdsMax - 2 * kPhiTileBytes) / TILE_BYTES;
+  static constexpr int NS = NS_FIT > 3 ? 3 : NS_FIT;
+  static constexpr int PHI_OFF = NS * TILE_BYTES;
+  static constexpr int LDS_BYTES = PHI_OFF + 2 * kPhiTileBytes;
+  static constexpr int LS = kTile * CPT / NT;             // store loads per thread per tile
+  static constexpr int LP = (kPhiTileBytes / 16) / NT;    // phi loads per thread per tile
   static constexpr int PAIRS = HPW / 2;
   static constexpr int KT = RK / 16;            // 32-row MFMA tiles per head pair
   static constexpr int CK_CHUNKS = RK / 8;
@@ -74,36 +76,25 @@ struct Cfg {
   static_assert(RK % 16 == 0 && RV % 8 == 0, "rank granularity");
   static_assert(CPT % 8 == 0, "swizzle works on groups of 8 chunks");
   static_assert((kTile * CPT) % NT == 0 && (kPhiTileBytes / 16) % NT == 0, "load split");
-  static_assert(NSTAGE >= 2, "two LDS stages must fit");
-  static_assert(NSTAGE * LOADS <= 63, "vmcnt range");
+  static_assert(NS >= 2, "two store stages must fit");
+  static_assert(2 * LS + LP <= 63, "vmcnt range");
   // LDS used before the pipeline starts: rotated queries + W_up,k,t of the group
   static_assert(HG * kD * 4 + HG * kD * RK * 2 <= LDS_BYTES, "setup staging");
   // LDS used by the final cross-lane reduction
   static_assert(NW * PAIRS * 64 * (RV + 2) * 4 <= LDS_BYTES, "reduction staging");
 };
 
-__device__ __forceinline__ void wait_vm(int n_outstanding_tiles, int loads) {
-  // Constant immediates only: n_outstanding_tiles is 0, 1 or 2.
-  if (n_outstanding_tiles <= 0) {
-    __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
-  } else if (n_outstanding_tiles == 1) {
-    switch (loads) {
-#define LLA_W(n) case n: __builtin_amdgcn_s_waitcnt(waitcnt_vm(n)); break;
-      LLA_W(2) LLA_W(3) LLA_W(4) LLA_W(5) LLA_W(6) LLA_W(7) LLA_W(8) LLA_W(9) LLA_W(10)
-      LLA_W(11) LLA_W(12) LLA_W(13) LLA_W(14) LLA_W(15) LLA_W(16) LLA_W(17) LLA_W(18)
-      LLA_W(19) LLA_W(20) LLA_W(21) LLA_W(22) LLA_W(23) LLA_W(24) LLA_W(25) LLA_W(26)
-      LLA_W(27) LLA_W(28) LLA_W(29) LLA_W(30) LLA_W(31)
-      default: __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
-    }
-  } else {
-    switch (2 * loads) {
-      LLA_W(4) LLA_W(6) LLA_W(8) LLA_W(10) LLA_W(12) LLA_W(14) LLA_W(16) LLA_W(18) LLA_W(20)
-      LLA_W(22) LLA_W(24) LLA_W(26) LLA_W(28) LLA_W(30) LLA_W(32) LLA_W(34) LLA_W(36)
-      LLA_W(38) LLA_W(40) LLA_W(42) LLA_W(44) LLA_W(46) LLA_W(48) LLA_W(50) LLA_W(52)
-      LLA_W(54) LLA_W(56) LLA_W(58) LLA_W(60) LLA_W(62)
+// Wait until at most n vector-memory operations are outstanding (0 <= n
+// <= 63); s_waitcnt takes an immediate, so dispatch over the values.
+__device__ __forceinline__ void wait_vm(int n) {
+  switch (n) {
+#define LLA_W(k) case k: __builtin_amdgcn_s_waitcnt(waitcnt_vm(k)); break;
+#define LLA_W8(k) LLA_W(k) LLA_W(k + 1) LLA_W(k + 2) LLA_W(k + 3) LLA_W(k + 4) LLA_W(k + 5) \
+    LLA_W(k + 6) LLA_W(k + 7)
+    LLA_W8(0) LLA_W8(8) LLA_W8(16) LLA_W8(24) LLA_W8(32) LLA_W8(40) LLA_W8(48) LLA_W8(56)
+#undef LLA_W8
 #undef LLA_W
-      default: __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
-    }
+    default: __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
   }
 }
 
@@ -225,25 +216,28 @@ __global__ __launch_bounds__(NW * 64, 1) void decode_mfma_split(DecodeParams p) 
       const_cast<uint16_t *>(p.rope_bf16), (short)0, phi_tiles * kPhiTileBytes, 0x00020000);
   const uint32_t tok_stride = (uint32_t)p.Hs * p.R * 2;  // bytes per slot in the slab
   const uint32_t grp_off = (uint32_t)h0 * C::REC;
-  uint32_t voff[C::LOADS_STORE];
+  uint32_t voff[C::LS];
 #pragma unroll
-  for (int n = 0; n < C::LOADS_STORE; ++n) {
+  for (int n = 0; n < C::LS; ++n) {
     const int P = n * C::NT + tid;           // LDS chunk this lane fills
     const int tj = P / C::CPT, qq = P % C::CPT;
     voff[n] = tj * tok_stride + grp_off + (uint32_t)((qq ^ (tj & 7)) * 16);
   }
-  auto issue = [&](int it, int buf) {
-    char *sb = lds + buf * C::STAGE_BYTES;
+  auto issue_store = [&](int it) {
+    char *sb = lds + (it % C::NS) * C::TILE_BYTES;
     const uint32_t tile_off = (uint32_t)(t0 + it * kTile) * tok_stride;
 #pragma unroll
-    for (int n = 0; n < C::LOADS_STORE; ++n)
+    for (int n = 0; n < C::LS; ++n)
       __builtin_amdgcn_raw_ptr_buffer_load_lds(
           rs, (LDS_AS void *)(sb + (n * C::NT + wave * 64) * 16), 16, voff[n] + tile_off, 0, 0, 0);
+  };
+  auto issue_phi = [&](int it) {
+    char *pb = lds + C::PHI_OFF + (it & 1) * kPhiTileBytes;
     const uint32_t phi_off = (uint32_t)(t0 / kTile + it) * kPhiTileBytes;
 #pragma unroll
-    for (int n = 0; n < C::LOADS_PHI; ++n)
+    for (int n = 0; n < C::LP; ++n)
       __builtin_amdgcn_raw_ptr_buffer_load_lds(
-          rphi, (LDS_AS void *)(sb + C::TILE_BYTES + (n * C::NT + wave * 64) * 16), 16,
+          rphi, (LDS_AS void *)(pb + (n * C::NT + wave * 64) * 16), 16,
           phi_off + (uint32_t)(n * C::NT + tid) * 16, 0, 0, 0);
   };
 
@@ -257,19 +251,32 @@ __global__ __launch_bounds__(NW * 64, 1) void decode_mfma_split(DecodeParams p) 
     for (int r = 0; r < RV; ++r) acc[pp][r] = 0.f;
   }
 
-  for (int st = 0; st < C::NSTAGE - 1; ++st)
-    if (st < ntiles) issue(st, st);
+  // Issue order: iteration it issues phi(it+1), then store(it+NS-1).  The
+  // prologue replays the issues of the iterations before 0.
+  for (int k = 0; k + 2 < C::NS; ++k)
+    if (k < ntiles) issue_store(k);
+  issue_phi(0);
+  if (C::NS - 2 < ntiles) issue_store(C::NS - 2);
 
   const int tj = lane & 31;
   const int swz = tj & 7;
   for (int it = 0; it < ntiles; ++it) {
-    const int buf = it % C::NSTAGE;
-    if (it + C::NSTAGE - 1 < ntiles) issue(it + C::NSTAGE - 1, (it + C::NSTAGE - 1) % C::NSTAGE);
-    wait_vm(min(C::NSTAGE - 1, ntiles - 1 - it), C::LOADS);
+    if (it + 1 < ntiles) issue_phi(it + 1);
+    if (it + C::NS - 1 < ntiles) issue_store(it + C::NS - 1);
+    // Wait for store(it) and phi(it): count what was issued after the later
+    // of the two (loads complete in issue order).
+    int after = 0;
+    if (C::NS >= 3) {
+      after = (it + C::NS - 2 < ntiles ? C::LS : 0) + (it + 1 < ntiles ? C::LP : 0) +
+              (it + C::NS - 1 < ntiles ? C::LS : 0);
+    } else {
+      after = (it + 1 < ntiles ? C::LP + C::LS : 0);
+    }
+    wait_vm(after);
     __builtin_amdgcn_s_barrier();
 
-    const char *sb = lds + buf * C::STAGE_BYTES;
-    const char *phb = sb + C::TILE_BYTES;
+    const char *sb = lds + (it % C::NS) * C::TILE_BYTES;
+    const char *phb = lds + C::PHI_OFF + (it & 1) * kPhiTileBytes;
     bf16x8_t bphi[kKSteps];
 #pragma unroll
     for (int st = 0; st < kKSteps; ++st)

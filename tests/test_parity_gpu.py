@@ -227,17 +227,18 @@ ENCODE_SHAPES = [
 
 
 def check_latents(got, want, dtype, K):
-    """Stored latents vs the oracle's exact value (rounded once by the GPU)."""
+    """Stored latents vs the oracle's exact value (rounded once by the GPU).
+    Returns the number of values that differ from the oracle's own rounding
+    (a float32 accumulation near a bf16 rounding tie may round the other
+    way; both results are correct)."""
     if dtype == "f32":
         np.testing.assert_allclose(got, want, rtol=0, atol=1e-5 * (1 + np.abs(want).max()))
-        return 1.0
+        return 0
     _, e = np.frexp(want)
     half_ulp = np.ldexp(1.0, np.maximum(e, -125) - 9)
     acc_bound = 4 * K * 2.0 ** -24 * (1 + np.abs(want))
     assert (np.abs(got - want) <= half_ulp + acc_bound).all()
-    exact = np.mean(got == O.bf16_round(want))
-    assert exact >= 0.98, exact
-    return exact
+    return int(np.sum(got != O.bf16_round(want)))
 
 
 @pytest.mark.parametrize("tmpl,kw", ENCODE_SHAPES, ids=[t for t, _ in ENCODE_SHAPES])
@@ -269,6 +270,7 @@ def test_encode_vs_oracle(device, tmpl, kw):
     torch.cuda.synchronize()
     got = from_device(store.tensor)
     written = np.zeros(w.store_shape[:3], bool)
+    flips, total = 0, 0
     for b in range(w.B):
         for j in range(n_new):
             slot = start[b] + j
@@ -279,7 +281,10 @@ def test_encode_vs_oracle(device, tmpl, kw):
             for h in range(w.store_heads):
                 for a, off, r in (("k", 0, w.r_k), ("v", w.r_k, w.r_v)):
                     want = O.encode(x[a][row, h], mu[a][h], wd[a][h])
-                    check_latents(got[b, layer, slot, h, off:off + r], want, w.dtype, K)
+                    flips += check_latents(got[b, layer, slot, h, off:off + r], want, w.dtype, K)
+                    total += r
+    say(f"  {total} latents, {flips} rounded the other way at a tie")
+    assert flips <= 0.02 * total
     assert (got[~written] == sentinel).all()
 
 
