@@ -67,12 +67,13 @@ uint16_t f64_to_bf16(double v) {
 }
 
 int32_t auto_splits(const lla_store_t *s, bool mfma) {
-  // Enough workgroups to cover 256 CUs several times, each split at least
-  // 256 slots long so that the per-workgroup setup stays amortised.
+  // Enough workgroups to cover the 256 CUs three times (the fast path holds
+  // one workgroup per CU), each split at least 256 slots long so that the
+  // per-workgroup setup stays amortised.
   const int64_t per_split =
       mfma ? (int64_t)s->batch * (s->heads / lla::decode_mfma_group_heads(s->r_k, s->r_v))
            : (int64_t)s->batch * s->heads;
-  const int64_t target = mfma ? 1024 : 2048;
+  const int64_t target = mfma ? 768 : 2048;
   int64_t S = (target + per_split - 1) / per_split;
   const int64_t max_s = std::max<int64_t>(1, s->max_ctx / 256);
   if (S > max_s) S = max_s;
