@@ -1,0 +1,270 @@
+// Append-time encoder on the matrix cores, for bf16 stores ("Looped Latent
+// Attention: Cross-Loop KV Compression for Looped Transformers", Sec. 3
+// Eq. 2):  c = (x - mu) W_down  for every new token, stored head and axis.
+//
+// The product is split as c = x W_down - mu W_down.  x and W_down are bf16,
+// so x W_down runs on v_mfma_f32_16x16x32_bf16 with exact products and fp32
+// sums.  mu is float32 and not representable in bf16; it is split exactly
+// into three bf16 parts (mu = hi + mid + lo, 8 + 8 + 8 significand bits),
+// which occupy three rows of one extra MFMA row tile, so mu W_down is also
+// formed from exact products.  The latent is rounded once to bf16 (nearest,
+// ties to even).
+//
+// Work split.  A workgroup of four waves owns (row block, stored head, axis);
+// each wave owns MT tiles of 16 rows (rows = (sequence, new token)).  The
+// stacked length K is walked in chunks of 128.  Rows of x stream from HBM
+// straight into registers: within a chunk, lane group g = lane/16 reads 64
+// contiguous bytes of its row, and the contraction index is permuted
+// accordingly (step s, group g, element e <-> k = 32 g + 8 s + e), so every
+// row is read in whole 256-byte segments.  The W_down chunk of the head is
+// shared by the four waves: it is loaded once per workgroup and written to
+// LDS transposed ([column][k], padded rows) so that each lane's B fragment
+// is one 16-byte read.  Chunk c+1 (x into registers, W_down into the other
+// LDS buffer) is fetched while chunk c is multiplied.
+#include "lla_device.h"
+#include "lla_internal.h"
+
+namespace lla {
+namespace detail {
+
+typedef __attribute__((__vector_size__(8 * sizeof(short)))) short bf16x8_t;
+typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4_t;
+typedef __attribute__((__vector_size__(4 * sizeof(uint32_t)))) uint32_t u32x4_t;
+
+constexpr int kKc = 128;           // contraction chunk
+constexpr int kPitch = kKc + 8;    // LDS row pitch of the transposed W_down chunk (elements)
+constexpr int kThreads = 256;
+constexpr int kMaxNT = 8;          // r <= 128
+
+__host__ __device__ constexpr size_t encode_lds_bytes(int r) {
+  return 2 * (size_t)r * kPitch * 2   // W_down chunk, two buffers
+         + 2 * kKc * 4                // mu chunk, two buffers
+         + (size_t)r * 4;             // mu W_down
+}
+
+__device__ __forceinline__ bf16x8_t as_bf16x8(u32x4_t v) { return __builtin_bit_cast(bf16x8_t, v); }
+
+// Part `which` (0 = hi, 1 = mid, 2 = lo) of the exact three-way bf16 split
+// of a float32 value.
+__device__ __forceinline__ uint16_t split3(float v, int which) {
+  const uint16_t h = f32_to_bf16_bits(v);
+  if (which == 0) return h;
+  const float r1 = v - bf16_bits_to_f32(h);  // exact
+  const uint16_t m = f32_to_bf16_bits(r1);
+  if (which == 1) return m;
+  return f32_to_bf16_bits(r1 - bf16_bits_to_f32(m));  // exact remainder
+}
+
+template <int MT, int NT>
+__device__ __forceinline__ void encode_body(const EncodeParams &p, int axis, char *lds) {
+  constexpr int R = NT * 16;
+  constexpr int PAIRS = kKc / 2 * (R / 8);        // (k pair, 8-column group) units per chunk
+  constexpr int PPT = (PAIRS + kThreads - 1) / kThreads;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int g = lane >> 4, rr = lane & 15;
+  const int hs = blockIdx.y;
+  const int M = p.B * p.n_new;
+  const int K = p.K;
+  const int nc = K / kKc;
+  const int row0 = (blockIdx.x * 4 + wave) * (16 * MT);
+
+  uint16_t *wt = reinterpret_cast<uint16_t *>(lds);                       // [2][R][kPitch]
+  float *mul = reinterpret_cast<float *>(lds + 2 * R * kPitch * 2);        // [2][kKc]
+  float *bias = mul + 2 * kKc;                                             // [R]
+
+  const uint16_t *wd = reinterpret_cast<const uint16_t *>(p.wd[axis]) + (int64_t)hs * K * R;
+  const float *mu = p.mu[axis] + (int64_t)hs * K;
+  const u32x4_t *xrow[MT];
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt) {
+    const int row = min(row0 + mt * 16 + rr, M - 1);  // rows past M: read a valid row, never stored
+    xrow[mt] = reinterpret_cast<const u32x4_t *>(reinterpret_cast<const uint16_t *>(p.x[axis]) +
+                                                 ((int64_t)row * p.Hs + hs) * K) + 4 * g;
+  }
+
+  // ---- staging of one W_down / mu chunk: global -> registers -> LDS ----
+  u32x4_t wreg[PPT][2];
+  float4 mureg;
+  auto fetch_w = [&](int c) {
+#pragma unroll
+    for (int i = 0; i < PPT; ++i) {
+      const int v = tid + i * kThreads;
+      if (v < PAIRS) {
+        const int kp = v / (R / 8), n0 = (v % (R / 8)) * 8;
+        const u32x4_t *src =
+            reinterpret_cast<const u32x4_t *>(wd + (int64_t)(c * kKc + 2 * kp) * R + n0);
+        wreg[i][0] = src[0];
+        wreg[i][1] = src[R / 8];
+      }
+    }
+    if (tid < kKc / 4) mureg = reinterpret_cast<const float4 *>(mu + c * kKc)[tid];
+  };
+  auto store_w = [&](int buf) {
+    uint16_t *w = wt + buf * R * kPitch;
+#pragma unroll
+    for (int i = 0; i < PPT; ++i) {
+      const int v = tid + i * kThreads;
+      if (v < PAIRS) {
+        const int kp = v / (R / 8), n0 = (v % (R / 8)) * 8;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const uint32_t lo = (wreg[i][0][e / 2] >> ((e & 1) * 16)) & 0xFFFFu;
+          const uint32_t hi = (wreg[i][1][e / 2] >> ((e & 1) * 16)) & 0xFFFFu;
+          *reinterpret_cast<uint32_t *>(w + (n0 + e) * kPitch + 2 * kp) = lo | (hi << 16);
+        }
+      }
+    }
+    if (tid < kKc / 4) reinterpret_cast<float4 *>(mul + buf * kKc)[tid] = mureg;
+  };
+
+  // ---- accumulators ----
+  f32x4_t acc[MT][NT];
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) acc[mt][nt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  // mu W_down: wave w owns the column tiles nt with nt % 4 == w
+  constexpr int NB = (NT + 3) / 4;
+  f32x4_t accb[NB];
+#pragma unroll
+  for (int i = 0; i < NB; ++i) accb[i] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+  u32x4_t xa[2][MT][4];
+  auto fetch_x = [&](int c, u32x4_t (&dst)[MT][4]) {
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+      for (int s = 0; s < 4; ++s) dst[mt][s] = __builtin_nontemporal_load(xrow[mt] + c * 16 + s);
+  };
+
+  auto compute = [&](int buf, const u32x4_t (&xc)[MT][4]) {
+    const uint16_t *w = wt + buf * R * kPitch;
+    const float *m = mul + buf * kKc;
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      bf16x8_t amu;
+      {
+        // rows 0..2 of the mu tile: hi / mid / lo parts of mu; other rows zero
+        const float4 m0 = *reinterpret_cast<const float4 *>(m + 32 * g + 8 * s);
+        const float4 m1 = *reinterpret_cast<const float4 *>(m + 32 * g + 8 * s + 4);
+        const float mv[8] = {m0.x, m0.y, m0.z, m0.w, m1.x, m1.y, m1.z, m1.w};
+#pragma unroll
+        for (int e = 0; e < 8; ++e) amu[e] = (rr < 3) ? (short)split3(mv[e], rr) : (short)0;
+      }
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) {
+        const bf16x8_t bw =
+            *reinterpret_cast<const bf16x8_t *>(w + (nt * 16 + rr) * kPitch + 32 * g + 8 * s);
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt)
+          acc[mt][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(xc[mt][s]), bw,
+                                                                 acc[mt][nt], 0, 0, 0);
+        if (nt % 4 == wave)
+          accb[nt / 4] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(amu, bw, accb[nt / 4], 0, 0, 0);
+      }
+    }
+  };
+
+  // ---- pipeline over chunks (unrolled by two: register buffers are static) ----
+  fetch_x(0, xa[0]);
+  fetch_w(0);
+  store_w(0);
+  __syncthreads();
+  for (int c = 0; c < nc; c += 2) {
+    if (c + 1 < nc) {
+      fetch_x(c + 1, xa[1]);
+      fetch_w(c + 1);
+    }
+    compute(0, xa[0]);
+    if (c + 1 < nc) store_w(1);
+    __syncthreads();
+    if (c + 1 >= nc) break;
+    if (c + 2 < nc) {
+      fetch_x(c + 2, xa[0]);
+      fetch_w(c + 2);
+    }
+    compute(1, xa[1]);
+    if (c + 2 < nc) store_w(0);
+    __syncthreads();
+  }
+
+  // ---- mu W_down: rows 0..2 of the mu tile live in lanes 0..15 ----
+#pragma unroll
+  for (int i = 0; i < NB; ++i) {
+    const int nt = 4 * i + wave;
+    if (nt < NT && g == 0) bias[nt * 16 + rr] = (accb[i][2] + accb[i][1]) + accb[i][0];
+  }
+  __syncthreads();
+
+  // ---- c = x W - mu W, rounded to bf16, written at the token's slot ----
+  uint16_t *st = reinterpret_cast<uint16_t *>(p.store);
+  const int koff = axis ? p.rk : 0;
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int row = row0 + mt * 16 + 4 * g + i;
+      if (row >= M) continue;
+      const int b = row / p.n_new, jn = row % p.n_new;
+      const int slot = p.start[b] + jn;
+      if (slot < 0 || slot >= p.N) continue;
+      uint16_t *dst = st + ((((int64_t)b * p.D + p.layer) * p.N + slot) * p.Hs + hs) * p.R + koff;
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt)
+        dst[nt * 16 + rr] = f32_to_bf16_bits(acc[mt][nt][i] - bias[nt * 16 + rr]);
+    }
+  }
+}
+
+template <int MT>
+__global__ __launch_bounds__(kThreads) void encode_mfma(EncodeParams p) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  extern __shared__ __attribute__((aligned(16))) char lds[];
+  const int axis = blockIdx.z;
+  const int r = axis ? p.rv : p.rk;
+  switch (r >> 4) {
+    case 1: encode_body<MT, 1>(p, axis, lds); break;
+    case 2: encode_body<MT, 2>(p, axis, lds); break;
+    case 3: encode_body<MT, 3>(p, axis, lds); break;
+    case 4: encode_body<MT, 4>(p, axis, lds); break;
+    case 5: encode_body<MT, 5>(p, axis, lds); break;
+    case 6: encode_body<MT, 6>(p, axis, lds); break;
+    case 7: encode_body<MT, 7>(p, axis, lds); break;
+    case 8: encode_body<MT, 8>(p, axis, lds); break;
+    default: break;
+  }
+#endif
+}
+
+}  // namespace detail
+
+using namespace detail;
+
+bool encode_mfma_supported(const EncodeParams &p, int dtype) {
+  auto al = [](const void *q) { return ((uintptr_t)q & 15u) == 0; };
+  return dtype == LLA_DT_BF16 && p.rk % 16 == 0 && p.rv % 16 == 0 && p.rk <= 16 * kMaxNT &&
+         p.rv <= 16 * kMaxNT && p.K % kKc == 0 && al(p.x[0]) && al(p.x[1]) && al(p.wd[0]) &&
+         al(p.wd[1]) && al(p.mu[0]) && al(p.mu[1]);
+}
+
+hipError_t launch_encode_mfma(const EncodeParams &p, hipStream_t st) {
+  const int M = p.B * p.n_new;
+  const size_t lds = encode_lds_bytes(p.rk > p.rv ? p.rk : p.rv);
+  // two row tiles per wave when that still gives a full wave of workgroups
+  const bool two = (int64_t)((M + 127) / 128) * p.Hs * 2 >= 256;
+  const void *fn = two ? reinterpret_cast<const void *>(&encode_mfma<2>)
+                       : reinterpret_cast<const void *>(&encode_mfma<1>);
+  const hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+  if (e != hipSuccess) return e;
+  if (two) {
+    const dim3 grid((M + 127) / 128, p.Hs, 2);
+    hipLaunchKernelGGL(encode_mfma<2>, grid, dim3(kThreads), lds, st, p);
+  } else {
+    const dim3 grid((M + 63) / 64, p.Hs, 2);
+    hipLaunchKernelGGL(encode_mfma<1>, grid, dim3(kThreads), lds, st, p);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace lla

@@ -185,7 +185,9 @@ lla_status_t encode_impl(const lla_store_t *st, int32_t want_variant, int32_t la
   p.wd[0] = wdk;
   p.wd[1] = wdv;
   p.start = start;
-  const hipError_t he = lla::launch_encode_valu(p, st->dtype, stream);
+  const hipError_t he = lla::encode_mfma_supported(p, st->dtype)
+                            ? lla::launch_encode_mfma(p, stream)
+                            : lla::launch_encode_valu(p, st->dtype, stream);
   return he == hipSuccess ? LLA_OK : LLA_E_HIP;
 }
 

@@ -68,5 +68,7 @@ bool decode_mfma_supported(int32_t H, int32_t d, int32_t rk, int32_t rv, int32_t
 int32_t decode_mfma_group_heads(int32_t rk, int32_t rv);
 hipError_t launch_decode_mfma(const DecodeParams &p, hipStream_t s);
 hipError_t launch_encode_valu(const EncodeParams &p, int dtype, hipStream_t s);
+bool encode_mfma_supported(const EncodeParams &p, int dtype);
+hipError_t launch_encode_mfma(const EncodeParams &p, hipStream_t s);
 
 }  // namespace lla

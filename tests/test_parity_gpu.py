@@ -223,6 +223,9 @@ ENCODE_SHAPES = [
     ("long_recurrence_t16_ctx8k", dict(B=3, D=2, N=64, H=4)),
     ("lla2d_b256_ctx4k", dict(B=3, D=2, N=32, H=4)),
     ("tiny_fp32", dict(B=3, N=64)),
+    # enough rows for two 16-row tiles per wave and several row blocks
+    ("extreme_batch_b768_ctx4k", dict(B=260, D=2, N=16)),
+    ("bf16_b32_ctx4k", dict(B=70, D=2, N=16, H=4, T=1)),
 ]
 
 
@@ -241,7 +244,9 @@ def check_latents(got, want, dtype, K):
     return int(np.sum(got != O.bf16_round(want)))
 
 
-@pytest.mark.parametrize("tmpl,kw", ENCODE_SHAPES, ids=[t for t, _ in ENCODE_SHAPES])
+@pytest.mark.parametrize("tmpl,kw", ENCODE_SHAPES,
+                         ids=[f"{t}-{'-'.join(f'{k}{v}' for k, v in kw.items())}"
+                              for t, kw in ENCODE_SHAPES])
 def test_encode_vs_oracle(device, tmpl, kw):
     w = small(tmpl, **kw)
     n_new = 5
@@ -249,6 +254,9 @@ def test_encode_vs_oracle(device, tmpl, kw):
     codec = Codec(w)
     layer = w.D - 1
     start = np.array([0, w.N - n_new, w.N - 2, 17, 40][:w.B], dtype=np.int32)  # one overflows
+    if w.B > 5:
+        start = np.resize(start % max(1, w.N - n_new + 1), w.B).astype(np.int32)
+        start[2] = w.N - 2
     sentinel = from_device(to_device(np.full(1, 3.0), w.dtype, device))[0]
     store = new_store(w, device)
     store.tensor.fill_(sentinel)
@@ -270,6 +278,8 @@ def test_encode_vs_oracle(device, tmpl, kw):
     torch.cuda.synchronize()
     got = from_device(store.tensor)
     written = np.zeros(w.store_shape[:3], bool)
+    want = {a: np.stack([O.encode(x[a][:, h], mu[a][h], wd[a][h]) for h in range(w.store_heads)],
+                        axis=1) for a in "kv"}                 # [rows, H', r]
     flips, total = 0, 0
     for b in range(w.B):
         for j in range(n_new):
@@ -278,14 +288,70 @@ def test_encode_vs_oracle(device, tmpl, kw):
                 continue
             written[b, layer, slot] = True
             row = b * n_new + j
-            for h in range(w.store_heads):
-                for a, off, r in (("k", 0, w.r_k), ("v", w.r_k, w.r_v)):
-                    want = O.encode(x[a][row, h], mu[a][h], wd[a][h])
-                    flips += check_latents(got[b, layer, slot, h, off:off + r], want, w.dtype, K)
-                    total += r
+            for a, off, r in (("k", 0, w.r_k), ("v", w.r_k, w.r_v)):
+                flips += check_latents(got[b, layer, slot, :, off:off + r], want[a][row], w.dtype,
+                                       K)
+                total += r * w.store_heads
     say(f"  {total} latents, {flips} rounded the other way at a tie")
     assert flips <= 0.02 * total
     assert (got[~written] == sentinel).all()
+
+
+@pytest.mark.parametrize("name", ["extreme_batch_b768_ctx4k", "long_recurrence_t16_ctx8k",
+                                  "lla2d_b256_ctx4k", "bf16_b32_ctx4k"])
+def test_encode_full_size(device, name):
+    """The append of one benchmark step at full size (all sequences, all
+    heads, the step's n_new tokens) into a full-size store, as the benchmark
+    launches it: every written latent against the oracle, and the slots on
+    either side of each append untouched."""
+    w = WORKLOADS[name]
+    n_new = w.n_new
+    say(f"[encode full] {name}: B={w.B} n_new={n_new} H'={w.store_heads} K={w.T * w.width}")
+    torch.cuda.empty_cache()
+    codec = Codec(w)
+    layer = 1
+    K = w.T * w.width
+    rng = np.random.default_rng(w.seed + 5)
+    start = rng.integers(1, w.N - n_new, size=w.B).astype(np.int32)
+    start[0] = w.N - n_new - 1
+    start[-1] = 1
+    sentinel = from_device(to_device(np.full(1, 3.0), w.dtype, device))[0]
+    store = new_store(w, device)
+    store.tensor[:, layer].fill_(sentinel)
+    x = {a: codec.x(a, layer, w.B * n_new) for a in "kv"}
+    mu = {a: codec.mu(a, layer) for a in "kv"}
+    wd = {a: codec.w_down(a, layer) for a in "kv"}
+    if w.variant == "2d":
+        args = [to_device(x[a].reshape(w.B, n_new, K), w.dtype, device) for a in "kv"]
+        args += [to_device(mu[a][0], "f32", device) for a in "kv"]
+        args += [to_device(wd[a][0], w.dtype, device) for a in "kv"]
+        fn = L.lla2d_encode_append
+    else:
+        args = [to_device(x[a].reshape(w.B, n_new, w.H, K), w.dtype, device) for a in "kv"]
+        args += [to_device(mu[a], "f32", device) for a in "kv"]
+        args += [to_device(wd[a], w.dtype, device) for a in "kv"]
+        fn = L.lla_encode_append
+    fn(store, layer, *args, torch.from_numpy(start).to(device))
+    torch.cuda.synchronize()
+    b_idx = torch.arange(w.B, device=device).repeat_interleave(n_new)
+    s_idx = (torch.from_numpy(start).to(device).long().repeat_interleave(n_new)
+             + torch.arange(n_new, device=device).repeat(w.B))
+    got = from_device(store.tensor[b_idx, layer, s_idx])            # [rows, H', R]
+    b_all = torch.arange(w.B, device=device)
+    st = torch.from_numpy(start).to(device).long()
+    before = from_device(store.tensor[b_all, layer, st - 1])
+    after = from_device(store.tensor[b_all, layer, st + n_new])
+    assert (before == sentinel).all() and (after == sentinel).all()
+    flips, total = 0, 0
+    for a, off, r in (("k", 0, w.r_k), ("v", w.r_k, w.r_v)):
+        for h in range(w.store_heads):
+            want = O.encode(x[a][:, h], mu[a][h], wd[a][h])           # [rows, r]
+            flips += check_latents(got[:, h, off:off + r], want, w.dtype, K)
+            total += want.size
+    say(f"  {total} latents, {flips} rounded the other way at a tie")
+    assert flips <= 0.02 * total
+    del store
+    torch.cuda.empty_cache()
 
 
 # ----------------------------------------------------------------- full size
