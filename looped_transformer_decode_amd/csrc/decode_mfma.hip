@@ -5,7 +5,8 @@
 // sequence b, head h, loop t and every slot j <= pos[b]
 //     s_j = scale * RoPE(q, pos) . RoPE(W_up,k,t c_k,j + mu_k,t, j)
 // followed by an online softmax and the latent-space value average
-// sum_j p_j c_v,j (the merge kernel applies W_up,v,t and mu_v,t once).
+// sum_j p_j c_v,j; W_up,v,t and mu_v,t are applied once at the end (here
+// when the context is not split, else by the merge kernel).
 //
 // How.  RoPE is a rotation by j*theta_i of each pair (i, i + d/2), so with
 // phi_j = [cos(j theta); sin(j theta)] in R^d the score is bilinear in the
@@ -80,8 +81,9 @@ struct Cfg {
   static_assert(2 * LS + LP <= 63, "vmcnt range");
   // LDS used before the pipeline starts: rotated queries + W_up,k,t of the group
   static_assert(HG * kD * 4 + HG * kD * RK * 2 <= LDS_BYTES, "setup staging");
-  // LDS used by the final cross-lane reduction
-  static_assert(NW * PAIRS * 64 * (RV + 2) * 4 <= LDS_BYTES, "reduction staging");
+  // LDS used by the final cross-lane reduction and the combined partials
+  static_assert((NW * PAIRS * 64 + HG) * (RV + 2) * 4 <= LDS_BYTES, "reduction staging");
+  static_assert(RV % 8 == 0, "W_up,v,t rows are read as 16-byte vectors");
 };
 
 // Wait until at most n vector-memory operations are outstanding (0 <= n
@@ -356,6 +358,7 @@ __global__ __launch_bounds__(NW * 64, 1) void decode_mfma_split(DecodeParams p) 
     for (int r = 0; r < RV; ++r) dst[2 + r] = acc[pp][r];
   }
   __syncthreads();
+  float *comb = red + NW * C::PAIRS * 64 * (RV + 2);  // [HG][RV + 2], one context split
   for (int o = tid; o < C::HG * (RV + 2); o += C::NT) {
     const int hl = o / (RV + 2), r = o % (RV + 2);
     const int w = hl / HPW, pp = (hl % HPW) / 2, half = hl & 1;
@@ -372,7 +375,34 @@ __global__ __launch_bounds__(NW * 64, 1) void decode_mfma_split(DecodeParams p) 
         if (mi != -INFINITY) v = fmaf(src[i * (RV + 2) + r], exp2f(mi - M), v);
       }
     }
-    p.ws[((int64_t)(b * p.H + h0 + hl) * p.S + s) * (RV + 2) + r] = v;
+    if (p.S == 1)
+      comb[o] = v;
+    else
+      p.ws[((int64_t)(b * p.H + h0 + hl) * p.S + s) * (RV + 2) + r] = v;
+  }
+  if (p.S == 1) {
+    // A single split holds the whole softmax: apply W_up,v,t and mu_v,t here
+    // (no merge launch).  out = W_up,v,t (acc / l) + mu_v,t, one thread per
+    // output element, the bf16 row of W_up,v,t read as 16-byte vectors.
+    __syncthreads();
+    for (int o = tid; o < C::HG * kD; o += C::NT) {
+      const int hl = o / kD, i = o % kD;
+      const float *c = comb + hl * (RV + 2);
+      const u32x4_t *wrow = reinterpret_cast<const u32x4_t *>(
+          reinterpret_cast<const uint16_t *>(p.wv) + ((int64_t)(h0 + hl) * kD + i) * RV);
+      float a = 0.f;
+#pragma unroll
+      for (int r8 = 0; r8 < RV / 8; ++r8) {
+        const u32x4_t wv = wrow[r8];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          a = fmaf(bf16_lo(wv[e]), c[2 + 8 * r8 + 2 * e], a);
+          a = fmaf(bf16_hi(wv[e]), c[3 + 8 * r8 + 2 * e], a);
+        }
+      }
+      const int64_t oi = ((int64_t)b * p.H + h0 + hl) * kD + i;
+      p.out[oi] = fmaf(a, 1.0f / c[1], p.muv[(int64_t)(h0 + hl) * kD + i]);
+    }
   }
 #endif
 }

@@ -121,30 +121,119 @@ __global__ __launch_bounds__(kThreads) void decode_valu_split(DecodeParams p) {
   if (tid < rv) part[2 + tid] = acc;
 }
 
-// Merge the context splits of one (sequence, head) by log-sum-exp and apply
-// the loop-t value up-projection once: out = W_up,v,t (A / L) + mu_v,t.
+// Merge the context splits of every (sequence, head) by log-sum-exp and
+// apply the loop-t value up-projection once: out = W_up,v,t (A / L) + mu_v,t.
+// A block covers merge_heads_per_block() heads of one sequence, one thread
+// per output element.
 template <typename E>
 __global__ __launch_bounds__(256) void decode_merge(DecodeParams p) {
-  const int h = blockIdx.x, b = blockIdx.y, tid = threadIdx.x;
+  const int tid = threadIdx.x, b = blockIdx.y;
   const int rv = p.rv, d = p.d, S = p.S;
-  extern __shared__ float abar[];  // [rv]
-  const float *part = p.ws + (int64_t)(b * p.H + h) * S * (rv + 2);
-  float M = -INFINITY;
-  for (int s = 0; s < S; ++s) M = fmaxf(M, part[s * (rv + 2)]);
-  float L = 0.f;
-  for (int s = 0; s < S; ++s) L += part[s * (rv + 2) + 1] * exp2f(part[s * (rv + 2)] - M);
-  for (int r = tid; r < rv; r += blockDim.x) {
-    float a = 0.f;
-    for (int s = 0; s < S; ++s) a += part[s * (rv + 2) + 2 + r] * exp2f(part[s * (rv + 2)] - M);
-    abar[r] = a / L;
+  const int hpb = merge_heads_per_block(d, rv);
+  const int h0 = blockIdx.x * hpb;
+  extern __shared__ float abar[];  // [hpb][rv]
+  for (int t = tid; t < hpb * rv; t += blockDim.x) {
+    const int hl = t / rv, r = t % rv;
+    if (h0 + hl >= p.H) continue;
+    const float *part = p.ws + (int64_t)(b * p.H + h0 + hl) * S * (rv + 2);
+    float M = -INFINITY;
+    for (int s = 0; s < S; ++s) M = fmaxf(M, part[s * (rv + 2)]);
+    float L = 0.f, A = 0.f;
+    for (int s = 0; s < S; ++s) {
+      const float *ps = part + s * (rv + 2);
+      if (ps[0] == -INFINITY) continue;  // empty split
+      const float f = exp2f(ps[0] - M);
+      L = fmaf(ps[1], f, L);
+      A = fmaf(ps[2 + r], f, A);
+    }
+    abar[t] = A / L;
   }
   __syncthreads();
-  const E *wv = reinterpret_cast<const E *>(p.wv) + (int64_t)h * d * rv;
+  const bool vec = sizeof(E) == 2 && rv % 8 == 0 && ((uintptr_t)p.wv & 15u) == 0;
+  for (int o = tid; o < hpb * d; o += blockDim.x) {
+    const int hl = o / d, i = o % d, h = h0 + hl;
+    if (h >= p.H) continue;
+    const float *ab = abar + hl * rv;
+    const E *w = reinterpret_cast<const E *>(p.wv) + ((int64_t)h * d + i) * rv;
+    float acc = 0.f;
+    if (vec) {
+      const uint4 *w4 = reinterpret_cast<const uint4 *>(w);
+      for (int r8 = 0; r8 < rv / 8; ++r8) {
+        const uint4 v = w4[r8];
+        const uint32_t u[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          acc = fmaf(bf16_lo(u[e]), ab[8 * r8 + 2 * e], acc);
+          acc = fmaf(bf16_hi(u[e]), ab[8 * r8 + 2 * e + 1], acc);
+        }
+      }
+    } else {
+      for (int r = 0; r < rv; ++r) acc = fmaf(load_elem(w, r), ab[r], acc);
+    }
+    p.out[((int64_t)b * p.H + h) * d + i] = acc + p.muv[(int64_t)h * d + i];
+  }
+}
+
+// Merge for LLA-2D stores: the same log-sum-exp merge, batched over
+// sequences so that each W_up,v,t head block (d x r_v) is read once per
+// kBT sequences instead of once per sequence.  Block = (head, sequence
+// tile); one thread per output element of the head.
+constexpr int kBT = 8;
+
+template <typename E>
+__global__ __launch_bounds__(256) void decode_merge_batched(DecodeParams p) {
+  const int h = blockIdx.x, b0 = blockIdx.y * kBT, tid = threadIdx.x;
+  const int rv = p.rv, d = p.d, S = p.S;
+  extern __shared__ float abar[];  // [kBT][rv]
+  for (int t = tid; t < kBT * rv; t += blockDim.x) {
+    const int bl = t / rv, r = t % rv, b = b0 + bl;
+    if (b >= p.B) {
+      abar[t] = 0.f;
+      continue;
+    }
+    const float *part = p.ws + (int64_t)(b * p.H + h) * S * (rv + 2);
+    float M = -INFINITY;
+    for (int s = 0; s < S; ++s) M = fmaxf(M, part[s * (rv + 2)]);
+    float L = 0.f, A = 0.f;
+    for (int s = 0; s < S; ++s) {
+      const float *ps = part + s * (rv + 2);
+      if (ps[0] == -INFINITY) continue;
+      const float f = exp2f(ps[0] - M);
+      L = fmaf(ps[1], f, L);
+      A = fmaf(ps[2 + r], f, A);
+    }
+    abar[t] = A / L;
+  }
+  __syncthreads();
+  const bool vec = sizeof(E) == 2 && rv % 8 == 0 && ((uintptr_t)p.wv & 15u) == 0;
   for (int i = tid; i < d; i += blockDim.x) {
-    float o = p.muv[(int64_t)h * d + i];
-    const E *w = wv + (int64_t)i * rv;
-    for (int r = 0; r < rv; ++r) o = fmaf(load_elem(w, r), abar[r], o);
-    p.out[((int64_t)b * p.H + h) * d + i] = o;
+    float acc[kBT];
+#pragma unroll
+    for (int bl = 0; bl < kBT; ++bl) acc[bl] = 0.f;
+    const E *w = reinterpret_cast<const E *>(p.wv) + ((int64_t)h * d + i) * rv;
+    if (vec) {
+      const uint4 *w4 = reinterpret_cast<const uint4 *>(w);
+      for (int r8 = 0; r8 < rv / 8; ++r8) {
+        const uint4 v = w4[r8];
+        const uint32_t u[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const float wf = (e & 1) ? bf16_hi(u[e / 2]) : bf16_lo(u[e / 2]);
+#pragma unroll
+          for (int bl = 0; bl < kBT; ++bl) acc[bl] = fmaf(wf, abar[bl * rv + 8 * r8 + e], acc[bl]);
+        }
+      }
+    } else {
+      for (int r = 0; r < rv; ++r) {
+        const float wf = load_elem(w, r);
+#pragma unroll
+        for (int bl = 0; bl < kBT; ++bl) acc[bl] = fmaf(wf, abar[bl * rv + r], acc[bl]);
+      }
+    }
+    const float mu = p.muv[(int64_t)h * d + i];
+#pragma unroll
+    for (int bl = 0; bl < kBT; ++bl)
+      if (b0 + bl < p.B) p.out[((int64_t)(b0 + bl) * p.H + h) * d + i] = acc[bl] + mu;
   }
 }
 
@@ -172,13 +261,25 @@ hipError_t launch_decode_valu(const DecodeParams &p, int dtype, hipStream_t st) 
   return dtype == LLA_DT_F32 ? launch_split_e<float>(p, st) : launch_split_e<bf16_t>(p, st);
 }
 
-hipError_t launch_decode_merge(const DecodeParams &p, int dtype, hipStream_t st) {
-  dim3 grid(p.H, p.B);
-  const size_t sm = sizeof(float) * p.rv;
+hipError_t launch_decode_merge_batched(const DecodeParams &p, int dtype, hipStream_t st) {
+  dim3 grid(p.H, (p.B + kBT - 1) / kBT);
+  const int threads = p.d >= 256 ? 256 : (p.d + 63) / 64 * 64;
+  const size_t sm = sizeof(float) * p.rv * kBT;
   if (dtype == LLA_DT_F32)
-    hipLaunchKernelGGL(decode_merge<float>, grid, dim3(128), sm, st, p);
+    hipLaunchKernelGGL(decode_merge_batched<float>, grid, dim3(threads), sm, st, p);
   else
-    hipLaunchKernelGGL(decode_merge<bf16_t>, grid, dim3(128), sm, st, p);
+    hipLaunchKernelGGL(decode_merge_batched<bf16_t>, grid, dim3(threads), sm, st, p);
+  return hipGetLastError();
+}
+
+hipError_t launch_decode_merge(const DecodeParams &p, int dtype, hipStream_t st) {
+  const int hpb = merge_heads_per_block(p.d, p.rv);
+  dim3 grid((p.H + hpb - 1) / hpb, p.B);
+  const size_t sm = sizeof(float) * p.rv * hpb;
+  if (dtype == LLA_DT_F32)
+    hipLaunchKernelGGL(decode_merge<float>, grid, dim3(256), sm, st, p);
+  else
+    hipLaunchKernelGGL(decode_merge<bf16_t>, grid, dim3(256), sm, st, p);
   return hipGetLastError();
 }
 

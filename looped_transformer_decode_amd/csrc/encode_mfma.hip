@@ -19,8 +19,9 @@
 // row is read in whole 256-byte segments.  The W_down chunk of the head is
 // shared by the four waves: it is loaded once per workgroup and written to
 // LDS transposed ([column][k], padded rows) so that each lane's B fragment
-// is one 16-byte read.  Chunk c+1 (x into registers, W_down into the other
-// LDS buffer) is fetched while chunk c is multiplied.
+// is one 16-byte read; the three bf16 parts of the mu chunk go to LDS with
+// it.  While chunk c is multiplied, x of chunk c+2 and W_down of chunk c+1
+// are in flight.
 #include "lla_device.h"
 #include "lla_internal.h"
 
@@ -38,7 +39,7 @@ constexpr int kMaxNT = 8;          // r <= 128
 
 __host__ __device__ constexpr size_t encode_lds_bytes(int r) {
   return 2 * (size_t)r * kPitch * 2   // W_down chunk, two buffers
-         + 2 * kKc * 4                // mu chunk, two buffers
+         + 2 * 3 * kKc * 2            // hi / mid / lo parts of the mu chunk, two buffers
          + (size_t)r * 4;             // mu W_down
 }
 
@@ -70,8 +71,8 @@ __device__ __forceinline__ void encode_body(const EncodeParams &p, int axis, cha
   const int row0 = (blockIdx.x * 4 + wave) * (16 * MT);
 
   uint16_t *wt = reinterpret_cast<uint16_t *>(lds);                       // [2][R][kPitch]
-  float *mul = reinterpret_cast<float *>(lds + 2 * R * kPitch * 2);        // [2][kKc]
-  float *bias = mul + 2 * kKc;                                             // [R]
+  uint16_t *mus = wt + 2 * R * kPitch;                                     // [2][3][kKc]
+  float *bias = reinterpret_cast<float *>(mus + 2 * 3 * kKc);              // [R]
 
   const uint16_t *wd = reinterpret_cast<const uint16_t *>(p.wd[axis]) + (int64_t)hs * K * R;
   const float *mu = p.mu[axis] + (int64_t)hs * K;
@@ -115,7 +116,16 @@ __device__ __forceinline__ void encode_body(const EncodeParams &p, int axis, cha
         }
       }
     }
-    if (tid < kKc / 4) reinterpret_cast<float4 *>(mul + buf * kKc)[tid] = mureg;
+    if (tid < kKc / 4) {
+      const float mv[4] = {mureg.x, mureg.y, mureg.z, mureg.w};
+#pragma unroll
+      for (int part = 0; part < 3; ++part) {
+        uint2 pk;
+        pk.x = split3(mv[0], part) | ((uint32_t)split3(mv[1], part) << 16);
+        pk.y = split3(mv[2], part) | ((uint32_t)split3(mv[3], part) << 16);
+        *reinterpret_cast<uint2 *>(mus + (buf * 3 + part) * kKc + 4 * tid) = pk;
+      }
+    }
   };
 
   // ---- accumulators ----
@@ -130,7 +140,7 @@ __device__ __forceinline__ void encode_body(const EncodeParams &p, int axis, cha
 #pragma unroll
   for (int i = 0; i < NB; ++i) accb[i] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
-  u32x4_t xa[2][MT][4];
+  u32x4_t xa[3][MT][4];
   auto fetch_x = [&](int c, u32x4_t (&dst)[MT][4]) {
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt)
@@ -140,18 +150,13 @@ __device__ __forceinline__ void encode_body(const EncodeParams &p, int axis, cha
 
   auto compute = [&](int buf, const u32x4_t (&xc)[MT][4]) {
     const uint16_t *w = wt + buf * R * kPitch;
-    const float *m = mul + buf * kKc;
+    // rows 0..2 of the mu tile: hi / mid / lo parts of mu; other rows zero
+    const uint16_t *mrow = mus + (buf * 3 + (rr < 3 ? rr : 0)) * kKc;
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
-      bf16x8_t amu;
-      {
-        // rows 0..2 of the mu tile: hi / mid / lo parts of mu; other rows zero
-        const float4 m0 = *reinterpret_cast<const float4 *>(m + 32 * g + 8 * s);
-        const float4 m1 = *reinterpret_cast<const float4 *>(m + 32 * g + 8 * s + 4);
-        const float mv[8] = {m0.x, m0.y, m0.z, m0.w, m1.x, m1.y, m1.z, m1.w};
-#pragma unroll
-        for (int e = 0; e < 8; ++e) amu[e] = (rr < 3) ? (short)split3(mv[e], rr) : (short)0;
-      }
+      const u32x4_t mz = {0u, 0u, 0u, 0u};
+      const bf16x8_t amu =
+          as_bf16x8(rr < 3 ? *reinterpret_cast<const u32x4_t *>(mrow + 32 * g + 8 * s) : mz);
 #pragma unroll
       for (int nt = 0; nt < NT; ++nt) {
         const bf16x8_t bw =
@@ -166,27 +171,30 @@ __device__ __forceinline__ void encode_body(const EncodeParams &p, int axis, cha
     }
   };
 
-  // ---- pipeline over chunks (unrolled by two: register buffers are static) ----
-  fetch_x(0, xa[0]);
+  // ---- pipeline over chunks ----
+  // x is fetched two chunks ahead (three register buffers, so the loop is
+  // unrolled by three), W_down / mu one chunk ahead through registers into
+  // the other LDS buffer.  Loads complete in issue order: storing W_down
+  // chunk c+1 waits only for loads issued before it, never for x of c+2.
+  auto step = [&](int c, const u32x4_t (&cur)[MT][4], u32x4_t (&ahead)[MT][4]) {
+    if (c + 2 < nc) fetch_x(c + 2, ahead);
+    compute(c & 1, cur);
+    if (c + 1 < nc) store_w((c + 1) & 1);
+    if (c + 2 < nc) fetch_w(c + 2);
+    __syncthreads();
+  };
   fetch_w(0);
+  fetch_x(0, xa[0]);
+  if (nc > 1) fetch_x(1, xa[1]);
   store_w(0);
+  if (nc > 1) fetch_w(1);
   __syncthreads();
-  for (int c = 0; c < nc; c += 2) {
-    if (c + 1 < nc) {
-      fetch_x(c + 1, xa[1]);
-      fetch_w(c + 1);
-    }
-    compute(0, xa[0]);
-    if (c + 1 < nc) store_w(1);
-    __syncthreads();
+  for (int c = 0; c < nc; c += 3) {
+    step(c, xa[0], xa[2]);
     if (c + 1 >= nc) break;
-    if (c + 2 < nc) {
-      fetch_x(c + 2, xa[0]);
-      fetch_w(c + 2);
-    }
-    compute(1, xa[1]);
-    if (c + 2 < nc) store_w(0);
-    __syncthreads();
+    step(c + 1, xa[1], xa[0]);
+    if (c + 2 >= nc) break;
+    step(c + 2, xa[2], xa[1]);
   }
 
   // ---- mu W_down: rows 0..2 of the mu tile live in lanes 0..15 ----
@@ -217,24 +225,46 @@ __device__ __forceinline__ void encode_body(const EncodeParams &p, int axis, cha
   }
 }
 
-template <int MT>
-__global__ __launch_bounds__(kThreads) void encode_mfma(EncodeParams p) {
+// NTK / NTV: column tiles of the K and V latents, 0 = chosen at run time
+// (one kernel body per rank, the register budget of the largest).
+template <int MT, int NTK, int NTV>
+__global__ __launch_bounds__(kThreads, 2) void encode_mfma(EncodeParams p) {
 #if defined(__HIP_DEVICE_COMPILE__)
   extern __shared__ __attribute__((aligned(16))) char lds[];
   const int axis = blockIdx.z;
-  const int r = axis ? p.rv : p.rk;
-  switch (r >> 4) {
-    case 1: encode_body<MT, 1>(p, axis, lds); break;
-    case 2: encode_body<MT, 2>(p, axis, lds); break;
-    case 3: encode_body<MT, 3>(p, axis, lds); break;
-    case 4: encode_body<MT, 4>(p, axis, lds); break;
-    case 5: encode_body<MT, 5>(p, axis, lds); break;
-    case 6: encode_body<MT, 6>(p, axis, lds); break;
-    case 7: encode_body<MT, 7>(p, axis, lds); break;
-    case 8: encode_body<MT, 8>(p, axis, lds); break;
-    default: break;
+  if constexpr (NTK > 0 && NTV > 0) {
+    if (axis == 0)
+      encode_body<MT, NTK>(p, 0, lds);
+    else
+      encode_body<MT, NTV>(p, 1, lds);
+  } else {
+    const int r = axis ? p.rv : p.rk;
+    switch (r >> 4) {
+      case 1: encode_body<MT, 1>(p, axis, lds); break;
+      case 2: encode_body<MT, 2>(p, axis, lds); break;
+      case 3: encode_body<MT, 3>(p, axis, lds); break;
+      case 4: encode_body<MT, 4>(p, axis, lds); break;
+      case 5: encode_body<MT, 5>(p, axis, lds); break;
+      case 6: encode_body<MT, 6>(p, axis, lds); break;
+      case 7: encode_body<MT, 7>(p, axis, lds); break;
+      case 8: encode_body<MT, 8>(p, axis, lds); break;
+      default: break;
+    }
   }
 #endif
+}
+
+template <int MT, int NTK, int NTV>
+hipError_t launch(const EncodeParams &p, hipStream_t st) {
+  const int M = p.B * p.n_new;
+  const size_t lds = encode_lds_bytes(p.rk > p.rv ? p.rk : p.rv);
+  const void *fn = reinterpret_cast<const void *>(&encode_mfma<MT, NTK, NTV>);
+  const hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+  if (e != hipSuccess) return e;
+  const int rows = 4 * 16 * MT;
+  const dim3 grid((M + rows - 1) / rows, p.Hs, 2);
+  hipLaunchKernelGGL((encode_mfma<MT, NTK, NTV>), grid, dim3(kThreads), lds, st, p);
+  return hipGetLastError();
 }
 
 }  // namespace detail
@@ -250,21 +280,16 @@ bool encode_mfma_supported(const EncodeParams &p, int dtype) {
 
 hipError_t launch_encode_mfma(const EncodeParams &p, hipStream_t st) {
   const int M = p.B * p.n_new;
-  const size_t lds = encode_lds_bytes(p.rk > p.rv ? p.rk : p.rv);
-  // two row tiles per wave when that still gives a full wave of workgroups
+  // Two row tiles per wave when that still gives a full wave of workgroups
+  // (only the smallest ranks: larger ones would spill at two waves per SIMD).
   const bool two = (int64_t)((M + 127) / 128) * p.Hs * 2 >= 256;
-  const void *fn = two ? reinterpret_cast<const void *>(&encode_mfma<2>)
-                       : reinterpret_cast<const void *>(&encode_mfma<1>);
-  const hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-  if (e != hipSuccess) return e;
-  if (two) {
-    const dim3 grid((M + 127) / 128, p.Hs, 2);
-    hipLaunchKernelGGL(encode_mfma<2>, grid, dim3(kThreads), lds, st, p);
-  } else {
-    const dim3 grid((M + 63) / 64, p.Hs, 2);
-    hipLaunchKernelGGL(encode_mfma<1>, grid, dim3(kThreads), lds, st, p);
-  }
-  return hipGetLastError();
+  const int k = p.rk / 16, v = p.rv / 16;
+  if (two && k == 1 && v == 2) return launch<2, 1, 2>(p, st);
+  if (k == 1 && v == 2) return launch<1, 1, 2>(p, st);
+  if (k == 2 && v == 4) return launch<1, 2, 4>(p, st);
+  if (k == 3 && v == 5) return launch<1, 3, 5>(p, st);
+  if (k == 4 && v == 8) return launch<1, 4, 8>(p, st);
+  return launch<1, 0, 0>(p, st);
 }
 
 }  // namespace lla

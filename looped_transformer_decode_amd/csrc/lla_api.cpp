@@ -67,13 +67,22 @@ uint16_t f64_to_bf16(double v) {
 }
 
 int32_t auto_splits(const lla_store_t *s, bool mfma) {
-  // Enough workgroups to cover the 256 CUs three times (the fast path holds
-  // one workgroup per CU), each split at least 256 slots long so that the
-  // per-workgroup setup stays amortised.
-  const int64_t per_split =
-      mfma ? (int64_t)s->batch * (s->heads / lla::decode_mfma_group_heads(s->r_k, s->r_v))
-           : (int64_t)s->batch * s->heads;
-  const int64_t target = mfma ? 768 : 2048;
+  // Per-head fast path: enough workgroups to cover the 256 CUs three times
+  // (one workgroup fills a CU's LDS).  LLA-2D fast path (bound by the matrix
+  // cores): one workgroup per CU.  Each split at least 256 slots long so that
+  // the per-workgroup setup stays amortised.
+  const bool is2d = s->variant == LLA_2D;
+  int64_t per_split, target;
+  if (mfma && is2d) {
+    per_split = s->batch;
+    target = 256;
+  } else if (mfma) {
+    per_split = (int64_t)s->batch * (s->heads / lla::decode_mfma_group_heads(s->r_k, s->r_v));
+    target = 768;
+  } else {
+    per_split = (int64_t)s->batch * s->heads;
+    target = 2048;
+  }
   int64_t S = (target + per_split - 1) / per_split;
   const int64_t max_s = std::max<int64_t>(1, s->max_ctx / 256);
   if (S > max_s) S = max_s;
@@ -82,8 +91,9 @@ int32_t auto_splits(const lla_store_t *s, bool mfma) {
 }
 
 bool use_mfma(const lla_store_t *s) {
-  return s->dtype == LLA_DT_BF16 &&
-         lla::decode_mfma_supported(s->heads, s->d_head, s->r_k, s->r_v, store_heads(s));
+  if (s->dtype != LLA_DT_BF16) return false;
+  if (s->variant == LLA_2D) return lla::decode2d_mfma_supported(s->heads, s->d_head, s->r_k, s->r_v);
+  return lla::decode_mfma_supported(s->heads, s->d_head, s->r_k, s->r_v, store_heads(s));
 }
 
 bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
@@ -100,7 +110,8 @@ lla_status_t decode_impl(const lla_store_t *st, int32_t want_variant, int32_t la
   if (layer < 0 || layer >= st->layers || loop < 0 || loop >= st->loops) return LLA_E_RANGE;
   if (n_splits < 0 || n_splits > st->max_ctx) return LLA_E_RANGE;
   if (std::isnan(scale) || std::isinf(scale)) return LLA_E_RANGE;
-  const bool mfma = use_mfma(st) && aligned16(st->data) && aligned16(wk) && aligned16(rope);
+  const bool mfma = use_mfma(st) && aligned16(st->data) && aligned16(wk) && aligned16(wv) &&
+                    aligned16(rope);
   if (!mfma) {
     if (st->d_head > 256 || st->r_k > 128 || st->r_v > 256 ||
         (size_t)st->d_head * st->r_k > 8192)
@@ -144,10 +155,14 @@ lla_status_t decode_impl(const lla_store_t *st, int32_t want_variant, int32_t la
   p.split_len = (per + 31) / 32 * 32;
   p.out = out;
 
-  hipError_t he = mfma ? lla::launch_decode_mfma(p, stream)
-                       : lla::launch_decode_valu(p, st->dtype, stream);
+  const bool is2d = st->variant == LLA_2D;
+  hipError_t he = !mfma ? lla::launch_decode_valu(p, st->dtype, stream)
+                  : is2d ? lla::launch_decode2d_mfma(p, stream)
+                         : lla::launch_decode_mfma(p, stream);
   if (he != hipSuccess) return LLA_E_HIP;
-  he = lla::launch_decode_merge(p, st->dtype, stream);
+  if (mfma && !is2d && S == 1) return LLA_OK;  // the split kernel wrote out itself
+  he = is2d ? lla::launch_decode_merge_batched(p, st->dtype, stream)
+            : lla::launch_decode_merge(p, st->dtype, stream);
   return he == hipSuccess ? LLA_OK : LLA_E_HIP;
 }
 

@@ -60,9 +60,21 @@ struct EncodeParams {
   const int32_t *start;    // [B]
 };
 
+// Heads one merge block covers: one thread per output element of 256, and
+// the merged latent averages of those heads (hpb * rv floats) within 32 KB.
+__host__ __device__ inline int32_t merge_heads_per_block(int32_t d, int32_t rv) {
+  int32_t h = d >= 256 ? 1 : 256 / d;
+  const int32_t cap = 8192 / rv;
+  if (h > cap) h = cap;
+  return h < 1 ? 1 : h;
+}
+
 // Launchers (return the launch status).  dtype is lla_dtype_t.
 hipError_t launch_decode_valu(const DecodeParams &p, int dtype, hipStream_t s);
 hipError_t launch_decode_merge(const DecodeParams &p, int dtype, hipStream_t s);
+hipError_t launch_decode_merge_batched(const DecodeParams &p, int dtype, hipStream_t s);
+bool decode2d_mfma_supported(int32_t H, int32_t d, int32_t rk, int32_t rv);
+hipError_t launch_decode2d_mfma(const DecodeParams &p, hipStream_t s);
 bool decode_mfma_supported(int32_t H, int32_t d, int32_t rk, int32_t rv, int32_t Hs);
 // Heads one fast-path workgroup covers (0 if the ranks have no instance).
 int32_t decode_mfma_group_heads(int32_t rk, int32_t rv);

@@ -117,7 +117,10 @@ def test_workspace_and_splits():
     assert L.lla_decode_workspace_bytes(s, -1) == 0
     t = WORKLOADS["tiny_fp32"]
     assert L.lla_decode_path(store_for(t)) == "valu"
-    assert L.lla_decode_path(store_for(WORKLOADS["lla2d_b256_ctx4k"])) == "valu"
+    s2 = store_for(WORKLOADS["lla2d_b256_ctx4k"])
+    assert L.lla_decode_path(s2) == "mfma"
+    assert L.lla_decode_auto_splits(s2) == 1      # B = 256: one workgroup per CU
+    assert L.lla_decode_path(store_for(WORKLOADS["lla2d_b256_ctx4k"].scaled(H=4))) == "valu"
 
 
 @pytest.mark.parametrize("d,N", [(64, 128), (128, 100)])

@@ -140,6 +140,7 @@ def test_fp32_encode_then_decode_exact_codec(device):
 BF16_SHAPES = [
     # (workload template, overrides): several tiles and a ragged tail
     ("extreme_batch_b768_ctx4k", dict(B=3, D=2, N=300)),
+    ("lla2d_b256_ctx4k", dict(B=3, D=2, N=1100)),                 # several splits of 256+
     ("bf16_b32_ctx4k", dict(B=3, D=2, N=200, H=8)),
     ("long_recurrence_t16_ctx8k", dict(B=2, D=2, N=260, H=8)),
     ("extreme_batch_b768_ctx4k", dict(B=2, D=1, N=160, d=64)),   # generic (VALU) bf16 path
@@ -162,7 +163,8 @@ def test_bf16_small_vs_oracle(device, tmpl, kw):
 
 
 def test_mfma_path_is_selected_for_paper_shapes():
-    for name in ("bf16_b32_ctx4k", "extreme_batch_b768_ctx4k", "long_recurrence_t16_ctx8k"):
+    for name in ("bf16_b32_ctx4k", "extreme_batch_b768_ctx4k", "long_recurrence_t16_ctx8k",
+                 "lla2d_b256_ctx4k"):
         w = WORKLOADS[name]
         s = L.LatentStore(w.variant, w.dtype, batch=w.B, layers=w.D, max_ctx=w.N, heads=w.H,
                           d_head=w.d, loops=w.T, r_k=w.r_k, r_v=w.r_v)
@@ -200,9 +202,10 @@ def test_explicit_softmax_scale(device):
     assert row_rel_l2(got, ref).max() <= TOL["bf16"]
 
 
-def test_garbage_beyond_pos_is_ignored(device):
+@pytest.mark.parametrize("tmpl", ["extreme_batch_b768_ctx4k", "lla2d_b256_ctx4k"])
+def test_garbage_beyond_pos_is_ignored(device, tmpl):
     """Slots after pos hold NaN: nothing of them may leak into the output."""
-    w = small("extreme_batch_b768_ctx4k", B=2, D=1, N=200)
+    w = small(tmpl, B=2, D=1, N=200)
     vals = host_store(w)
     dev_vals = to_device(vals, w.dtype, device)
     dev_vals[:, :, 150:] = float("nan")
