@@ -364,18 +364,19 @@ __global__ __launch_bounds__(512, 1) void decode2d_split(DecodeParams p) {
     for (int pp = 0; pp < C::PAIRS; ++pp) {
       const int hsel = HPW * wave + 2 * pp + khalf;
       float sc = 0.f;
+      // phi fragments of the tile: read from LDS once per pair, reused by
+      // every row tile (LDS bandwidth is as scarce as registers here)
+      bf16x8_t bphi[kKSteps];
+#pragma unroll
+      for (int st = 0; st < kKSteps; ++st)
+        bphi[st] = *reinterpret_cast<const bf16x8_t *>(phb + (st * 64 + lane) * 16);
 #pragma unroll
       for (int ti = 0; ti < C::KT; ++ti) {
-        // phi fragments are re-read from LDS for every row tile (registers
-        // are the scarce resource here, not LDS bandwidth)
-        asm volatile("" ::: "memory");
         f32x16_t u = {};
 #pragma unroll
-        for (int st = 0; st < kKSteps; ++st) {
-          const bf16x8_t bp = *reinterpret_cast<const bf16x8_t *>(phb + (st * 64 + lane) * 16);
+        for (int st = 0; st < kKSteps; ++st)
           u = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, Ak[pp][ti][st]),
-                                                      bp, u, 0, 0, 0);
-        }
+                                                      bphi[st], u, 0, 0, 0);
         // accumulator a of row tile ti is k = 16 ti + a of this lane's head
         sc = dot16(u, rec, 2 * ti, fj, sc);
       }

@@ -27,7 +27,9 @@
 // serve the first head of a pair, lanes 32-63 the second, so no cross-lane
 // reduction is needed anywhere in the slot loop.
 //
-// Data movement.  A workgroup owns (b, head group, context split).  Slot
+// Data movement.  A workgroup owns (b, head group, context split): 16 heads
+// in 8 waves (two per SIMD) for r_k + r_v = 48, 8 heads in 4 waves for the
+// larger ranks, whose 32-slot tiles would not fit LDS three deep.  Slot
 // records of the head group are contiguous in HBM; tiles of 32 slots are
 // streamed with buffer loads that write LDS directly (no VGPR staging),
 // three or two tiles deep, plus the matching 8 KB tile of bf16 phi rows.
@@ -432,14 +434,14 @@ bool decode_mfma_supported(int32_t H, int32_t d, int32_t rk, int32_t rv, int32_t
 }
 
 int32_t decode_mfma_group_heads(int32_t rk, int32_t rv) {
-  if (rk == 16 && rv == 32) return Cfg<16, 32, 4, 4>::HG;
+  if (rk == 16 && rv == 32) return Cfg<16, 32, 2, 8>::HG;
   if (rk == 32 && rv == 64) return Cfg<32, 64, 2, 4>::HG;
   if (rk == 48 && rv == 80) return Cfg<48, 80, 2, 4>::HG;
   return 0;
 }
 
 hipError_t launch_decode_mfma(const DecodeParams &p, hipStream_t st) {
-  if (p.rk == 16 && p.rv == 32) return launch<16, 32, 4, 4>(p, st);
+  if (p.rk == 16 && p.rv == 32) return launch<16, 32, 2, 8>(p, st);
   if (p.rk == 32 && p.rv == 64) return launch<32, 64, 2, 4>(p, st);
   if (p.rk == 48 && p.rv == 80) return launch<48, 80, 2, 4>(p, st);
   return hipErrorInvalidValue;

@@ -10,8 +10,10 @@
 // formed from exact products.  The latent is rounded once to bf16 (nearest,
 // ties to even).
 //
-// Work split.  A workgroup of four waves owns (row block, stored head, axis);
-// each wave owns MT tiles of 16 rows (rows = (sequence, new token)).  The
+// Work split.  A workgroup of four waves owns (row block, stored head, axis,
+// column group); each wave owns MT tiles of 16 rows (rows = (sequence, new
+// token)).  With few row blocks (LLA-2D, small batches) a column group is
+// one 16-column tile, so that W_down is spread over many workgroups.  The
 // stacked length K is walked in chunks of 128.  Rows of x stream from HBM
 // straight into registers: within a chunk, lane group g = lane/16 reads 64
 // contiguous bytes of its row, and the contraction index is permuted
@@ -57,7 +59,8 @@ __device__ __forceinline__ uint16_t split3(float v, int which) {
 }
 
 template <int MT, int NT>
-__device__ __forceinline__ void encode_body(const EncodeParams &p, int axis, char *lds) {
+// Columns [col0, col0 + 16 NT) of the latents of one axis (rfull wide).
+__device__ __forceinline__ void encode_body(const EncodeParams &p, int axis, int col0, char *lds) {
   constexpr int R = NT * 16;
   constexpr int PAIRS = kKc / 2 * (R / 8);        // (k pair, 8-column group) units per chunk
   constexpr int PPT = (PAIRS + kThreads - 1) / kThreads;
@@ -74,7 +77,9 @@ __device__ __forceinline__ void encode_body(const EncodeParams &p, int axis, cha
   uint16_t *mus = wt + 2 * R * kPitch;                                     // [2][3][kKc]
   float *bias = reinterpret_cast<float *>(mus + 2 * 3 * kKc);              // [R]
 
-  const uint16_t *wd = reinterpret_cast<const uint16_t *>(p.wd[axis]) + (int64_t)hs * K * R;
+  const int rfull = axis ? p.rv : p.rk;
+  const uint16_t *wd =
+      reinterpret_cast<const uint16_t *>(p.wd[axis]) + (int64_t)hs * K * rfull + col0;
   const float *mu = p.mu[axis] + (int64_t)hs * K;
   const u32x4_t *xrow[MT];
 #pragma unroll
@@ -94,9 +99,9 @@ __device__ __forceinline__ void encode_body(const EncodeParams &p, int axis, cha
       if (v < PAIRS) {
         const int kp = v / (R / 8), n0 = (v % (R / 8)) * 8;
         const u32x4_t *src =
-            reinterpret_cast<const u32x4_t *>(wd + (int64_t)(c * kKc + 2 * kp) * R + n0);
+            reinterpret_cast<const u32x4_t *>(wd + (int64_t)(c * kKc + 2 * kp) * rfull + n0);
         wreg[i][0] = src[0];
-        wreg[i][1] = src[R / 8];
+        wreg[i][1] = src[rfull / 8];
       }
     }
     if (tid < kKc / 4) mureg = reinterpret_cast<const float4 *>(mu + c * kKc)[tid];
@@ -207,7 +212,7 @@ __device__ __forceinline__ void encode_body(const EncodeParams &p, int axis, cha
 
   // ---- c = x W - mu W, rounded to bf16, written at the token's slot ----
   uint16_t *st = reinterpret_cast<uint16_t *>(p.store);
-  const int koff = axis ? p.rk : 0;
+  const int koff = (axis ? p.rk : 0) + col0;
 #pragma unroll
   for (int mt = 0; mt < MT; ++mt) {
 #pragma unroll
@@ -225,45 +230,33 @@ __device__ __forceinline__ void encode_body(const EncodeParams &p, int axis, cha
   }
 }
 
-// NTK / NTV: column tiles of the K and V latents, 0 = chosen at run time
-// (one kernel body per rank, the register budget of the largest).
+// NTK / NTV: column tiles per workgroup of the K and V latents.
+// blockIdx.z enumerates the column groups: gk groups of the K latent, then
+// those of the V latent.
 template <int MT, int NTK, int NTV>
-__global__ __launch_bounds__(kThreads, 2) void encode_mfma(EncodeParams p) {
+__global__ __launch_bounds__(kThreads, 2) void encode_mfma(EncodeParams p, int gk) {
 #if defined(__HIP_DEVICE_COMPILE__)
   extern __shared__ __attribute__((aligned(16))) char lds[];
-  const int axis = blockIdx.z;
-  if constexpr (NTK > 0 && NTV > 0) {
-    if (axis == 0)
-      encode_body<MT, NTK>(p, 0, lds);
-    else
-      encode_body<MT, NTV>(p, 1, lds);
-  } else {
-    const int r = axis ? p.rv : p.rk;
-    switch (r >> 4) {
-      case 1: encode_body<MT, 1>(p, axis, lds); break;
-      case 2: encode_body<MT, 2>(p, axis, lds); break;
-      case 3: encode_body<MT, 3>(p, axis, lds); break;
-      case 4: encode_body<MT, 4>(p, axis, lds); break;
-      case 5: encode_body<MT, 5>(p, axis, lds); break;
-      case 6: encode_body<MT, 6>(p, axis, lds); break;
-      case 7: encode_body<MT, 7>(p, axis, lds); break;
-      case 8: encode_body<MT, 8>(p, axis, lds); break;
-      default: break;
-    }
-  }
+  const int z = blockIdx.z;
+  if (z < gk)
+    encode_body<MT, NTK>(p, 0, z * 16 * NTK, lds);
+  else
+    encode_body<MT, NTV>(p, 1, (z - gk) * 16 * NTV, lds);
 #endif
 }
 
 template <int MT, int NTK, int NTV>
 hipError_t launch(const EncodeParams &p, hipStream_t st) {
   const int M = p.B * p.n_new;
-  const size_t lds = encode_lds_bytes(p.rk > p.rv ? p.rk : p.rv);
+  const int gk = p.rk / (16 * NTK);
+  const int gv = p.rv / (16 * NTV);
+  const size_t lds = encode_lds_bytes(16 * (NTK > NTV ? NTK : NTV));
   const void *fn = reinterpret_cast<const void *>(&encode_mfma<MT, NTK, NTV>);
   const hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
   if (e != hipSuccess) return e;
   const int rows = 4 * 16 * MT;
-  const dim3 grid((M + rows - 1) / rows, p.Hs, 2);
-  hipLaunchKernelGGL((encode_mfma<MT, NTK, NTV>), grid, dim3(kThreads), lds, st, p);
+  const dim3 grid((M + rows - 1) / rows, p.Hs, gk + gv);
+  hipLaunchKernelGGL((encode_mfma<MT, NTK, NTV>), grid, dim3(kThreads), lds, st, p, gk);
   return hipGetLastError();
 }
 
@@ -280,16 +273,20 @@ bool encode_mfma_supported(const EncodeParams &p, int dtype) {
 
 hipError_t launch_encode_mfma(const EncodeParams &p, hipStream_t st) {
   const int M = p.B * p.n_new;
+  const int k = p.rk / 16, v = p.rv / 16;
+  const int64_t blocks1 = (int64_t)((M + 63) / 64) * p.Hs;  // workgroups per column group
+  // Few row blocks (small batch, LLA-2D): give each workgroup one 16-column
+  // tile so that W_down is split over more workgroups instead of being
+  // re-read whole by each of a handful of them.
+  if (blocks1 * 2 < 128) return launch<1, 1, 1>(p, st);
   // Two row tiles per wave when that still gives a full wave of workgroups
   // (only the smallest ranks: larger ones would spill at two waves per SIMD).
   const bool two = (int64_t)((M + 127) / 128) * p.Hs * 2 >= 256;
-  const int k = p.rk / 16, v = p.rv / 16;
   if (two && k == 1 && v == 2) return launch<2, 1, 2>(p, st);
   if (k == 1 && v == 2) return launch<1, 1, 2>(p, st);
   if (k == 2 && v == 4) return launch<1, 2, 4>(p, st);
   if (k == 3 && v == 5) return launch<1, 3, 5>(p, st);
-  if (k == 4 && v == 8) return launch<1, 4, 8>(p, st);
-  return launch<1, 0, 0>(p, st);
+  return launch<1, 1, 1>(p, st);  // any other ranks: one 16-column tile per workgroup
 }
 
 }  // namespace lla
