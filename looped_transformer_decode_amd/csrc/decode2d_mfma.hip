@@ -24,20 +24,23 @@
 //    the score is then an r_k-term dot with c_k.
 //  * phi_j^T g0_h for all heads: eight v_mfma_f32_16x16x32_bf16 per tile
 //    ((slot half) x (d quarter)), one per wave, partial sums exchanged
-//    through LDS, computed one tile ahead.
+//    through LDS.
 //  * online softmax per head over the 32 lanes of a half (lazy rescaling:
 //    the running max moves only when a score exceeds it by kRescaleGap),
 //    the weights rounded to bf16 and published in LDS.
-//  * P C_v on v_mfma_f32_16x16x32_bf16, one tile behind: wave w owns value
-//    columns 16w..16w+15 of all heads (rows = heads, K = 32 slots).
+//  * P C_v on v_mfma_f32_16x16x32_bf16: wave w owns value columns
+//    16w..16w+15 of all heads (rows = heads, K = 32 slots).
+// The three stages run as a software pipeline, tile it's scores with tile
+// it-1's softmax and tile it-2's P C_v in one iteration, and the two waves
+// of a SIMD take them in opposite orders so that matrix and vector work
+// overlap.
 // G is formed once per workgroup in LDS (32 latent components of every head
 // at a time, transposed so that d is contiguous) and each lane then loads
 // its 16-byte A fragments.
-// One barrier per tile.  Latent tiles (NS = 4 LDS buffers, two in flight)
+// One barrier per tile.  Latent tiles (NS = 5 LDS buffers, two in flight)
 // and bf16 phi tiles (three buffers) arrive by buffer loads that write LDS
-// directly; 16-byte chunks of a slot record are XOR-swizzled by
-// f(j) = (j ^ j >> 3) & 7 so that lanes reading different slots hit
-// different banks.  The partial (m, l, sum p c_v) of every head goes to the
+// directly; 16-byte chunks of a slot record are XOR-swizzled by slot
+// (swz, swz_v) so that lanes reading different slots hit different banks.  The partial (m, l, sum p c_v) of every head goes to the
 // workspace; the merge kernel applies W_up,v,t and mu_v,t batched over
 // sequences.
 #include "lla_device.h"
@@ -70,12 +73,13 @@ struct Cfg {
   static constexpr int R = RK + RV;
   static constexpr int REC = 2 * R;                   // bytes per slot record
   static constexpr int CPT = REC / 16;                // 16-byte chunks per record
+  static constexpr int CK = RK * 2 / 16;              // of which hold the K latent
   static constexpr int TILE_BYTES = kTile * REC;
   static constexpr int WLOADS = TILE_BYTES / 1024;    // 64-lane x 16 B loads per tile
   static constexpr int LW_MAX = (WLOADS + NW - 1) / NW;
   static constexpr int PHI_LOADS = kPhiTileBytes / 1024 / NW;
   static constexpr int MU_PIECES = 8 / NW;            // (slot half, d quarter) pieces per wave
-  static constexpr int NS = 4;
+  static constexpr int NS = 5;     // tiles it-2 .. it+2: stage C reads it-2, two in flight
   static constexpr int NPHI = 3;
   static constexpr int KT = RK / 16;
   static constexpr int VB = RV / 16 / NW;             // 16-column value blocks per wave
@@ -85,7 +89,8 @@ struct Cfg {
   static constexpr int OFF_P = OFF_MU + 2 * MU_BUF;
   static constexpr int P_BUF = H * kPPitch * 2;
   static constexpr int OFF_ALPHA = OFF_P + 2 * P_BUF;
-  static constexpr int PIPE_BYTES = OFF_ALPHA + 2 * H * 4;
+  static constexpr int OFF_AMU = OFF_ALPHA + 2 * H * 4;   // g0 A fragments [NW][pieces][64][16 B]
+  static constexpr int PIPE_BYTES = OFF_AMU + NW * (8 / NW) * 64 * 16;
   static constexpr int WPITCH = kD + 8;               // LDS row pitch of G^T (elements)
   static constexpr int WSTAGE = H * 32 * WPITCH * 2;  // G^T for 32 k of every head, [h][k][i]
   static constexpr int SETUP_BYTES = WSTAGE + H * kD * 4;
@@ -93,27 +98,40 @@ struct Cfg {
   static_assert(H == 16, "heads = rows of the 16x16 MFMAs");
   static_assert(VB >= 1 && RV == 16 * VB * NW, "value columns split evenly over the waves");
   static_assert(RK % 32 == 0 && KT >= 2, "rank granularity (setup builds 32 k per round)");
-  static_assert(CPT % 8 == 0, "swizzle works on groups of 8 chunks");
+  static_assert(CPT % 8 == 0 && CK % 8 == 0, "swizzles work on groups of 8 chunks");
   static_assert(TILE_BYTES % 1024 == 0 && PHI_LOADS >= 1 && MU_PIECES >= 1, "load split");
   static_assert(LDS_BYTES <= kLdsMax, "LDS");
   static_assert(H * (RV + 2) * 4 <= 2 * MU_BUF, "epilogue staging");
   static_assert(LW_MAX + PHI_LOADS <= 6, "vmcnt range of wait_vm_small");
+  static_assert(OFF_AMU % 16 == 0 && PIPE_BYTES <= WSTAGE, "g0 fragments live below the queries");
 };
 
+// LDS placement of a slot record's 16-byte chunks.  K-latent chunks
+// (lanes = 32 consecutive slots read the same chunk) are XOR-swizzled by
+// swz(j); V-latent chunks (lanes = 16 columns of 4 slots 8 apart) by
+// 2 ((j >> 3) & 3), which moves each 8-slot group to its own chunk pair and
+// keeps the per-slot offsets of a gather a compile-time stride.
 __device__ __forceinline__ int swz(int j) { return (j ^ (j >> 3)) & 7; }
+__device__ __forceinline__ int swz_v(int j) { return 2 * ((j >> 3) & 3); }
 
 // sc + sum_a u[a] * c[8 c0 + a]: the 16 latent values of chunks c0, c0+1
-// of a (swizzled) slot record against one 32x32 accumulator column.
+// of a (swizzled) slot record against one 32x32 accumulator column.  The
+// accumulators are rounded to bf16 pairs and multiplied with the bf16
+// latent pairs by v_dot2 (fp32 sums): half the vector instructions of
+// unpacking every latent to fp32.  (The latent pairs are converted to
+// uint32_t before the bit cast: a bit cast of a vector element directly
+// has been miscompiled into a reuse of element 0.)
 __device__ __forceinline__ float dot16(const f32x16_t &u, const char *rec, int c0, int fj,
                                        float sc) {
   const u32x4_t a = *reinterpret_cast<const u32x4_t *>(rec + ((c0 ^ fj) * 16));
   const u32x4_t b = *reinterpret_cast<const u32x4_t *>(rec + (((c0 + 1) ^ fj) * 16));
 #pragma unroll
   for (int w = 0; w < 4; ++w) {
-    sc = fmaf(u[2 * w], bf16_lo(a[w]), sc);
-    sc = fmaf(u[2 * w + 1], bf16_hi(a[w]), sc);
-    sc = fmaf(u[8 + 2 * w], bf16_lo(b[w]), sc);
-    sc = fmaf(u[8 + 2 * w + 1], bf16_hi(b[w]), sc);
+    const bf16x2_v ca = __builtin_bit_cast(bf16x2_v, (uint32_t)a[w]);
+    const bf16x2_v cb = __builtin_bit_cast(bf16x2_v, (uint32_t)b[w]);
+    const f32x2_v ua = {u[2 * w], u[2 * w + 1]}, ub = {u[8 + 2 * w], u[8 + 2 * w + 1]};
+    sc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_convertvector(ua, bf16x2_v), ca, sc, false);
+    sc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_convertvector(ub, bf16x2_v), cb, sc, false);
   }
   return sc;
 }
@@ -219,8 +237,9 @@ __global__ __launch_bounds__(512, 1) void decode2d_split(DecodeParams p) {
     __syncthreads();
   }
   // g0 rows for the mu term: wave w computes the (slot half cb, d quarter
-  // ks) pieces c = w + NW v of the eight, for all 16 heads.
-  u32x4_t Amu[C::MU_PIECES];
+  // ks) pieces c = w + NW v of the eight, for all 16 heads.  They are kept
+  // in LDS (read once per tile) rather than in registers.
+  u32x4_t *amu_l = reinterpret_cast<u32x4_t *>(lds + C::OFF_AMU) + (wave * C::MU_PIECES) * 64 + lane;
 #pragma unroll
   for (int v = 0; v < C::MU_PIECES; ++v) {
     const int c = wave + NW * v, ks = c >> 1;
@@ -233,9 +252,10 @@ __global__ __launch_bounds__(512, 1) void decode2d_split(DecodeParams p) {
       gv[e] = (i < kD / 2) ? qh[i] * mu[i] + qh[i + kD / 2] * mu[i + kD / 2]
                            : qh[i] * mu[i - kD / 2] - qh[i - kD / 2] * mu[i];
     }
+    u32x4_t frag;
 #pragma unroll
-    for (int w = 0; w < 4; ++w)
-      Amu[v][w] = pack_bf16x2(gv[2 * w], gv[2 * w + 1]);
+    for (int w = 0; w < 4; ++w) frag[w] = pack_bf16x2(gv[2 * w], gv[2 * w + 1]);
+    amu_l[v * 64] = frag;
   }
   __syncthreads();  // the setup LDS is reused by the pipeline
 
@@ -255,7 +275,7 @@ __global__ __launch_bounds__(512, 1) void decode2d_split(DecodeParams p) {
   for (int u = 0; u < C::LW_MAX; ++u) {
     const int P = (wave + u * NW) * 64 + lane;
     const int tj = P / C::CPT, q = P % C::CPT;
-    voff[u] = tj * C::REC + (uint32_t)((q ^ swz(tj)) * 16);
+    voff[u] = tj * C::REC + (uint32_t)((q ^ (q < C::CK ? swz(tj) : swz_v(tj))) * 16);
   }
   auto issue_store = [&](int t) {
     char *sb = lds + (t % C::NS) * C::TILE_BYTES;
@@ -287,8 +307,8 @@ __global__ __launch_bounds__(512, 1) void decode2d_split(DecodeParams p) {
       const bf16x8_t bm = *reinterpret_cast<const bf16x8_t *>(
           pb + ((2 * ks + (g4 >> 1)) * 64 + 16 * cb + l16 + 32 * (g4 & 1)) * 16);
       f32x4_t o = {0.f, 0.f, 0.f, 0.f};
-      o = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, Amu[v]), bm, o, 0,
-                                                   0, 0);
+      o = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, amu_l[v * 64]), bm,
+                                                   o, 0, 0, 0);
 #pragma unroll
       for (int i = 0; i < 4; ++i) mb[(ks * H + 4 * g4 + i) * kTile + 16 * cb + l16] = o[i];
     }
@@ -307,13 +327,13 @@ __global__ __launch_bounds__(512, 1) void decode2d_split(DecodeParams p) {
 #pragma unroll
     for (int v = 0; v < C::VB; ++v) {
       const int comp = RK + 16 * (C::VB * wave + v) + l16;
-      const int cchunk = comp >> 3, cwithin = (comp & 7) * 2;
+      // slots 8 g4 + e share swz_v = 2 g4: one base address, stride REC
+      const char *gb = sb + 8 * g4 * C::REC + (((comp >> 3) ^ (2 * g4)) * 16) + (comp & 7) * 2;
       bf16x8_t bv;
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
         const int sl = 8 * g4 + e;
-        const uint16_t x = *reinterpret_cast<const uint16_t *>(
-            sb + sl * C::REC + ((cchunk ^ swz(sl)) * 16) + cwithin);
+        const uint16_t x = *reinterpret_cast<const uint16_t *>(gb + e * C::REC);
         bv[e] = (t0 + t * kTile + sl < t1) ? (short)x : (short)0;
       }
 #pragma unroll
@@ -339,37 +359,24 @@ __global__ __launch_bounds__(512, 1) void decode2d_split(DecodeParams p) {
   }
   wait_vm_small(ntiles > 1 ? C::PHI_LOADS + LW : 0);  // store(0), phi(0) have landed
   __syncthreads();
-  mu_step(0);
-  wait_vm_small(ntiles > 1 ? LW : 0);                 // phi(1)
-  __syncthreads();
 
   const int j = lane & 31;
   const int fj = swz(j);
-  for (int it = 0; it < ntiles; ++it) {
-    if (it + 2 < ntiles) {
-      issue_phi(it + 2);
-      issue_store(it + 2);
-    }
-    if (it >= 1) pv_step(it - 1);
-    if (it + 1 < ntiles) mu_step(it + 1);
 
-    const char *sb = lds + (it % C::NS) * C::TILE_BYTES;
-    const char *phb = lds + C::OFF_PHI + (it % C::NPHI) * kPhiTileBytes;
+  // Stage A(t): K-side MFMA chains of tile t and the dots with c_k -> sc.
+  auto stage_scores = [&](int t, float (&sc)[C::PAIRS]) {
+    const char *sb = lds + (t % C::NS) * C::TILE_BYTES;
+    const char *phb = lds + C::OFF_PHI + (t % C::NPHI) * kPhiTileBytes;
     const char *rec = sb + j * C::REC;
-    const float *mb = reinterpret_cast<const float *>(lds + C::OFF_MU + (it & 1) * C::MU_BUF);
-    uint16_t *Pw = reinterpret_cast<uint16_t *>(lds + C::OFF_P + (it & 1) * C::P_BUF);
-    float *Aw = reinterpret_cast<float *>(lds + C::OFF_ALPHA + (it & 1) * H * 4);
-    const bool valid = (t0 + it * kTile + j) < t1;
 #pragma unroll
     for (int pp = 0; pp < C::PAIRS; ++pp) {
-      const int hsel = HPW * wave + 2 * pp + khalf;
-      float sc = 0.f;
       // phi fragments of the tile: read from LDS once per pair, reused by
       // every row tile (LDS bandwidth is as scarce as registers here)
       bf16x8_t bphi[kKSteps];
 #pragma unroll
       for (int st = 0; st < kKSteps; ++st)
         bphi[st] = *reinterpret_cast<const bf16x8_t *>(phb + (st * 64 + lane) * 16);
+      float acc = 0.f;
 #pragma unroll
       for (int ti = 0; ti < C::KT; ++ti) {
         f32x16_t u = {};
@@ -378,16 +385,29 @@ __global__ __launch_bounds__(512, 1) void decode2d_split(DecodeParams p) {
           u = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, Ak[pp][ti][st]),
                                                       bphi[st], u, 0, 0, 0);
         // accumulator a of row tile ti is k = 16 ti + a of this lane's head
-        sc = dot16(u, rec, 2 * ti, fj, sc);
+        acc = dot16(u, rec, 2 * ti, fj, acc);
       }
-#pragma unroll
-      for (int q = 0; q < 4; ++q) sc += mb[(q * H + hsel) * kTile + j];
-      sc = valid ? sc : -INFINITY;
+      sc[pp] = acc;
+    }
+  };
 
+  // Stage B(t): mu term, online softmax of every head -> P(t), alpha(t).
+  auto stage_softmax = [&](int t, const float (&sc)[C::PAIRS]) {
+    const float *mb = reinterpret_cast<const float *>(lds + C::OFF_MU + (t & 1) * C::MU_BUF);
+    uint16_t *Pw = reinterpret_cast<uint16_t *>(lds + C::OFF_P + (t & 1) * C::P_BUF);
+    float *Aw = reinterpret_cast<float *>(lds + C::OFF_ALPHA + (t & 1) * H * 4);
+    const bool valid = (t0 + t * kTile + j) < t1;
+#pragma unroll
+    for (int pp = 0; pp < C::PAIRS; ++pp) {
+      const int hsel = HPW * wave + 2 * pp + khalf;
+      float s = sc[pp];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) s += mb[(q * H + hsel) * kTile + j];
+      s = valid ? s : -INFINITY;
       // online softmax of head hsel over the 32 lanes of this half
       float alpha = 1.f;
-      if (__any(sc > m[pp] + kRescaleGap)) {
-        float tm = sc;
+      if (__any(s > m[pp] + kRescaleGap)) {
+        float tm = s;
 #pragma unroll
         for (int o = 16; o > 0; o >>= 1) tm = fmaxf(tm, __shfl_xor(tm, o, 64));
         if (tm > m[pp] + kRescaleGap) {
@@ -395,17 +415,50 @@ __global__ __launch_bounds__(512, 1) void decode2d_split(DecodeParams p) {
           m[pp] = tm;
         }
       }
-      const float pe = valid ? exp2f(sc - m[pp]) : 0.f;
+      const float pe = valid ? exp2f(s - m[pp]) : 0.f;
       const uint16_t pb16 = f32_to_bf16_bits(pe);
       lsum[pp] = fmaf(lsum[pp], alpha, bf16_bits_to_f32(pb16));
       Pw[hsel * kPPitch + j] = pb16;
       if (j == 0) Aw[hsel] = alpha;
     }
+  };
 
-    wait_vm_small(it + 2 < ntiles ? LW : 0);
+  // Software pipeline over tiles: iteration it runs A(it) (with the mu term
+  // of tile it), B(it - 1) and C(it - 2) = pv_step; one barrier per
+  // iteration publishes mu(it) and P(it - 1).  The two waves that share a
+  // SIMD take the stages in opposite orders (matrix work first, vector work
+  // first), so that one's MFMA chains overlap the other's softmax and
+  // gathers.
+  const bool mfma_first = wave < NW / 2;
+  float scp[C::PAIRS];  // scores of tile it - 1, waiting for stage B
+#pragma unroll
+  for (int pp = 0; pp < C::PAIRS; ++pp) scp[pp] = 0.f;
+  for (int it = 0; it < ntiles + 2; ++it) {
+    if (it + 2 < ntiles) {
+      issue_phi(it + 2);
+      issue_store(it + 2);
+    }
+    float scc[C::PAIRS];
+    if (mfma_first) {
+      if (it < ntiles) {
+        mu_step(it);
+        stage_scores(it, scc);
+      }
+      if (it >= 1 && it <= ntiles) stage_softmax(it - 1, scp);
+      if (it >= 2) pv_step(it - 2);
+    } else {
+      if (it >= 1 && it <= ntiles) stage_softmax(it - 1, scp);
+      if (it >= 2) pv_step(it - 2);
+      if (it < ntiles) {
+        mu_step(it);
+        stage_scores(it, scc);
+      }
+    }
+#pragma unroll
+    for (int pp = 0; pp < C::PAIRS; ++pp) scp[pp] = scc[pp];
+    wait_vm_small(it + 2 < ntiles ? C::PHI_LOADS + LW : 0);  // store(it+1), phi(it+1)
     __syncthreads();
   }
-  pv_step(ntiles - 1);
 
   // ---- partials (m, l, sum p c_v) of every head ----
   __syncthreads();  // everyone is done with the mu buffers
