@@ -8,9 +8,14 @@ state).  Inputs are synthetic and resident in HBM before timing starts.
 
 Prints one JSON line (rank 0, N = 1 GPU):
   value      = B / step time  (tokens/s, all sequences)
-  roofline   = algorithmic bytes of one decode call / its average duration,
-               HIP events on the launch stream over the timed region,
-               against 8 TB/s
+  roofline   = per-head stores (HBM-bound): algorithmic bytes of one decode
+               call / its average duration, against 8 TB/s;
+               LLA-2D stores (bound by the matrix cores): the K-side
+               contraction's flops / the call's duration, against 2.5 PFLOP/s
+               dense bf16.  Durations are HIP events recorded on the launch
+               stream around every call of the timed region.
+               traffic = HBM bytes per launch from the committed rocprofv3
+               FETCH_SIZE / WRITE_SIZE summary (null if the kernel changed).
   cpu_baseline = the fp64 oracle timed on a bounded sample on host cores
 """
 from __future__ import annotations
@@ -28,9 +33,12 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 METRIC = "LLA decode-attn tokens/s at B=768, 4k ctx, ρ=21.3 + % of HBM roofline"
-HBM_PEAK_GBS = 8000.0
-KERNEL_SRC = os.path.join(ROOT, "looped_transformer_decode_amd", "csrc", "decode_mfma.hip")
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_mfma_extreme_batch_traffic.json")
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
+MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 matrix cores
+CSRC = os.path.join(ROOT, "looped_transformer_decode_amd", "csrc")
+# FETCH_SIZE / WRITE_SIZE of a plain 8 GB device copy (one dispatch) read 3,906,278 KiB
+# and 7,812,500 KiB: the fetch counter reports half of the bytes read.
+FETCH_SCALE, WRITE_SCALE = 2.0, 1.0
 
 
 def parse():
@@ -47,6 +55,9 @@ def parse():
                     help="instead of the benchmark, copy a buffer of this size a few times "
                          "(reference for HBM byte counters)")
     ap.add_argument("--no-encode", action="store_true", help=argparse.SUPPRESS)
+    ap.add_argument("--summarize-counters", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
+                    help="write profiles/traffic_<workload>.json from two rocprofv3 --pmc "
+                         "output directories (FETCH_SIZE, WRITE_SIZE) and exit")
     return ap.parse_args()
 
 
@@ -64,18 +75,67 @@ def algorithmic_bytes(w, pos_plus_one: int) -> int:
     return store + q_out + codec
 
 
-def traffic_for_current_kernel():
-    """HBM bytes per launch from the committed rocprofv3 counter summary,
-    or None when absent or taken on a different kernel source."""
+def kernel_source(w) -> str:
+    return os.path.join(CSRC, "decode2d_mfma.hip" if w.variant == "2d" else "decode_mfma.hip")
+
+
+def traffic_file(w) -> str:
+    return os.path.join(ROOT, "profiles", f"traffic_{w.name}.json")
+
+
+def kernel_sha(w) -> str:
+    return hashlib.sha256(open(kernel_source(w), "rb").read()).hexdigest()
+
+
+def traffic_for_current_kernel(w):
+    """HBM bytes per launch of the decode split kernel from the committed
+    rocprofv3 counter summary, or None when absent or taken on a different
+    kernel source."""
     try:
-        with open(TRAFFIC_FILE) as f:
+        with open(traffic_file(w)) as f:
             t = json.load(f)
-        src = hashlib.sha256(open(KERNEL_SRC, "rb").read()).hexdigest()
-        if t.get("kernel_sha256") != src:
+        if t.get("kernel_sha256") != kernel_sha(w):
             return None
         return t.get("hbm_bytes_per_launch")
     except (OSError, ValueError):
         return None
+
+
+def algorithmic_flops(w, pos_plus_one: int) -> int:
+    """Matrix-core work of one LLA-2D decode call: the K-side contraction
+    (tokens x d x r_k per head) that reconstruction, RoPE and q.k share."""
+    return 2 * w.B * pos_plus_one * w.H * w.d * w.r_k
+
+
+def summarize_counters(w, fetch_dir: str, write_dir: str) -> dict:
+    """Per-launch HBM bytes of the decode split kernel from two rocprofv3
+    --pmc runs (FETCH_SIZE, then WRITE_SIZE, in KiB per dispatch), scaled by
+    the copy-kernel calibration; written to profiles/traffic_<workload>.json."""
+    import csv
+    import glob
+
+    def per_dispatch(d, counter):
+        vals = []
+        for f in glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True):
+            for r in csv.DictReader(open(f)):
+                if r["Counter_Name"] == counter and "split" in r["Kernel_Name"]:
+                    vals.append(float(r["Counter_Value"]))
+        if not vals:
+            raise SystemExit(f"no {counter} rows for a split kernel under {d}")
+        return sum(vals) / len(vals), len(vals)
+
+    fetch, nf = per_dispatch(fetch_dir, "FETCH_SIZE")
+    write, nw = per_dispatch(write_dir, "WRITE_SIZE")
+    hbm = fetch * 1024 * FETCH_SCALE + write * 1024 * WRITE_SCALE
+    res = {"workload": w.name, "kernel_source": os.path.relpath(kernel_source(w), ROOT),
+           "kernel_sha256": kernel_sha(w), "fetch_kib_per_dispatch": round(fetch, 1),
+           "write_kib_per_dispatch": round(write, 1), "dispatches": [nf, nw],
+           "fetch_scale": FETCH_SCALE, "write_scale": WRITE_SCALE,
+           "hbm_bytes_per_launch": int(hbm),
+           "algorithmic_bytes_per_launch": algorithmic_bytes(w, w.N)}
+    with open(traffic_file(w), "w") as f:
+        json.dump(res, f, indent=1)
+    return res
 
 
 def cpu_baseline(w, codec, budget_s: float):
@@ -114,10 +174,14 @@ def cpu_baseline(w, codec, budget_s: float):
 def main():
     args = parse()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
-        print("bench.py measures one GPU: this build has no multi-GPU path "
-              "(the hot path shards by sequence with no exchange; see DESIGN.md).",
-              file=sys.stderr)
+        print("bench.py measures one GPU: there is no multi-GPU path here (the hot path "
+              "would shard by sequence with no exchange).", file=sys.stderr)
         sys.exit(2)
+
+    if args.summarize_counters:
+        from synth.workloads import WORKLOADS
+        print(json.dumps(summarize_counters(WORKLOADS[args.workload], *args.summarize_counters)))
+        return
 
     import torch
 
@@ -236,7 +300,27 @@ def main():
         f"max {call_ms.max() * 1e3:.1f})")
     value = w.B / (ms_step / 1e3)
     bytes_call = algorithmic_bytes(w, w.N)
-    achieved = bytes_call / (call_ms.mean() / 1e3) / 1e9
+    path = L.lla_decode_path(store)
+    if w.variant == "2d":
+        flops_call = algorithmic_flops(w, w.N)
+        achieved = flops_call / (call_ms.mean() / 1e3) / 1e12
+        roofline = {"bound": "mfma", "achieved": round(achieved, 1),
+                    "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                    "frac": round(achieved / MFMA_BF16_PEAK_TFLOPS, 4),
+                    "traffic": traffic_for_current_kernel(w),
+                    "kernel": "decode2d_split + decode_merge_batched (one lla2d_decode_attn call)",
+                    "flops_per_launch": flops_call, "bytes_per_launch": bytes_call,
+                    "hbm_GBps": round(bytes_call / (call_ms.mean() / 1e3) / 1e9, 1),
+                    "launch_us": round(call_ms.mean() * 1e3, 2)}
+    else:
+        achieved = bytes_call / (call_ms.mean() / 1e3) / 1e9
+        splits = args.splits or L.lla_decode_auto_splits(store)
+        roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
+                    "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                    "traffic": traffic_for_current_kernel(w),
+                    "kernel": "decode_mfma_split (one lla_decode_attn call"
+                              + (")" if splits == 1 and path == "mfma" else " + decode_merge)"),
+                    "bytes_per_launch": bytes_call, "launch_us": round(call_ms.mean() * 1e3, 2)}
     res = {
         "metric": METRIC, "value": round(value, 2), "unit": "tokens/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_step, 4),
@@ -247,12 +331,8 @@ def main():
                    "r_v": w.r_v, "rho": str(L.lla_compression_ratio(store)),
                    "calls_per_step": w.D * w.T, "encode_appends_per_step": 0 if args.no_encode
                    else w.D, "splits": args.splits or L.lla_decode_auto_splits(store),
-                   "path": L.lla_decode_path(store)},
-        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
-                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
-                     "traffic": traffic_for_current_kernel(),
-                     "kernel": "decode_mfma_split + decode_merge (one lla_decode_attn call)",
-                     "bytes_per_launch": bytes_call, "launch_us": round(call_ms.mean() * 1e3, 2)},
+                   "path": path},
+        "roofline": roofline,
     }
     if args.cpu_seconds > 0:
         del store, q, xk, xv

@@ -212,15 +212,28 @@ __global__ __launch_bounds__(256) void decode_merge_batched(DecodeParams p) {
     for (int bl = 0; bl < kBT; ++bl) acc[bl] = 0.f;
     const E *w = reinterpret_cast<const E *>(p.wv) + ((int64_t)h * d + i) * rv;
     if (vec) {
+      // 8 weights of the row per 16-byte load; the 8 matching averages of
+      // each sequence as two 16-byte LDS reads (the same address in every
+      // lane: a broadcast)
       const uint4 *w4 = reinterpret_cast<const uint4 *>(w);
       for (int r8 = 0; r8 < rv / 8; ++r8) {
         const uint4 v = w4[r8];
-        const uint32_t u[4] = {v.x, v.y, v.z, v.w};
+        const float wf[8] = {bf16_lo(v.x), bf16_hi(v.x), bf16_lo(v.y), bf16_hi(v.y),
+                             bf16_lo(v.z), bf16_hi(v.z), bf16_lo(v.w), bf16_hi(v.w)};
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const float wf = (e & 1) ? bf16_hi(u[e / 2]) : bf16_lo(u[e / 2]);
-#pragma unroll
-          for (int bl = 0; bl < kBT; ++bl) acc[bl] = fmaf(wf, abar[bl * rv + 8 * r8 + e], acc[bl]);
+        for (int bl = 0; bl < kBT; ++bl) {
+          const float4 a0 = *reinterpret_cast<const float4 *>(abar + bl * rv + 8 * r8);
+          const float4 a1 = *reinterpret_cast<const float4 *>(abar + bl * rv + 8 * r8 + 4);
+          float t = acc[bl];
+          t = fmaf(wf[0], a0.x, t);
+          t = fmaf(wf[1], a0.y, t);
+          t = fmaf(wf[2], a0.z, t);
+          t = fmaf(wf[3], a0.w, t);
+          t = fmaf(wf[4], a1.x, t);
+          t = fmaf(wf[5], a1.y, t);
+          t = fmaf(wf[6], a1.z, t);
+          t = fmaf(wf[7], a1.w, t);
+          acc[bl] = t;
         }
       }
     } else {

@@ -25,7 +25,7 @@ What the oracle computes, in the paper's notation:
   Attention itself is ordinary causal softmax attention (Section 3 intro:
   only what the cache stores changes).
 
-Readings where the pages are silent (each is also listed in the design doc):
+Readings where the pages are silent (each is a named choice, mirrored by the kernels):
   * RoPE pairing is rotate-half, pairs (i, i + d/2), theta_i = base^(-2i/d),
     applied over the full head width.  Parity unpinned by the pages: the
     pages name RoPE but print no convention.
