@@ -55,6 +55,8 @@ def parse():
                     help="instead of the benchmark, copy a buffer of this size a few times "
                          "(reference for HBM byte counters)")
     ap.add_argument("--no-encode", action="store_true", help=argparse.SUPPRESS)
+    ap.add_argument("--eager", action="store_true",
+                    help="report the eagerly launched step time (no HIP graph replay)")
     ap.add_argument("--summarize-counters", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
                     help="write profiles/traffic_<workload>.json from two rocprofv3 --pmc "
                          "output directories (FETCH_SIZE, WRITE_SIZE) and exit")
@@ -284,20 +286,38 @@ def main():
         step()
         torch.cuda.synchronize()
         log(f"[bench] warmup step {i + 1}/{args.warmup} done")
+
+    def timed(run):
+        torch.cuda.synchronize()
+        t_start = torch.cuda.Event(enable_timing=True)
+        t_end = torch.cuda.Event(enable_timing=True)
+        t_start.record(stream)
+        for _ in range(args.steps):
+            run()
+        t_end.record(stream)
+        torch.cuda.synchronize()
+        return t_start.elapsed_time(t_end) / args.steps
+
+    # Eager pass: every call launched from the host, a pair of events around
+    # each decode call (its duration feeds the roofline).
     ev = ([], [])
-    torch.cuda.synchronize()
-    t_start = torch.cuda.Event(enable_timing=True)
-    t_end = torch.cuda.Event(enable_timing=True)
-    t_start.record(stream)
-    for i in range(args.steps):
-        step(ev)
-    t_end.record(stream)
-    torch.cuda.synchronize()
-    ms_step = t_start.elapsed_time(t_end) / args.steps
+    ms_eager = timed(lambda: step(ev))
     call_ms = np.array([a.elapsed_time(b) for a, b in zip(*ev)])
-    log(f"[bench] {args.steps} steps: {ms_step:.3f} ms/step; decode call mean "
+    log(f"[bench] {args.steps} eager steps: {ms_eager:.3f} ms/step; decode call mean "
         f"{call_ms.mean() * 1e3:.1f} us (min {call_ms.min() * 1e3:.1f}, "
         f"max {call_ms.max() * 1e3:.1f})")
+    # Graph pass: the same step captured once as a HIP graph and replayed, so
+    # that host launch overhead (ctypes marshalling of 100+ calls) does not
+    # leave the GPU idle between short calls.  This is the step time reported.
+    ms_step = ms_eager
+    if not args.eager:
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            step()
+        graph.replay()
+        torch.cuda.synchronize()
+        ms_step = timed(graph.replay)
+        log(f"[bench] {args.steps} graph replays: {ms_step:.3f} ms/step")
     value = w.B / (ms_step / 1e3)
     bytes_call = algorithmic_bytes(w, w.N)
     path = L.lla_decode_path(store)
@@ -324,6 +344,8 @@ def main():
     res = {
         "metric": METRIC, "value": round(value, 2), "unit": "tokens/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_step, 4),
+        "ms_per_step_eager": round(ms_eager, 4),
+        "launch": "eager" if args.eager else "hip_graph_replay",
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16"
         if w.dtype == "bf16" else "f32", "data": "synthetic",
         "config": {"workload": w.name, "variant": w.variant, "B": w.B, "layers": w.D,

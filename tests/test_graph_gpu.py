@@ -1,0 +1,73 @@
+"""GPU: the decode and encode calls captured in a HIP graph (as the benchmark
+replays its step) give, on every replay, exactly what the same calls give
+when launched eagerly.  Replays are interleaved with eager work and
+synchronisations."""
+import numpy as np
+import pytest
+import torch
+
+import looped_transformer_decode_amd as L
+from synth.workloads import WORKLOADS, Codec
+from tests.gpu_cases import DecodeInputs, host_store, new_store, to_device
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.mark.parametrize("tmpl,kw", [
+    ("extreme_batch_b768_ctx4k", dict(B=3, D=2, N=300)),
+    ("lla2d_b256_ctx4k", dict(B=2, D=2, N=170)),
+    ("bf16_b32_ctx4k", dict(B=3, D=2, N=700, H=8)),      # several splits + merge
+], ids=["per_head", "lla2d", "per_head_split"])
+def test_graph_replay_matches_eager(device, tmpl, kw):
+    w = WORKLOADS[tmpl].scaled(**kw)
+    vals = host_store(w)
+    store = new_store(w, device, tensor=to_device(vals, w.dtype, device))
+    rope = L.rope_table(store, device)
+    codec = Codec(w)
+    inp = DecodeInputs(w, codec, 1, w.T - 1, device)
+    is2d = w.variant == "2d"
+    decode = L.lla2d_decode_attn if is2d else L.lla_decode_attn
+    encode = L.lla2d_encode_append if is2d else L.lla_encode_append
+    K = w.T * w.width
+    x = {a: codec.x(a, 0, w.B) for a in "kv"}
+    if is2d:
+        xs = [to_device(x[a].reshape(w.B, 1, K), w.dtype, device) for a in "kv"]
+        mus = [to_device(codec.mu(a, 0)[0], "f32", device) for a in "kv"]
+        wds = [to_device(codec.w_down(a, 0)[0], w.dtype, device) for a in "kv"]
+    else:
+        xs = [to_device(x[a].reshape(w.B, 1, w.H, K), w.dtype, device) for a in "kv"]
+        mus = [to_device(codec.mu(a, 0), "f32", device) for a in "kv"]
+        wds = [to_device(codec.w_down(a, 0), w.dtype, device) for a in "kv"]
+    pos = torch.tensor([w.N - 1, 41, 200][:w.B], dtype=torch.int32, device=device)
+    start = torch.full((w.B,), w.N - 1, dtype=torch.int32, device=device)
+    out = torch.empty((w.B, w.H, w.d), dtype=torch.float32, device=device)
+    ws = L.workspace(store)
+
+    def step():
+        decode(store, 1, w.T - 1, inp.d_q, inp.d_wk, inp.d_wv, inp.d_mk, inp.d_mv, pos, rope,
+               out, ws)
+        encode(store, 0, *xs, *mus, *wds, start)
+
+    store0 = store.tensor.clone()
+    step()
+    torch.cuda.synchronize()
+    want_out = out.clone()
+    want_store = store.tensor.clone()
+
+    store.tensor.copy_(store0)
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        step()
+    other_q = torch.randn_like(inp.d_q)
+    for rep in range(3):
+        out.zero_()
+        store.tensor.copy_(store0)
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out, want_out), f"replay {rep}: decode output differs"
+        assert torch.equal(store.tensor, want_store), f"replay {rep}: encoded store differs"
+        # eager work between replays, on the same buffers
+        decode(store, 1, 0, other_q, inp.d_wk, inp.d_wv, inp.d_mk, inp.d_mv, pos, rope, out, ws)
+        torch.cuda.synchronize()
+        assert np.isfinite(out.cpu().numpy()).all()
