@@ -184,6 +184,39 @@ lla_status_t lla2d_decode_attn(const lla_store_t *store, int32_t layer,
                                void *workspace, size_t ws_bytes,
                                int32_t n_splits, hipStream_t stream);
 
+/* ---------------------------------------------------------------------------
+ * Multi-query causal decode with the exact in-flight self-term.  In a looped
+ * model the tokens of the current step run their T loops before their
+ * latents can be encoded (Eq. 2 of the paper's Sec. 3 needs the whole T-loop
+ * stack), so at loop t they must attend to their own fresh loop-t keys and
+ * values in full precision.  For each sequence b the call handles n_q
+ * consecutive new tokens at positions pos0[b] .. pos0[b] + n_q - 1; query i
+ * attends
+ *   - the store slots 0 .. pos0[b] - 1 (reconstructed exactly as in
+ *     lla_decode_attn / lla2d_decode_attn, RoPE at each slot's position), and
+ *   - the in-flight tokens m = 0 .. i (causal), key RoPE(k_new[b][m], pos0[b] + m),
+ *     value v_new[b][m],
+ * with the query rotated at pos0[b] + i.  Works on per-head and LLA-2D stores
+ * (the store's variant selects the reconstruction).
+ *   n_q          1 .. 32
+ *   q, k_new, v_new  device, float32, [B, n_q, H, d] (pre-RoPE)
+ *   pos0         device, int32, [B]; clamped into [0, N]; positions past N-1
+ *                use the rotary phase of N-1
+ *   out          device, float32, [B, n_q, H, d]
+ *   workspace    >= lla_decode_inflight_workspace_bytes(store, n_q, n_splits)
+ *   other arguments as lla_decode_attn.
+ * ------------------------------------------------------------------------- */
+size_t lla_decode_inflight_workspace_bytes(const lla_store_t *store, int32_t n_q,
+                                           int32_t n_splits);
+lla_status_t lla_decode_attn_inflight(const lla_store_t *store, int32_t layer, int32_t loop,
+                                      int32_t n_q, const float *q, const float *k_new,
+                                      const float *v_new, const void *w_up_k_t,
+                                      const void *w_up_v_t, const float *mu_k_t,
+                                      const float *mu_v_t, const int32_t *pos0,
+                                      const void *rope_table, float softmax_scale, float *out,
+                                      void *workspace, size_t ws_bytes, int32_t n_splits,
+                                      hipStream_t stream);
+
 /* Name of the kernel family lla_decode_attn / lla2d_decode_attn would
  * launch for this store ("mfma" fast path or "valu" generic path), or NULL
  * for an invalid descriptor.  Host-only. */

@@ -5,7 +5,8 @@ HIP sources (csrc/), the in-tree build, and a thin ctypes binding whose
 functions carry the C entry points' names."""
 from .lla import (LLA_2D, LLA_DT_BF16, LLA_DT_F32, LLA_PER_HEAD, EXPORTS, LatentStore,
                   LlaError, StoreDesc, lib, lla2d_decode_attn, lla2d_encode_append,
-                  lla_compression_ratio, lla_decode_attn, lla_decode_auto_splits, lla_decode_path,
+                  lla_compression_ratio, lla_decode_attn, lla_decode_attn_inflight,
+                  lla_decode_auto_splits, lla_decode_inflight_workspace_bytes, lla_decode_path,
                   lla_decode_workspace_bytes, lla_encode_append, lla_rope_table_bytes,
                   lla_rope_table_fill, lla_store_bytes, lla_store_check, lla_store_offset,
                   rope_table, status_string, workspace)

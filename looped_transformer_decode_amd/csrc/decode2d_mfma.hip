@@ -158,13 +158,14 @@ __global__ __launch_bounds__(512, 1) void decode2d_split(DecodeParams p) {
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int s = blockIdx.x % p.S;
-  const int b = blockIdx.x / p.S;
+  const int vb = blockIdx.x / p.S;  // query (virtual sequence)
 
-  const int pos = min(max(p.pos[b], 0), p.N - 1);
+  const QuerySlot qs = query_slot(p, vb);
+  const int b = qs.b, pos = qs.qpos;
   const int t0 = s * p.split_len;
-  const int t1 = min(t0 + p.split_len, pos + 1);
-  float *part = p.ws + ((int64_t)b * H * p.S + s) * (RV + 2);  // head h at + h * S * (RV + 2)
-  if (t0 >= t1) {  // split entirely after the query: empty partials
+  const int t1 = min(t0 + p.split_len, qs.last + 1);
+  float *part = p.ws + ((int64_t)vb * H * p.S + s) * (RV + 2);  // head h at + h * S * (RV + 2)
+  if (t0 >= t1) {  // split entirely after the attended slots: empty partials
     for (int i = tid; i < H * (RV + 2); i += C::NT) {
       const int h = i / (RV + 2), r = i % (RV + 2);
       part[(int64_t)h * p.S * (RV + 2) + r] = (r == 0) ? -INFINITY : 0.f;
@@ -181,7 +182,7 @@ __global__ __launch_bounds__(512, 1) void decode2d_split(DecodeParams p) {
     const float *rq = p.rope_f32 + (int64_t)pos * kD;
     for (int i = tid; i < H * (kD / 2); i += C::NT) {
       const int h = i / (kD / 2), ii = i % (kD / 2);
-      const float *qb = p.q + ((int64_t)b * H + h) * kD;
+      const float *qb = p.q + ((int64_t)vb * H + h) * kD;
       const float c = rq[2 * ii], sn = rq[2 * ii + 1];
       const float a = qb[ii], bb = qb[ii + kD / 2];
       qr[h * kD + ii] = (a * c - bb * sn) * p.scale_log2;

@@ -119,16 +119,18 @@ __global__ __launch_bounds__(NW * 64, 1) void decode_mfma_split(DecodeParams p) 
   const int s = bid % p.S;
   bid /= p.S;
   const int g = bid % groups;
-  const int b = bid / groups;
+  const int vb = bid / groups;  // query (virtual sequence)
   const int h0 = g * C::HG;
 
-  const int pos = min(max(p.pos[b], 0), p.N - 1);
+  const QuerySlot qs = query_slot(p, vb);
+  const int b = qs.b;  // stored sequence
+  const int pos = qs.qpos;
   const int t0 = s * p.split_len;
-  const int t1 = min(t0 + p.split_len, pos + 1);
-  if (t0 >= t1) {  // split entirely after the query: empty partials
+  const int t1 = min(t0 + p.split_len, qs.last + 1);
+  if (t0 >= t1) {  // split entirely after the attended slots: empty partials
     for (int i = tid; i < C::HG * (RV + 2); i += C::NT) {
       const int hl = i / (RV + 2), r = i % (RV + 2);
-      p.ws[((int64_t)(b * p.H + h0 + hl) * p.S + s) * (RV + 2) + r] = (r == 0) ? -INFINITY : 0.f;
+      p.ws[((int64_t)(vb * p.H + h0 + hl) * p.S + s) * (RV + 2) + r] = (r == 0) ? -INFINITY : 0.f;
     }
     return;
   }
@@ -141,7 +143,7 @@ __global__ __launch_bounds__(NW * 64, 1) void decode_mfma_split(DecodeParams p) 
     const float *rq = p.rope_f32 + (int64_t)pos * kD;  // [kD/2][2] at pos
     for (int i = tid; i < C::HG * (kD / 2); i += C::NT) {
       const int hl = i / (kD / 2), ii = i % (kD / 2);
-      const float *qb = p.q + ((int64_t)b * p.H + h0 + hl) * kD;
+      const float *qb = p.q + ((int64_t)vb * p.H + h0 + hl) * kD;
       const float c = rq[2 * ii], sn = rq[2 * ii + 1];
       const float a = qb[ii], bb = qb[ii + kD / 2];
       qr[hl * kD + ii] = (a * c - bb * sn) * p.scale_log2;
@@ -377,12 +379,12 @@ __global__ __launch_bounds__(NW * 64, 1) void decode_mfma_split(DecodeParams p) 
         if (mi != -INFINITY) v = fmaf(src[i * (RV + 2) + r], exp2f(mi - M), v);
       }
     }
-    if (p.S == 1)
+    if (p.write_out)
       comb[o] = v;
     else
-      p.ws[((int64_t)(b * p.H + h0 + hl) * p.S + s) * (RV + 2) + r] = v;
+      p.ws[((int64_t)(vb * p.H + h0 + hl) * p.S + s) * (RV + 2) + r] = v;
   }
-  if (p.S == 1) {
+  if (p.write_out) {
     // A single split holds the whole softmax: apply W_up,v,t and mu_v,t here
     // (no merge launch).  out = W_up,v,t (acc / l) + mu_v,t, one thread per
     // output element, the bf16 row of W_up,v,t read as 16-byte vectors.
@@ -402,7 +404,7 @@ __global__ __launch_bounds__(NW * 64, 1) void decode_mfma_split(DecodeParams p) 
           a = fmaf(bf16_hi(wv[e]), c[3 + 8 * r8 + 2 * e], a);
         }
       }
-      const int64_t oi = ((int64_t)b * p.H + h0 + hl) * kD + i;
+      const int64_t oi = ((int64_t)vb * p.H + h0 + hl) * kD + i;
       p.out[oi] = fmaf(a, 1.0f / c[1], p.muv[(int64_t)(h0 + hl) * kD + i]);
     }
   }

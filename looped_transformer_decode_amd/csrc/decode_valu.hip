@@ -20,7 +20,7 @@ constexpr int kWaves = kThreads / 64;
 
 template <typename E, int RKM>
 __global__ __launch_bounds__(kThreads) void decode_valu_split(DecodeParams p) {
-  const int s = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+  const int s = blockIdx.x, h = blockIdx.y, vb = blockIdx.z;  // vb: query (virtual sequence)
   const int tid = threadIdx.x;
   const int d = p.d, half = d / 2, rk = p.rk, rv = p.rv;
 
@@ -31,11 +31,12 @@ __global__ __launch_bounds__(kThreads) void decode_valu_split(DecodeParams p) {
   float *pj = qr + d;                // [kThreads] weights of the current chunk
   float *red = pj + kThreads;        // [2 * kWaves]
 
-  const int pos = min(max(p.pos[b], 0), p.N - 1);
+  const QuerySlot qs = query_slot(p, vb);
+  const int b = qs.b, pos = qs.qpos;
   const int t0 = s * p.split_len;
-  const int t1 = min(t0 + p.split_len, pos + 1);
-  float *part = p.ws + ((int64_t)(b * p.H + h) * p.S + s) * (rv + 2);
-  if (t0 >= t1) {  // split entirely after the query: an empty partial
+  const int t1 = min(t0 + p.split_len, qs.last + 1);
+  float *part = p.ws + ((int64_t)(vb * p.H + h) * p.S + s) * (rv + 2);
+  if (t0 >= t1) {  // split entirely after the attended slots: an empty partial
     for (int r = tid; r < rv + 2; r += kThreads) part[r] = (r == 0) ? -INFINITY : 0.f;
     return;
   }
@@ -43,7 +44,7 @@ __global__ __launch_bounds__(kThreads) void decode_valu_split(DecodeParams p) {
   const E *wk = reinterpret_cast<const E *>(p.wk) + (int64_t)h * d * rk;
   for (int i = tid; i < d * rk; i += kThreads) Wk[i] = load_elem(wk, i);
   for (int i = tid; i < d; i += kThreads) muk[i] = p.muk[(int64_t)h * d + i];
-  const float *qb = p.q + ((int64_t)b * p.H + h) * d;
+  const float *qb = p.q + ((int64_t)vb * p.H + h) * d;
   const float *rq = p.rope_f32 + (int64_t)pos * d;  // [d/2][2] at the query position
   for (int i = tid; i < half; i += kThreads) {
     const float c = rq[2 * i], sn = rq[2 * i + 1];
@@ -250,6 +251,92 @@ __global__ __launch_bounds__(256) void decode_merge_batched(DecodeParams p) {
   }
 }
 
+// Multi-query causal merge with the in-flight tokens.  For query i of
+// sequence b (position pos0 + i) and head h the attended set is the store
+// slots < pos0 (the split partials (m, l, sum p c_v) of that query) plus the
+// in-flight tokens m <= i of the same call, whose loop-t keys and values
+// exist only in full precision (their latents need all T loops, Eq. 2):
+//   out = [e^(M_s - M) (W_up,v,t A + mu_v,t L_s) + sum_m e^(s_m - M) v_m]
+//         / [e^(M_s - M) L_s + sum_m e^(s_m - M)],
+//   s_m = scale * RoPE(q_i, pos0 + i) . RoPE(k_m, pos0 + m)   (log2 domain).
+// One block per (head, sequence); one thread per element of d.
+template <typename E>
+__global__ __launch_bounds__(256) void decode_merge_inflight(DecodeParams p, const float *k_new,
+                                                            const float *v_new) {
+  const int h = blockIdx.x, b = blockIdx.y, t = threadIdx.x, nt = blockDim.x;
+  const int d = p.d, half = d / 2, rv = p.rv, S = p.S, nq = p.qps, H = p.H;
+  const int lane = t & 63, wave = t >> 6, nw = nt >> 6;
+  extern __shared__ float sm[];
+  float *kr = sm;                 // [nq][d]  rotated in-flight keys
+  float *qr = kr + nq * d;        // [nq][d]  rotated, scaled queries
+  float *sc = qr + nq * d;        // [nq][nq] in-flight scores (m <= i)
+  float *abar = sc + nq * nq;     // [rv]     store latent numerator of one query
+  float *st = abar + rv;          // [2]      store M, L of one query
+  const int first = min(max(p.pos[b], 0), p.N);
+  const bool act = t < d;
+
+  // rotate-half RoPE of element t of x at position pp
+  auto rot = [&](const float *x, int pp) -> float {
+    const float *cs = p.rope_f32 + (int64_t)min(pp, p.N - 1) * d;  // [d/2][2]
+    if (t < half) return x[t] * cs[2 * t] - x[t + half] * cs[2 * t + 1];
+    const int u = t - half;
+    return x[t] * cs[2 * u] + x[u] * cs[2 * u + 1];
+  };
+  if (act) {
+    for (int m = 0; m < nq; ++m) {
+      const int64_t row = ((int64_t)(b * nq + m) * H + h) * d;
+      kr[m * d + t] = rot(k_new + row, first + m);
+      qr[m * d + t] = rot(p.q + row, first + m) * p.scale_log2;
+    }
+  }
+  __syncthreads();
+  // scores s[i][m], m <= i: one wave per dot product, lanes over d
+  for (int pr = wave; pr < nq * nq; pr += nw) {
+    const int i = pr / nq, m = pr % nq;
+    if (m > i) continue;
+    float v = 0.f;
+    for (int e = lane; e < d; e += 64) v = fmaf(qr[i * d + e], kr[m * d + e], v);
+    v = wave_sum(v);
+    if (lane == 0) sc[i * nq + m] = v;
+  }
+  const E *wrow = reinterpret_cast<const E *>(p.wv) + ((int64_t)h * d + (act ? t : 0)) * rv;
+  const float mu = act ? p.muv[(int64_t)h * d + t] : 0.f;
+  for (int i = 0; i < nq; ++i) {
+    const int vb = b * nq + i;
+    const float *part = p.ws + (int64_t)(vb * H + h) * S * (rv + 2);
+    __syncthreads();  // scores ready; previous query's abar / st consumed
+    for (int r = t; r < rv + 2; r += nt) {
+      float M = -INFINITY;
+      for (int s2 = 0; s2 < S; ++s2) M = fmaxf(M, part[s2 * (rv + 2)]);
+      float a = 0.f;
+      if (r > 0) {
+        for (int s2 = 0; s2 < S; ++s2) {
+          const float *ps = part + s2 * (rv + 2);
+          if (ps[0] != -INFINITY) a = fmaf(ps[r], exp2f(ps[0] - M), a);
+        }
+      }
+      if (r == 0) st[0] = M;
+      else if (r == 1) st[1] = a;
+      else abar[r - 2] = a;
+    }
+    __syncthreads();
+    if (!act) continue;
+    const float Ms = st[0], Ls = st[1];
+    float M = Ms;
+    for (int m = 0; m <= i; ++m) M = fmaxf(M, sc[i * nq + m]);
+    const float fs = (Ms == -INFINITY) ? 0.f : exp2f(Ms - M);
+    float wa = 0.f;
+    for (int r = 0; r < rv; ++r) wa = fmaf(load_elem(wrow, r), abar[r], wa);
+    float num = fs * fmaf(mu, Ls, wa), den = fs * Ls;
+    for (int m = 0; m <= i; ++m) {
+      const float e = exp2f(sc[i * nq + m] - M);
+      den += e;
+      num = fmaf(e, v_new[((int64_t)(b * nq + m) * H + h) * d + t], num);
+    }
+    p.out[((int64_t)vb * H + h) * d + t] = num / den;
+  }
+}
+
 template <typename E, int RKM>
 hipError_t launch_split(const DecodeParams &p, hipStream_t st) {
   const size_t sm = sizeof(float) * ((size_t)p.d * p.rk + 2 * p.d + kThreads + 2 * kWaves);
@@ -282,6 +369,18 @@ hipError_t launch_decode_merge_batched(const DecodeParams &p, int dtype, hipStre
     hipLaunchKernelGGL(decode_merge_batched<float>, grid, dim3(threads), sm, st, p);
   else
     hipLaunchKernelGGL(decode_merge_batched<bf16_t>, grid, dim3(threads), sm, st, p);
+  return hipGetLastError();
+}
+
+hipError_t launch_decode_merge_inflight(const DecodeParams &p, int32_t B_real, const float *k_new,
+                                        const float *v_new, int dtype, hipStream_t st) {
+  const int threads = (p.d + 63) / 64 * 64;
+  const size_t sm = sizeof(float) * ((size_t)2 * p.qps * p.d + (size_t)p.qps * p.qps + p.rv + 2);
+  dim3 grid(p.H, B_real);
+  if (dtype == LLA_DT_F32)
+    hipLaunchKernelGGL(decode_merge_inflight<float>, grid, dim3(threads), sm, st, p, k_new, v_new);
+  else
+    hipLaunchKernelGGL(decode_merge_inflight<bf16_t>, grid, dim3(threads), sm, st, p, k_new, v_new);
   return hipGetLastError();
 }
 

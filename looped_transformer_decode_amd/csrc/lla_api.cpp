@@ -98,15 +98,26 @@ bool use_mfma(const lla_store_t *s) {
 
 bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
 
+constexpr int32_t kMaxInflight = 32;  // in-flight tokens per call (merge kernel LDS)
+
+// n_q queries per stored sequence; with k_new / v_new (in-flight call) query
+// i of sequence b sits at pos[b] + i and the in-flight tokens are merged in.
 lla_status_t decode_impl(const lla_store_t *st, int32_t want_variant, int32_t layer,
                          int32_t loop, const float *q, const void *wk, const void *wv,
                          const float *muk, const float *muv, const int32_t *pos,
                          const void *rope, float scale, float *out, void *ws, size_t ws_bytes,
-                         int32_t n_splits, hipStream_t stream) {
+                         int32_t n_splits, hipStream_t stream, int32_t n_q = 1,
+                         const float *k_new = nullptr, const float *v_new = nullptr) {
   lla_status_t e = lla_store_check(st);
   if (e != LLA_OK) return e;
   if (st->variant != want_variant) return LLA_E_VARIANT;
   if (!st->data || !q || !wk || !wv || !muk || !muv || !pos || !rope || !out) return LLA_E_NULL;
+  const bool inflight = k_new != nullptr || v_new != nullptr;
+  if (inflight && (!k_new || !v_new)) return LLA_E_NULL;
+  if (n_q < 1) return LLA_E_RANGE;
+  if (n_q > kMaxInflight || (!inflight && n_q != 1)) return LLA_E_UNSUPPORTED;
+  if (inflight && st->d_head > 256) return LLA_E_UNSUPPORTED;
+  if ((int64_t)st->batch * n_q > INT32_MAX) return LLA_E_OVERFLOW;
   if (layer < 0 || layer >= st->layers || loop < 0 || loop >= st->loops) return LLA_E_RANGE;
   if (n_splits < 0 || n_splits > st->max_ctx) return LLA_E_RANGE;
   if (std::isnan(scale) || std::isinf(scale)) return LLA_E_RANGE;
@@ -122,13 +133,16 @@ lla_status_t decode_impl(const lla_store_t *st, int32_t want_variant, int32_t la
     if (slab >= (1ull << 31)) return LLA_E_UNSUPPORTED;
   }
   const int32_t S = n_splits ? n_splits : auto_splits(st, mfma);
-  const size_t need = lla_decode_workspace_bytes(st, S);
+  size_t need = lla_decode_workspace_bytes(st, S);
+  if (!mul_ok(need, (size_t)n_q, &need)) return LLA_E_OVERFLOW;
   if (!ws) return LLA_E_WORKSPACE;
   if (need == 0 || ws_bytes < need) return LLA_E_WORKSPACE;
 
   DecodeParams p{};
   p.store = st->data;
-  p.B = st->batch;
+  p.B = st->batch * n_q;  // queries
+  p.qps = n_q;
+  p.inflight = inflight ? 1 : 0;
   p.D = st->layers;
   p.N = st->max_ctx;
   p.H = st->heads;
@@ -156,13 +170,15 @@ lla_status_t decode_impl(const lla_store_t *st, int32_t want_variant, int32_t la
   p.out = out;
 
   const bool is2d = st->variant == LLA_2D;
+  p.write_out = (mfma && !is2d && S == 1 && !inflight) ? 1 : 0;
   hipError_t he = !mfma ? lla::launch_decode_valu(p, st->dtype, stream)
                   : is2d ? lla::launch_decode2d_mfma(p, stream)
                          : lla::launch_decode_mfma(p, stream);
   if (he != hipSuccess) return LLA_E_HIP;
-  if (mfma && !is2d && S == 1) return LLA_OK;  // the split kernel wrote out itself
-  he = is2d ? lla::launch_decode_merge_batched(p, st->dtype, stream)
-            : lla::launch_decode_merge(p, st->dtype, stream);
+  if (p.write_out) return LLA_OK;  // the split kernel applied W_up,v,t itself
+  he = inflight ? lla::launch_decode_merge_inflight(p, st->batch, k_new, v_new, st->dtype, stream)
+       : is2d   ? lla::launch_decode_merge_batched(p, st->dtype, stream)
+                : lla::launch_decode_merge(p, st->dtype, stream);
   return he == hipSuccess ? LLA_OK : LLA_E_HIP;
 }
 
@@ -356,6 +372,28 @@ lla_status_t lla2d_decode_attn(const lla_store_t *store, int32_t layer, int32_t 
                                hipStream_t stream) {
   return decode_impl(store, LLA_2D, layer, loop, q, w_up_k_t, w_up_v_t, mu_k_t, mu_v_t, pos,
                      rope_table, softmax_scale, out, workspace, ws_bytes, n_splits, stream);
+}
+
+size_t lla_decode_inflight_workspace_bytes(const lla_store_t *s, int32_t n_q, int32_t n_splits) {
+  if (n_q < 1) return 0;
+  size_t n = lla_decode_workspace_bytes(s, n_splits);
+  if (!mul_ok(n, (size_t)n_q, &n)) return 0;
+  return n;
+}
+
+lla_status_t lla_decode_attn_inflight(const lla_store_t *store, int32_t layer, int32_t loop,
+                                      int32_t n_q, const float *q, const float *k_new,
+                                      const float *v_new, const void *w_up_k_t,
+                                      const void *w_up_v_t, const float *mu_k_t,
+                                      const float *mu_v_t, const int32_t *pos0,
+                                      const void *rope_table, float softmax_scale, float *out,
+                                      void *workspace, size_t ws_bytes, int32_t n_splits,
+                                      hipStream_t stream) {
+  if (!k_new || !v_new) return LLA_E_NULL;
+  const int32_t variant = store ? store->variant : LLA_PER_HEAD;
+  return decode_impl(store, variant, layer, loop, q, w_up_k_t, w_up_v_t, mu_k_t, mu_v_t, pos0,
+                     rope_table, softmax_scale, out, workspace, ws_bytes, n_splits, stream, n_q,
+                     k_new, v_new);
 }
 
 const char *lla_decode_path(const lla_store_t *s) {

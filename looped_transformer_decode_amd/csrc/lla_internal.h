@@ -46,7 +46,30 @@ struct DecodeParams {
   int32_t S;               // context splits
   int32_t split_len;       // slots per split (multiple of 32)
   float *out;              // [B, H, d]
+  // Multi-query / in-flight calls: the B above counts queries (virtual
+  // sequences); query vb reads store sequence vb / qps.  With inflight set,
+  // query i = vb % qps of sequence b sits at position pos[b] + i and attends
+  // store slots < pos[b] only (its own loop-t keys are still in flight).
+  int32_t qps;
+  int32_t inflight;
+  int32_t write_out;       // the split kernel applies W_up,v,t itself (one split)
 };
+
+// Which store sequence a (virtual) query reads, its rotary position, and the
+// last store slot it attends (-1: none).
+struct QuerySlot {
+  int32_t b, qpos, last;
+};
+__device__ __forceinline__ QuerySlot query_slot(const DecodeParams &p, int32_t vb) {
+  const int32_t b = vb / p.qps;
+  const int32_t base = p.pos[b];
+  if (p.inflight) {
+    const int32_t first = min(max(base, 0), p.N);
+    return {b, min(first + (vb - b * p.qps), p.N - 1), first - 1};
+  }
+  const int32_t q = min(max(base, 0), p.N - 1);
+  return {b, q, q};
+}
 
 struct EncodeParams {
   void *store;
@@ -73,6 +96,11 @@ __host__ __device__ inline int32_t merge_heads_per_block(int32_t d, int32_t rv) 
 hipError_t launch_decode_valu(const DecodeParams &p, int dtype, hipStream_t s);
 hipError_t launch_decode_merge(const DecodeParams &p, int dtype, hipStream_t s);
 hipError_t launch_decode_merge_batched(const DecodeParams &p, int dtype, hipStream_t s);
+// In-flight merge: store partials of every query + the exact causal term of
+// the n_q in-flight tokens (k_new, v_new: [B, n_q, H, d] fp32).  B_real is
+// the number of stored sequences.
+hipError_t launch_decode_merge_inflight(const DecodeParams &p, int32_t B_real, const float *k_new,
+                                        const float *v_new, int dtype, hipStream_t s);
 bool decode2d_mfma_supported(int32_t H, int32_t d, int32_t rk, int32_t rv);
 hipError_t launch_decode2d_mfma(const DecodeParams &p, hipStream_t s);
 bool decode_mfma_supported(int32_t H, int32_t d, int32_t rk, int32_t rv, int32_t Hs);

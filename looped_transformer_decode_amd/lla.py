@@ -60,6 +60,9 @@ _SIGS = {
     "lla2d_decode_attn": ([_P, _I32, _I32, _P, _P, _P, _P, _P, _P, _P, _F, _P, _P, _SZ, _I32,
                            _P], _I32),
     "lla_decode_path": ([_P], ctypes.c_char_p),
+    "lla_decode_inflight_workspace_bytes": ([_P, _I32, _I32], _SZ),
+    "lla_decode_attn_inflight": ([_P, _I32, _I32, _I32, _P, _P, _P, _P, _P, _P, _P, _P, _P, _F,
+                                  _P, _P, _SZ, _I32, _P], _I32),
 }
 EXPORTS = tuple(_SIGS)
 
@@ -196,8 +199,14 @@ def lla_decode_path(store: LatentStore) -> str | None:
     return None if r is None else r.decode()
 
 
-def workspace(store: LatentStore, n_splits: int = 0, device=None) -> torch.Tensor:
-    n = lla_decode_workspace_bytes(store, n_splits)
+def lla_decode_inflight_workspace_bytes(store: LatentStore, n_q: int, n_splits: int = 0) -> int:
+    d = store.desc()
+    return lib().lla_decode_inflight_workspace_bytes(ctypes.byref(d), n_q, n_splits)
+
+
+def workspace(store: LatentStore, n_splits: int = 0, device=None, n_q: int = 1) -> torch.Tensor:
+    n = (lla_decode_workspace_bytes(store, n_splits) if n_q == 1
+         else lla_decode_inflight_workspace_bytes(store, n_q, n_splits))
     dev = device if device is not None else store.tensor.device
     return torch.empty(max(n, 4), dtype=torch.uint8, device=dev)
 
@@ -289,3 +298,37 @@ def lla2d_decode_attn(store, layer, loop, q, w_up_k_t, w_up_v_t, mu_k_t, mu_v_t,
     """LLA-2D decode: one latent per token decodes all H heads."""
     return _decode(lib().lla2d_decode_attn, store, layer, loop, q, w_up_k_t, w_up_v_t, mu_k_t,
                    mu_v_t, pos, rope_table, out, workspace, softmax_scale, n_splits, stream)
+
+
+def lla_decode_attn_inflight(store, layer, loop, q, k_new, v_new, w_up_k_t, w_up_v_t, mu_k_t,
+                             mu_v_t, pos0, rope_table, out, workspace, softmax_scale=0.0,
+                             n_splits=0, stream=None):
+    """Multi-query causal decode with the exact in-flight self-term: query i of
+    sequence b (position pos0[b] + i) attends store slots < pos0[b] and the
+    in-flight tokens 0..i (q, k_new, v_new, out: [B, n_q, H, d] float32)."""
+    s = store
+    H, d = s.heads, s.d_head
+    if q.dim() != 4:
+        raise ValueError("q must be [B, n_q, H, d]")
+    n_q = q.shape[1]
+    for t, nm in ((q, "q"), (k_new, "k_new"), (v_new, "v_new"), (out, "out")):
+        _need(t, torch.float32, (s.batch, n_q, H, d), nm)
+    if s.variant == LLA_PER_HEAD:
+        _need(w_up_k_t, s.torch_dtype, (H, d, s.r_k), "w_up_k_t")
+        _need(w_up_v_t, s.torch_dtype, (H, d, s.r_v), "w_up_v_t")
+        _need(mu_k_t, torch.float32, (H, d), "mu_k_t")
+        _need(mu_v_t, torch.float32, (H, d), "mu_v_t")
+    else:
+        _need(w_up_k_t, s.torch_dtype, (H * d, s.r_k), "w_up_k_t")
+        _need(w_up_v_t, s.torch_dtype, (H * d, s.r_v), "w_up_v_t")
+        _need(mu_k_t, torch.float32, (H * d,), "mu_k_t")
+        _need(mu_v_t, torch.float32, (H * d,), "mu_v_t")
+    _need(pos0, torch.int32, (s.batch,), "pos0")
+    dsc = s.desc()
+    f = lib().lla_decode_attn_inflight
+    _check(f(ctypes.byref(dsc), layer, loop, n_q, _ptr(q), _ptr(k_new), _ptr(v_new),
+             _ptr(w_up_k_t), _ptr(w_up_v_t), _ptr(mu_k_t), _ptr(mu_v_t), _ptr(pos0),
+             _ptr(rope_table), float(softmax_scale), _ptr(out), _ptr(workspace),
+             0 if workspace is None else workspace.numel() * workspace.element_size(), n_splits,
+             _stream(stream)), "lla_decode_attn_inflight")
+    return out

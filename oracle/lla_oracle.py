@@ -262,3 +262,46 @@ def materialise_loop_cache(c_k: np.ndarray, c_v: np.ndarray,
     V = np.stack([reconstruct(c_v, W_up_v[t], loop_slice(mu_v, t, d))
                   for t in range(T)])
     return K, V
+
+
+# --------------------------------------------------------------------------
+# Multi-query causal decode with the in-flight tokens
+# --------------------------------------------------------------------------
+def decode_inflight(c_k: np.ndarray, c_v: np.ndarray, q: np.ndarray, k_new: np.ndarray,
+                    v_new: np.ndarray, W_up_k_t: np.ndarray, W_up_v_t: np.ndarray,
+                    mu_k_t: np.ndarray, mu_v_t: np.ndarray, pos0: int,
+                    variant: str = "per_head", scale: float | None = None,
+                    base: float = ROPE_BASE) -> np.ndarray:
+    """Decode at loop t for n_q new tokens of one sequence whose latents do
+    not exist yet ([paper] Sec. 3 Eq. 2 needs the whole T-loop stack): new
+    token i sits at position pos0 + i and attends, with ordinary causal
+    softmax attention, the stored slots 0..pos0-1 (reconstructed by Eq. 3,
+    RoPE at each slot's position) and the new tokens 0..i through their own
+    loop-t keys and values k_new, v_new (RoPE at pos0 + m).
+
+    c_k, c_v: [N, H', r] latents of the (sequence, layer) slab (H' = H
+    per-head, 1 for LLA-2D); q, k_new, v_new: [n_q, H, d]; W_up_*_t, mu_*_t
+    as decode / decode_2d.  Returns out: [n_q, H, d]."""
+    q = np.asarray(q, np.float64)
+    n_q, H, d = q.shape
+    if scale is None:
+        scale = 1.0 / np.sqrt(d)
+    out = np.zeros((n_q, H, d))
+    for h in range(H):
+        if variant == "2d":
+            rows = slice(h * d, (h + 1) * d)
+            ck, cv = c_k[:pos0, 0], c_v[:pos0, 0]
+            Wk, Wv, mk, mv = W_up_k_t[rows], W_up_v_t[rows], mu_k_t[rows], mu_v_t[rows]
+        else:
+            ck, cv = c_k[:pos0, h], c_v[:pos0, h]
+            Wk, Wv, mk, mv = W_up_k_t[h], W_up_v_t[h], mu_k_t[h], mu_v_t[h]
+        K_store = rope(reconstruct(ck, Wk, mk), np.arange(pos0), base)      # [pos0, d]
+        V_store = reconstruct(cv, Wv, mv)
+        K_new = rope(np.asarray(k_new, np.float64)[:, h], pos0 + np.arange(n_q), base)
+        V_new = np.asarray(v_new, np.float64)[:, h]
+        for i in range(n_q):
+            K = np.concatenate([K_store, K_new[:i + 1]])
+            V = np.concatenate([V_store, V_new[:i + 1]])
+            p = _softmax(scale * (K @ rope(q[i, h], pos0 + i, base)))
+            out[i, h] = p @ V
+    return out

@@ -273,6 +273,66 @@ def pin_2d_reduces_to_per_head():
     assert np.abs(c1 - c2).max() < 1e-12
 
 
+def pin_inflight():
+    """Multi-query decode with in-flight tokens.
+    (a) A new token whose loop-t key/value are exactly the reconstruction of
+        a latent gives the store-only decode of that latent placed at slot
+        pos0 (the same attention, assembled from two independent paths).
+    (b) pos0 = 0, one new token: it attends only itself, out = v_new.
+    (c) Causality: query i ignores the new tokens after it.
+    (d) All queries against library attention (torch, fp64) over the
+        explicitly concatenated [materialised store; new] keys with a causal
+        mask, complex-number RoPE."""
+    rng = np.random.default_rng(12)
+    H, d, rk, rv, N, n_q = 2, 8, 3, 5, 30, 4
+    ck, cv = rng.standard_normal((N, H, rk)), rng.standard_normal((N, H, rv))
+    Wk, Wv = rng.standard_normal((H, d, rk)), rng.standard_normal((H, d, rv))
+    mk, mv = rng.standard_normal((H, d)), rng.standard_normal((H, d))
+    q = rng.standard_normal((n_q, H, d))
+    kn, vn = rng.standard_normal((n_q, H, d)), rng.standard_normal((n_q, H, d))
+    pos0 = 17
+    # (a)
+    k1 = np.stack([O.reconstruct(ck[pos0, h], Wk[h], mk[h]) for h in range(H)])
+    v1 = np.stack([O.reconstruct(cv[pos0, h], Wv[h], mv[h]) for h in range(H)])
+    got = O.decode_inflight(ck, cv, q[:1], k1[None], v1[None], Wk, Wv, mk, mv, pos0)[0]
+    ref = O.decode(ck, cv, q[0], Wk, Wv, mk, mv, pos0)
+    assert rel(got, ref) < 1e-12, rel(got, ref)
+    # (b)
+    got = O.decode_inflight(ck, cv, q[:1], kn[:1], vn[:1], Wk, Wv, mk, mv, 0)[0]
+    assert np.abs(got - vn[0]).max() < 1e-12
+    # (c)
+    a = O.decode_inflight(ck, cv, q, kn, vn, Wk, Wv, mk, mv, pos0)
+    kn2, vn2 = kn.copy(), vn.copy()
+    kn2[2:], vn2[2:] = rng.standard_normal((2, H, d)), rng.standard_normal((2, H, d))
+    b = O.decode_inflight(ck, cv, q, kn2, vn2, Wk, Wv, mk, mv, pos0)
+    assert np.array_equal(a[:2], b[:2]) and not np.allclose(a[2:], b[2:])
+    # (d)
+    for h in range(H):
+        Ks = rope_complex(ck[:pos0, h] @ Wk[h].T + mk[h], np.arange(pos0))
+        Vs = cv[:pos0, h] @ Wv[h].T + mv[h]
+        K = np.concatenate([Ks, rope_complex(kn[:, h], pos0 + np.arange(n_q))])
+        V = np.concatenate([Vs, vn[:, h]])
+        Q = rope_complex(q[:, h], pos0 + np.arange(n_q))
+        mask = np.arange(pos0 + n_q)[None, :] <= (pos0 + np.arange(n_q))[:, None]
+        ref = torch.nn.functional.scaled_dot_product_attention(
+            torch.from_numpy(Q)[None, None], torch.from_numpy(K)[None, None],
+            torch.from_numpy(V)[None, None], attn_mask=torch.from_numpy(mask)[None, None],
+            scale=1 / np.sqrt(d))[0, 0].numpy()
+        assert rel(a[:, h], ref) < 1e-12, (h, rel(a[:, h], ref))
+    # (e) LLA-2D with concatenated per-head latents and a block-diagonal W_up
+    #     is per-head LLA, in-flight tokens included
+    c2k = ck.reshape(N, 1, H * rk)
+    c2v = cv.reshape(N, 1, H * rv)
+    W2k = np.zeros((H * d, H * rk))
+    W2v = np.zeros((H * d, H * rv))
+    for h in range(H):
+        W2k[h * d:(h + 1) * d, h * rk:(h + 1) * rk] = Wk[h]
+        W2v[h * d:(h + 1) * d, h * rv:(h + 1) * rv] = Wv[h]
+    g = O.decode_inflight(c2k, c2v, q, kn, vn, W2k, W2v, mk.reshape(-1), mv.reshape(-1), pos0,
+                          variant="2d")
+    assert rel(g, a) < 1e-12
+
+
 def pin_bf16_round():
     one = 1.0
     cases = {one: one, one + 2 ** -8: one, one + 3 * 2 ** -8: one + 2 ** -6,
@@ -288,7 +348,7 @@ def pin_bf16_round():
 PINS = [pin_ratio_closed_form, pin_serving_capacity_example, pin_store_offset,
         pin_exact_reconstruction, pin_decode_equals_teacher_attention,
         pin_decode_equals_materialised_cache, pin_special_cases, pin_rope,
-        pin_2d_reduces_to_per_head, pin_bf16_round]
+        pin_2d_reduces_to_per_head, pin_bf16_round, pin_inflight]
 
 
 @pytest.mark.parametrize("pin", PINS, ids=[p.__name__ for p in PINS])

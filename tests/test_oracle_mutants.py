@@ -56,7 +56,45 @@ def _decode_2d_interleaved_heads(c_k, c_v, q, W_up_k_t, W_up_v_t, mu_k_t, mu_v_t
                      for h in range(H)])
 
 
+def _inflight_variant(new_pos_shift=0, causal=True, q_at_pos0=False, store_extra=0,
+                      new_values_are_keys=False):
+    """decode_inflight with one planted slip."""
+    def decode_inflight(c_k, c_v, q, k_new, v_new, W_up_k_t, W_up_v_t, mu_k_t, mu_v_t, pos0,
+                        variant="per_head", scale=None, base=O.ROPE_BASE):
+        q = np.asarray(q, np.float64)
+        n_q, H, d = q.shape
+        scale = 1.0 / np.sqrt(d) if scale is None else scale
+        out = np.zeros((n_q, H, d))
+        ns = pos0 + store_extra
+        for h in range(H):
+            if variant == "2d":
+                rows = slice(h * d, (h + 1) * d)
+                ck, cv = c_k[:ns, 0], c_v[:ns, 0]
+                Wk, Wv, mk, mv = W_up_k_t[rows], W_up_v_t[rows], mu_k_t[rows], mu_v_t[rows]
+            else:
+                ck, cv = c_k[:ns, h], c_v[:ns, h]
+                Wk, Wv, mk, mv = W_up_k_t[h], W_up_v_t[h], mu_k_t[h], mu_v_t[h]
+            Ks = O.rope(O.reconstruct(ck, Wk, mk), np.arange(ns), base)
+            Vs = O.reconstruct(cv, Wv, mv)
+            Kn = O.rope(np.asarray(k_new, np.float64)[:, h],
+                        pos0 + np.arange(n_q) + new_pos_shift, base)
+            Vn = (np.asarray(k_new if new_values_are_keys else v_new, np.float64))[:, h]
+            for i in range(n_q):
+                m = i + 1 if causal else n_q
+                K, V = np.concatenate([Ks, Kn[:m]]), np.concatenate([Vs, Vn[:m]])
+                s = scale * (K @ O.rope(q[i, h], pos0 if q_at_pos0 else pos0 + i, base))
+                e = np.exp(s - s.max())
+                out[i, h] = (e / e.sum()) @ V
+        return out
+    return decode_inflight
+
+
 MUTANTS = {
+    "inflight_keys_rotated_one_early": ("decode_inflight", _inflight_variant(new_pos_shift=-1)),
+    "inflight_not_causal": ("decode_inflight", _inflight_variant(causal=False)),
+    "inflight_queries_at_pos0": ("decode_inflight", _inflight_variant(q_at_pos0=True)),
+    "inflight_store_one_slot_long": ("decode_inflight", _inflight_variant(store_extra=1)),
+    "inflight_values_are_keys": ("decode_inflight", _inflight_variant(new_values_are_keys=True)),
     "reconstruct_drops_mu": ("reconstruct", lambda c, W, mu: np.asarray(c) @ np.asarray(W).T),
     "encode_uncentred": ("encode", lambda x, mu, W: np.asarray(x) @ np.asarray(W)),
     "encode_adds_mu": ("encode", lambda x, mu, W: (np.asarray(x) + mu) @ np.asarray(W)),

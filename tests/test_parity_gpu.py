@@ -220,6 +220,130 @@ def test_garbage_beyond_pos_is_ignored(device, tmpl):
     assert row_rel_l2(got, ref).max() <= TOL["bf16"]
 
 
+# ----------------------------------------------------------------- in-flight
+INFLIGHT_SHAPES = [
+    ("long_recurrence_t16_ctx8k", dict(B=2, D=2, N=300, H=8), 16),   # fast path, n_q = 16
+    ("extreme_batch_b768_ctx4k", dict(B=3, D=1, N=200), 4),
+    ("tiny_fp32", dict(B=3, N=128), 3),                              # generic fp32 path
+    ("lla2d_b256_ctx4k", dict(B=2, D=1, N=170), 4),                  # LLA-2D fast path
+]
+
+
+def inflight_case(w, n_q, pos0, device, n_splits=0, layer=None):
+    """Returns (gpu [B, n_q, H, d], oracle [B, n_q, H, d])."""
+    layer = w.D - 1 if layer is None else layer
+    t = w.T - 1
+    say(f"[inflight] {w.name} {w.variant} {w.dtype} B={w.B} N={w.N} H={w.H} n_q={n_q} "
+        f"pos0={list(pos0)} splits={n_splits}")
+    vals = host_store(w)
+    store = new_store(w, device, tensor=to_device(vals, w.dtype, device))
+    rope = L.rope_table(store, device)
+    inp = DecodeInputs(w, Codec(w), layer, t, device)
+    rng = np.random.default_rng(w.seed + 77)
+    f32 = lambda a: a.astype(np.float32).astype(np.float64)
+    q = f32(rng.standard_normal((w.B, n_q, w.H, w.d)))
+    kn = f32(rng.standard_normal((w.B, n_q, w.H, w.d)))
+    vn = f32(rng.standard_normal((w.B, n_q, w.H, w.d)))
+    out = torch.empty((w.B, n_q, w.H, w.d), dtype=torch.float32, device=device)
+    ws = L.workspace(store, n_splits, n_q=n_q)
+    L.lla_decode_attn_inflight(store, layer, t, to_device(q, "f32", device),
+                               to_device(kn, "f32", device), to_device(vn, "f32", device),
+                               inp.d_wk, inp.d_wv, inp.d_mk, inp.d_mv,
+                               torch.from_numpy(np.asarray(pos0, np.int32)).to(device), rope, out,
+                               ws, n_splits=n_splits)
+    torch.cuda.synchronize()
+    got = out.cpu().numpy().astype(np.float64)
+    is2d = w.variant == "2d"
+    ref = np.stack([O.decode_inflight(vals[b, layer, :, :, :w.r_k], vals[b, layer, :, :, w.r_k:],
+                                      q[b], kn[b], vn[b], inp.wk.reshape(-1, w.r_k) if is2d
+                                      else inp.wk, inp.wv.reshape(-1, w.r_v) if is2d else inp.wv,
+                                      inp.mk.reshape(-1) if is2d else inp.mk,
+                                      inp.mv.reshape(-1) if is2d else inp.mv, int(pos0[b]),
+                                      variant=w.variant) for b in range(w.B)])
+    return got, ref
+
+
+@pytest.mark.parametrize("tmpl,kw,n_q", INFLIGHT_SHAPES,
+                         ids=[f"{t}-nq{n}" for t, _, n in INFLIGHT_SHAPES])
+def test_inflight_vs_oracle(device, tmpl, kw, n_q):
+    w = small(tmpl, **kw)
+    pos0 = np.array([w.N - n_q, 0, 57][:w.B])
+    for n_splits in (1, 3, 0):
+        got, ref = inflight_case(w, n_q, pos0, device, n_splits=n_splits)
+        err = row_rel_l2(got, ref)
+        say(f"  splits={n_splits} max row rel L2 {err.max():.3e}")
+        assert err.max() <= TOL[w.dtype]
+        assert np.isfinite(got).all()
+
+
+def test_inflight_single_query_matches_decode(device):
+    """One in-flight token whose key/value are the exact reconstruction of
+    the latent at slot pos0 = the store-only decode at pos0 (same kernels'
+    store part, different assembly)."""
+    w = small("extreme_batch_b768_ctx4k", B=2, D=1, N=160)
+    vals = host_store(w)
+    store = new_store(w, device, tensor=to_device(vals, w.dtype, device))
+    rope = L.rope_table(store, device)
+    inp = DecodeInputs(w, Codec(w), 0, 1, device)
+    pos = np.array([159, 40])
+    want = inp.run(store, pos, rope)
+    ck = vals[np.arange(w.B), 0, pos][:, :, :w.r_k]                 # [B, H, r_k]
+    cv = vals[np.arange(w.B), 0, pos][:, :, w.r_k:]
+    kn = np.einsum("hdr,bhr->bhd", inp.wk, ck) + inp.mk[None]
+    vn = np.einsum("hdr,bhr->bhd", inp.wv, cv) + inp.mv[None]
+    out = torch.empty((w.B, 1, w.H, w.d), dtype=torch.float32, device=device)
+    L.lla_decode_attn_inflight(store, 0, 1, inp.d_q[:, None].contiguous(),
+                               to_device(kn[:, None], "f32", device),
+                               to_device(vn[:, None], "f32", device), inp.d_wk, inp.d_wv,
+                               inp.d_mk, inp.d_mv,
+                               torch.from_numpy(pos.astype(np.int32)).to(device), rope, out,
+                               L.workspace(store, n_q=1))
+    torch.cuda.synchronize()
+    got = out.cpu().numpy()[:, 0].astype(np.float64)
+    assert row_rel_l2(got, want).max() <= TOL["bf16"]
+
+
+def test_inflight_full_size_sampled(device):
+    """Long-recurrence shape at full size (B=64, N=8192, T=16) with the
+    step's 16 appended tokens in flight, launched as the benchmark launches
+    it; sampled sequences against the oracle on slabs regenerated on the host."""
+    w = WORKLOADS["long_recurrence_t16_ctx8k"]
+    n_q = w.n_new
+    say(f"[inflight full] {w.name}: n_q={n_q}")
+    torch.cuda.empty_cache()
+    store = new_store(w, device)
+    fill_store_on_device(w, store)
+    rope = L.rope_table(store, device)
+    layer, t = w.D - 1, w.T - 1
+    inp = DecodeInputs(w, Codec(w), layer, t, device)
+    rng = np.random.default_rng(w.seed + 78)
+    f32 = lambda a: a.astype(np.float32).astype(np.float64)
+    q = f32(rng.standard_normal((w.B, n_q, w.H, w.d)))
+    kn = f32(rng.standard_normal((w.B, n_q, w.H, w.d)))
+    vn = f32(rng.standard_normal((w.B, n_q, w.H, w.d)))
+    pos0 = np.full(w.B, w.N - n_q)
+    pos0[1::3] = rng.integers(0, w.N - n_q, size=len(pos0[1::3]))
+    out = torch.empty((w.B, n_q, w.H, w.d), dtype=torch.float32, device=device)
+    L.lla_decode_attn_inflight(store, layer, t, to_device(q, "f32", device),
+                               to_device(kn, "f32", device), to_device(vn, "f32", device),
+                               inp.d_wk, inp.d_wv, inp.d_mk, inp.d_mv,
+                               torch.from_numpy(pos0.astype(np.int32)).to(device), rope, out,
+                               L.workspace(store, n_q=n_q))
+    torch.cuda.synchronize()
+    got = out.cpu().numpy().astype(np.float64)
+    worst = 0.0
+    for b in sorted({0, 1, w.B - 1}):
+        ck, cv = device_slab(w, b, layer)
+        ref = O.decode_inflight(ck, cv, q[b], kn[b], vn[b], inp.wk, inp.wv, inp.mk, inp.mv,
+                                int(pos0[b]))
+        err = row_rel_l2(got[b], ref).max()
+        worst = max(worst, err)
+        say(f"  b={b} pos0={pos0[b]} max row rel L2 {err:.3e}")
+    assert worst <= TOL["bf16"]
+    del store
+    torch.cuda.empty_cache()
+
+
 # ----------------------------------------------------------------- encode
 ENCODE_SHAPES = [
     ("extreme_batch_b768_ctx4k", dict(B=5, D=2, N=64)),
