@@ -55,6 +55,9 @@ def parse():
                     help="instead of the benchmark, copy a buffer of this size a few times "
                          "(reference for HBM byte counters)")
     ap.add_argument("--no-encode", action="store_true", help=argparse.SUPPRESS)
+    ap.add_argument("--inflight", action="store_true",
+                    help="decode with the step's n_new tokens in flight (multi-query causal "
+                         "call with their exact loop-t keys and values)")
     ap.add_argument("--eager", action="store_true",
                     help="report the eagerly launched step time (no HIP graph replay)")
     ap.add_argument("--summarize-counters", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
@@ -261,6 +264,17 @@ def main():
     start = torch.full((w.B,), w.N - w.n_new, dtype=torch.int32, device=dev)
     out = torch.empty((w.B, w.H, w.d), dtype=torch.float32, device=dev)
     ws = L.workspace(store, args.splits)
+    nq = w.n_new if args.inflight else 1
+    if args.inflight:
+        # the step's n_new tokens run their loops before their latents exist:
+        # every decode call is the multi-query call with them in flight
+        qi = torch.empty((w.D, w.T, w.B, nq, w.H, w.d), dtype=torch.float32, device=dev)
+        fill_hash_normal(qi, gen.stream_key(w.seed, TID_Q) + 1)
+        kvi = torch.empty((2, w.D, w.T, w.B, nq, w.H, w.d), dtype=torch.float32, device=dev)
+        fill_hash_normal(kvi, gen.stream_key(w.seed, TID_Q) + 2)
+        pos0 = start
+        out = torch.empty((w.B, nq, w.H, w.d), dtype=torch.float32, device=dev)
+        ws = L.workspace(store, args.splits, n_q=nq)
     decode = L.lla2d_decode_attn if is2d else L.lla_decode_attn
     encode = L.lla2d_encode_append if is2d else L.lla_encode_append
     stream = torch.cuda.current_stream()
@@ -273,8 +287,13 @@ def main():
                 if events is not None:
                     events[0].append(torch.cuda.Event(enable_timing=True))
                     events[0][-1].record(stream)
-                decode(store, l, t, q[l, t], wk[l, t], wv[l, t], mk[l, t], mv[l, t], pos, rope,
-                       out, ws, n_splits=args.splits)
+                if args.inflight:
+                    L.lla_decode_attn_inflight(store, l, t, qi[l, t], kvi[0, l, t], kvi[1, l, t],
+                                               wk[l, t], wv[l, t], mk[l, t], mv[l, t], pos0,
+                                               rope, out, ws, n_splits=args.splits)
+                else:
+                    decode(store, l, t, q[l, t], wk[l, t], wv[l, t], mk[l, t], mv[l, t], pos,
+                           rope, out, ws, n_splits=args.splits)
                 if events is not None:
                     events[1].append(torch.cuda.Event(enable_timing=True))
                     events[1][-1].record(stream)
@@ -318,8 +337,12 @@ def main():
         torch.cuda.synchronize()
         ms_step = timed(graph.replay)
         log(f"[bench] {args.steps} graph replays: {ms_step:.3f} ms/step")
-    value = w.B / (ms_step / 1e3)
+    value = w.B * nq / (ms_step / 1e3)   # generated tokens per second, all sequences
     bytes_call = algorithmic_bytes(w, w.N)
+    if args.inflight:
+        # store slots before pos0 once, plus q, k_new, v_new and out of every query
+        bytes_call = (algorithmic_bytes(w, w.N - w.n_new) - 2 * w.B * w.H * w.d * 4
+                      + 4 * w.B * nq * w.H * w.d * 4)
     path = L.lla_decode_path(store)
     if w.variant == "2d":
         flops_call = algorithmic_flops(w, w.N)
@@ -338,8 +361,10 @@ def main():
         roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                     "traffic": traffic_for_current_kernel(w),
-                    "kernel": "decode_mfma_split (one lla_decode_attn call"
-                              + (")" if splits == 1 and path == "mfma" else " + decode_merge)"),
+                    "kernel": ("decode_mfma_split + decode_merge_inflight (one "
+                               "lla_decode_attn_inflight call)") if args.inflight else
+                              ("decode_mfma_split (one lla_decode_attn call"
+                               + (")" if splits == 1 and path == "mfma" else " + decode_merge)")),
                     "bytes_per_launch": bytes_call, "launch_us": round(call_ms.mean() * 1e3, 2)}
     res = {
         "metric": METRIC, "value": round(value, 2), "unit": "tokens/s", "n_gpus": 1,
@@ -352,7 +377,9 @@ def main():
                    "ctx": w.N, "heads": w.H, "d_head": w.d, "loops": w.T, "r_k": w.r_k,
                    "r_v": w.r_v, "rho": str(L.lla_compression_ratio(store)),
                    "calls_per_step": w.D * w.T, "encode_appends_per_step": 0 if args.no_encode
-                   else w.D, "splits": args.splits or L.lla_decode_auto_splits(store),
+                   else w.D, "tokens_per_sequence_per_step": nq,
+                   "in_flight": bool(args.inflight),
+                   "splits": args.splits or L.lla_decode_auto_splits(store),
                    "path": path},
         "roofline": roofline,
     }
