@@ -305,3 +305,48 @@ def decode_inflight(c_k: np.ndarray, c_v: np.ndarray, q: np.ndarray, k_new: np.n
             p = _softmax(scale * (K @ rope(q[i, h], pos0 + i, base)))
             out[i, h] = p @ V
     return out
+
+
+# --------------------------------------------------------------------------
+# Uncompressed K/V cache: the serving "fast path" and the final-loop control
+# --------------------------------------------------------------------------
+def fast_path_rows(c_k: np.ndarray, c_v: np.ndarray, W_up_k_t: np.ndarray,
+                   W_up_v_t: np.ndarray, mu_k_t: np.ndarray, mu_v_t: np.ndarray,
+                   positions, base: float = ROPE_BASE):
+    """The rows the serving fast path caches ([summary] "Serving Capacity":
+    reconstruct once, keep full K/V): for latents c_*: [n, r] of the slots at
+    `positions`, the loop-t key reconstructed by Eq. 3 and then rotated at
+    its slot ("RoPE and reconstruction"), and the loop-t value.
+    Returns (K, V): [n, d] each."""
+    K = rope(reconstruct(c_k, W_up_k_t, mu_k_t), positions, base)
+    V = reconstruct(c_v, W_up_v_t, mu_v_t)
+    return K, V
+
+
+def cache_rows(k: np.ndarray, v: np.ndarray, positions, base: float = ROPE_BASE):
+    """What an ordinary K/V cache stores for raw keys/values k, v: [n, d]
+    at `positions`: the key rotated at its slot, the value unchanged."""
+    return rope(k, positions, base), np.asarray(v, np.float64)
+
+
+def decode_cache(K: np.ndarray, V: np.ndarray, q: np.ndarray, pos: int,
+                 scale: float | None = None, base: float = ROPE_BASE) -> np.ndarray:
+    """Ordinary causal softmax attention of one head's pre-RoPE query q: [d]
+    at position pos over a cache whose keys K: [N, d] are already rotated
+    (values V: [N, d]): softmax(scale * K[:pos+1] . RoPE(q, pos)) V[:pos+1]."""
+    q = np.asarray(q, np.float64)
+    d = q.shape[-1]
+    if scale is None:
+        scale = 1.0 / np.sqrt(d)
+    n = pos + 1
+    p = _softmax(scale * (np.asarray(K, np.float64)[:n] @ rope(q, pos, base)))
+    return p @ np.asarray(V, np.float64)[:n]
+
+
+def final_loop_control(k_last: np.ndarray, v_last: np.ndarray, q_t: np.ndarray, pos: int,
+                       scale: float | None = None, base: float = ROPE_BASE) -> np.ndarray:
+    """The zero-parameter control of [paper] Sec. 3 (matched-axis baselines):
+    only the final loop's keys and values k_last, v_last: [N, d] (pre-RoPE)
+    are cached, and the query of every loop t attends to them.  q_t: [d]."""
+    K, V = cache_rows(k_last, v_last, np.arange(np.asarray(k_last).shape[0]), base)
+    return decode_cache(K, V, q_t, pos, scale, base)

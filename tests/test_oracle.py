@@ -345,10 +345,73 @@ def pin_bf16_round():
     assert np.array_equal(O.bf16_round(x32.astype(np.float64)), want)
 
 
+def pin_kv_cache():
+    """The uncompressed-cache paths: the serving fast path ([summary]
+    "Serving Capacity") and the final-loop control ([paper] Sec. 3,
+    matched-axis baselines).
+    (a) decode_cache over cache_rows equals torch's library attention (fp64)
+        over keys rotated by complex multiplication, at every position.
+    (b) fast_path_rows equals c W^T + mu rotated by complex multiplication at
+        the slot, and decoding over them equals the LLA oracle (reconstruct on
+        read) at every position: the two serving paths compute one thing.
+    (c) Special cases: at pos = 0 the output is V[0]; with all keys equal it
+        is the mean of V[:pos+1].
+    (d) With an exact codec (r = T*d, square orthonormal W_down, W_up,t its
+        loop-t rows) LLA at the final loop equals the control; at loop 0 the
+        control still attends final-loop keys and differs."""
+    rng = np.random.default_rng(21)
+    d, N, rk, rv = 8, 19, 3, 5
+    k, v = rng.standard_normal((N, d)), rng.standard_normal((N, d))
+    q = rng.standard_normal(d)
+    K, V = O.cache_rows(k, v, np.arange(N))
+    for pos in (0, 1, 7, N - 1):
+        got = O.decode_cache(K, V, q, pos)
+        ref = sdpa_last_query(rope_complex(q, pos), rope_complex(k[:pos + 1], np.arange(pos + 1)),
+                              v[:pos + 1], 1 / np.sqrt(d))
+        assert rel(got, ref) < 1e-12, (pos, rel(got, ref))
+    # (b)
+    ck, cv = rng.standard_normal((N, rk)), rng.standard_normal((N, rv))
+    Wk, Wv = rng.standard_normal((d, rk)), rng.standard_normal((d, rv))
+    mk, mv = rng.standard_normal(d), rng.standard_normal(d)
+    Kf, Vf = O.fast_path_rows(ck, cv, Wk, Wv, mk, mv, np.arange(N))
+    assert rel(Kf, rope_complex(ck @ Wk.T + mk, np.arange(N))) < 1e-12
+    assert rel(Vf, cv @ Wv.T + mv) < 1e-12
+    for pos in (0, 5, N - 1):
+        got = O.decode_cache(Kf, Vf, q, pos)
+        ref = O.decode_head(ck, cv, q, Wk, Wv, mk, mv, pos)
+        assert rel(got, ref) < 1e-12, (pos, rel(got, ref))
+    # rows for a slot range starting past 0 are those rows of the full fill
+    K3, V3 = O.fast_path_rows(ck[4:9], cv[4:9], Wk, Wv, mk, mv, np.arange(4, 9))
+    assert rel(K3, Kf[4:9]) < 1e-14 and rel(V3, Vf[4:9]) < 1e-14
+    # (c)
+    assert np.abs(O.decode_cache(K, V, q, 0) - v[0]).max() < 1e-12
+    Keq = np.tile(rng.standard_normal(d), (N, 1))
+    assert np.abs(O.decode_cache(Keq, V, q, 9) - v[:10].mean(0)).max() < 1e-12
+    # (d)
+    T, dd, n = 3, 4, 11
+    xk = rng.standard_normal((n, T, dd))
+    xv = rng.standard_normal((n, T, dd))
+    muk, muv = rng.standard_normal(T * dd), rng.standard_normal(T * dd)
+    Qk, _ = np.linalg.qr(rng.standard_normal((T * dd, T * dd)))
+    Qv, _ = np.linalg.qr(rng.standard_normal((T * dd, T * dd)))
+    c_k = O.encode(O.stack_loops(xk), muk, Qk)
+    c_v = O.encode(O.stack_loops(xv), muv, Qv)
+    qq = rng.standard_normal(dd)
+    pos = n - 1
+    for t in (T - 1, 0):
+        lla = O.decode_head(c_k, c_v, qq, Qk[t * dd:(t + 1) * dd], Qv[t * dd:(t + 1) * dd],
+                            O.loop_slice(muk, t, dd), O.loop_slice(muv, t, dd), pos)
+        ctl = O.final_loop_control(xk[:, T - 1], xv[:, T - 1], qq, pos)
+        if t == T - 1:
+            assert rel(ctl, lla) < 1e-10, rel(ctl, lla)
+        else:
+            assert rel(ctl, lla) > 1e-3
+
+
 PINS = [pin_ratio_closed_form, pin_serving_capacity_example, pin_store_offset,
         pin_exact_reconstruction, pin_decode_equals_teacher_attention,
         pin_decode_equals_materialised_cache, pin_special_cases, pin_rope,
-        pin_2d_reduces_to_per_head, pin_bf16_round, pin_inflight]
+        pin_2d_reduces_to_per_head, pin_bf16_round, pin_inflight, pin_kv_cache]
 
 
 @pytest.mark.parametrize("pin", PINS, ids=[p.__name__ for p in PINS])

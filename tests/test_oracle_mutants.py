@@ -89,7 +89,43 @@ def _inflight_variant(new_pos_shift=0, causal=True, q_at_pos0=False, store_extra
     return decode_inflight
 
 
+def _decode_cache_variant(rotate_q=True, extra=0):
+    def decode_cache(K, V, q, pos, scale=None, base=O.ROPE_BASE):
+        q = np.asarray(q, np.float64)
+        d = q.shape[-1]
+        scale = 1.0 / np.sqrt(d) if scale is None else scale
+        n = pos + 1 + extra
+        s = scale * (np.asarray(K)[:n] @ (O.rope(q, pos, base) if rotate_q else q))
+        e = np.exp(s - s.max())
+        return (e / e.sum()) @ np.asarray(V)[:n]
+    return decode_cache
+
+
+def _fast_path_variant(rotate_before_mu=False, rotate_values=False):
+    def fast_path_rows(c_k, c_v, W_up_k_t, W_up_v_t, mu_k_t, mu_v_t, positions,
+                       base=O.ROPE_BASE):
+        if rotate_before_mu:
+            K = O.rope(np.asarray(c_k) @ np.asarray(W_up_k_t).T, positions, base) + mu_k_t
+        else:
+            K = O.rope(O.reconstruct(c_k, W_up_k_t, mu_k_t), positions, base)
+        V = O.reconstruct(c_v, W_up_v_t, mu_v_t)
+        return K, (O.rope(V, positions, base) if rotate_values else V)
+    return fast_path_rows
+
+
 MUTANTS = {
+    "cache_keys_not_rotated": ("cache_rows", lambda k, v, positions, base=O.ROPE_BASE:
+                               (np.asarray(k, np.float64), np.asarray(v, np.float64))),
+    "cache_values_rotated": ("cache_rows", lambda k, v, positions, base=O.ROPE_BASE:
+                             (O.rope(k, positions, base), O.rope(v, positions, base))),
+    "decode_cache_query_not_rotated": ("decode_cache", _decode_cache_variant(rotate_q=False)),
+    "decode_cache_one_slot_long": ("decode_cache", _decode_cache_variant(extra=1)),
+    "fast_path_rotates_before_mu": ("fast_path_rows", _fast_path_variant(rotate_before_mu=True)),
+    "fast_path_rotates_values": ("fast_path_rows", _fast_path_variant(rotate_values=True)),
+    "control_keys_at_slot_zero": ("final_loop_control",
+                                  lambda k_last, v_last, q_t, pos, scale=None, base=O.ROPE_BASE:
+                                  O.decode_cache(O.rope(k_last, 0, base), v_last, q_t, pos,
+                                                 scale, base)),
     "inflight_keys_rotated_one_early": ("decode_inflight", _inflight_variant(new_pos_shift=-1)),
     "inflight_not_causal": ("decode_inflight", _inflight_variant(causal=False)),
     "inflight_queries_at_pos0": ("decode_inflight", _inflight_variant(q_at_pos0=True)),
