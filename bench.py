@@ -17,6 +17,14 @@ Prints one JSON line (rank 0, N = 1 GPU):
                traffic = HBM bytes per launch from the committed rocprofv3
                FETCH_SIZE / WRITE_SIZE summary (null if the kernel changed).
   cpu_baseline = the fp64 oracle timed on a bounded sample on host cores
+
+--path fast / final_loop time the two uncompressed-cache paths on the same
+workload instead (a cache [B, D, L, N, H, 2, d]): the serving fast path
+(every loop's K/V reconstructed once into the cache, L = T, plain
+flash-decode; each step encodes the new token and reconstructs its T loops)
+and the final-loop control (L = 1: every loop's query attends the last
+loop's K/V; each step appends the new token's final-loop K/V).  When the
+cache does not fit in HBM the line says so (value null) instead.
 """
 from __future__ import annotations
 
@@ -47,6 +55,11 @@ def parse():
     ap.add_argument("--steps", type=int, default=5)
     ap.add_argument("--warmup", type=int, default=2)
     ap.add_argument("--workload", default="extreme_batch_b768_ctx4k")
+    ap.add_argument("--path", choices=("lla", "fast", "final_loop"), default="lla",
+                    help="lla: the latent store (default); fast: reconstructed full K/V cache; "
+                         "final_loop: the final-loop-reuse control")
+    ap.add_argument("--batch", type=int, default=0,
+                    help="sequences (0 = the workload's own batch)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="budget of the oracle timing sample (0 disables it)")
     ap.add_argument("--splits", type=int, default=0,
@@ -80,26 +93,35 @@ def algorithmic_bytes(w, pos_plus_one: int) -> int:
     return store + q_out + codec
 
 
-def kernel_source(w) -> str:
+def kv_algorithmic_bytes(w, pos_plus_one: int) -> int:
+    """Bytes one flash-decode call over an uncompressed cache must move: the
+    K and V rows of slots 0..pos of every head and sequence, q and out."""
+    return w.B * pos_plus_one * w.H * 2 * w.d * w.elt_bytes + 2 * w.B * w.H * w.d * 4
+
+
+def kernel_source(w, path="lla") -> str:
+    if path != "lla":
+        return os.path.join(CSRC, "kvcache.hip")
     return os.path.join(CSRC, "decode2d_mfma.hip" if w.variant == "2d" else "decode_mfma.hip")
 
 
-def traffic_file(w) -> str:
-    return os.path.join(ROOT, "profiles", f"traffic_{w.name}.json")
+def traffic_file(w, path="lla") -> str:
+    tag = "" if path == "lla" else f"{path}_"
+    return os.path.join(ROOT, "profiles", f"traffic_{tag}{w.name}.json")
 
 
-def kernel_sha(w) -> str:
-    return hashlib.sha256(open(kernel_source(w), "rb").read()).hexdigest()
+def kernel_sha(w, path="lla") -> str:
+    return hashlib.sha256(open(kernel_source(w, path), "rb").read()).hexdigest()
 
 
-def traffic_for_current_kernel(w):
+def traffic_for_current_kernel(w, path="lla"):
     """HBM bytes per launch of the decode split kernel from the committed
-    rocprofv3 counter summary, or None when absent or taken on a different
-    kernel source."""
+    rocprofv3 counter summary, or None when absent, taken on a different
+    kernel source or at another batch."""
     try:
-        with open(traffic_file(w)) as f:
+        with open(traffic_file(w, path)) as f:
             t = json.load(f)
-        if t.get("kernel_sha256") != kernel_sha(w):
+        if t.get("kernel_sha256") != kernel_sha(w, path) or t.get("batch", w.B) != w.B:
             return None
         return t.get("hbm_bytes_per_launch")
     except (OSError, ValueError):
@@ -112,7 +134,7 @@ def algorithmic_flops(w, pos_plus_one: int) -> int:
     return 2 * w.B * pos_plus_one * w.H * w.d * w.r_k
 
 
-def summarize_counters(w, fetch_dir: str, write_dir: str) -> dict:
+def summarize_counters(w, fetch_dir: str, write_dir: str, path: str = "lla") -> dict:
     """Per-launch HBM bytes of the decode split kernel from two rocprofv3
     --pmc runs (FETCH_SIZE, then WRITE_SIZE, in KiB per dispatch), scaled by
     the copy-kernel calibration; written to profiles/traffic_<workload>.json."""
@@ -132,13 +154,14 @@ def summarize_counters(w, fetch_dir: str, write_dir: str) -> dict:
     fetch, nf = per_dispatch(fetch_dir, "FETCH_SIZE")
     write, nw = per_dispatch(write_dir, "WRITE_SIZE")
     hbm = fetch * 1024 * FETCH_SCALE + write * 1024 * WRITE_SCALE
-    res = {"workload": w.name, "kernel_source": os.path.relpath(kernel_source(w), ROOT),
-           "kernel_sha256": kernel_sha(w), "fetch_kib_per_dispatch": round(fetch, 1),
+    algo = algorithmic_bytes(w, w.N) if path == "lla" else kv_algorithmic_bytes(w, w.N)
+    res = {"workload": w.name, "path": path, "batch": w.B,
+           "kernel_source": os.path.relpath(kernel_source(w, path), ROOT),
+           "kernel_sha256": kernel_sha(w, path), "fetch_kib_per_dispatch": round(fetch, 1),
            "write_kib_per_dispatch": round(write, 1), "dispatches": [nf, nw],
            "fetch_scale": FETCH_SCALE, "write_scale": WRITE_SCALE,
-           "hbm_bytes_per_launch": int(hbm),
-           "algorithmic_bytes_per_launch": algorithmic_bytes(w, w.N)}
-    with open(traffic_file(w), "w") as f:
+           "hbm_bytes_per_launch": int(hbm), "algorithmic_bytes_per_launch": algo}
+    with open(traffic_file(w, path), "w") as f:
         json.dump(res, f, indent=1)
     return res
 
@@ -176,6 +199,254 @@ def cpu_baseline(w, codec, budget_s: float):
                       f"{w.D * w.T} calls per step"}
 
 
+def memory_summary(bytes_total: int, batch: int, hbm_bytes: int) -> dict:
+    """Footprint of the cache or store and how many sequences of this
+    shape fit in the GPU's memory."""
+    per_seq = bytes_total // batch
+    return {"bytes": bytes_total, "per_sequence_bytes": per_seq, "hbm_bytes": hbm_bytes,
+            "max_batch_in_hbm": int(hbm_bytes // per_seq)}
+
+
+def cpu_baseline_kv(w, budget_s: float):
+    """Oracle flash-decode (decode_cache) of one (layer, loop) call, one
+    sequence at a time on seeded slabs of the cache's shape, until the time
+    budget is spent; scaled to tokens/s of the whole step."""
+    from threadpoolctl import threadpool_info
+
+    from oracle import lla_oracle as O
+    from synth import gen
+    calls = w.D * w.T
+    done, spent = 0, 0.0
+    while spent < budget_s and done < w.B:
+        slab = gen.normal(w.seed, 7000 + done % 4, (w.N, w.H, 2, w.d))
+        q = gen.normal(w.seed, 7100 + done % 4, (w.H, w.d))
+        t0 = time.perf_counter()
+        for h in range(w.H):
+            O.decode_cache(slab[:, h, 0], slab[:, h, 1], q[h], w.N - 1)
+        spent += time.perf_counter() - t0
+        done += 1
+    t_step = spent / done * w.B * calls
+    threads = max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
+    return {"value": w.B / t_step, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "sample": f"{done} sequence(s) x {w.H} heads of one flash-decode call at pos "
+                      f"{w.N - 1}, {spent:.1f} s; scaled x{w.B}/{done} sequences x {calls} "
+                      f"calls per step"}
+
+
+def run_kv_path(args, w, torch, L, dev):
+    """The serving fast path or the final-loop control on workload w."""
+    from synth import gen
+    from synth.device import fill_hash_normal
+    from synth.workloads import TID_Q, TID_X_K, TID_X_V, Codec, store_key
+
+    fast = args.path == "fast"
+    metric = ("fast-path decode tokens/s (latents reconstructed into a full K/V cache, "
+              "flash-decode)" if fast else
+              "final-loop-control decode tokens/s (last loop's K/V cached, reused by every loop)")
+    cache = L.KvCache(w.dtype, batch=w.B, layers=w.D, loops=w.T if fast else 1, max_ctx=w.N,
+                      heads=w.H, d_head=w.d)
+    sdesc = L.LatentStore(w.variant, w.dtype, batch=w.B, layers=w.D, max_ctx=w.N, heads=w.H,
+                          d_head=w.d, loops=w.T, r_k=w.r_k, r_v=w.r_v)
+    cache_bytes = L.lla_kv_cache_bytes(cache)
+    need = cache_bytes + (L.lla_store_bytes(sdesc) if fast else 0)
+    free, hbm = torch.cuda.mem_get_info(dev)
+    config = {"workload": w.name, "path": args.path, "variant": w.variant, "B": w.B,
+              "layers": w.D, "ctx": w.N, "heads": w.H, "d_head": w.d, "loops": w.T,
+              "cache_loops": cache.loops, "calls_per_step": w.D * w.T}
+    res = {"metric": metric, "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
+           "warmup": args.warmup, "higher_is_better": True, "scaling": "weak",
+           "vs_baseline": None, "dtype": "bf16" if w.dtype == "bf16" else "f32",
+           "data": "synthetic", "config": config,
+           "memory": memory_summary(cache_bytes, w.B, hbm)}
+    log(f"[bench] {args.path} path, workload {w.name} B={w.B}: cache {cache_bytes / 1e9:.2f} GB "
+        f"(+ latent store {L.lla_store_bytes(sdesc) / 1e9:.2f} GB)" if fast else
+        f"[bench] {args.path} path, workload {w.name} B={w.B}: cache {cache_bytes / 1e9:.2f} GB")
+    if need > free - (4 << 30):
+        log(f"[bench] does not fit: {need / 1e9:.1f} GB needed, {free / 1e9:.1f} GB free")
+        res.update({"value": None, "ms_per_step": None, "roofline": None, "cpu_baseline": None,
+                    "oom": {"bytes_needed": need, "bytes_free": free}})
+        print(json.dumps(res), flush=True)
+        return
+
+    cache.tensor = torch.empty(cache.shape, dtype=cache.torch_dtype, device=dev)
+    rope = L.lla_kv_rope_table_fill(cache).to(dev)
+    tdt = cache.torch_dtype
+    is2d = w.variant == "2d"
+    q = torch.empty((w.D, w.T, w.B, w.H, w.d), dtype=torch.float32, device=dev)
+    fill_hash_normal(q, gen.stream_key(w.seed, TID_Q))
+    pos = torch.full((w.B,), w.N - 1, dtype=torch.int32, device=dev)
+    start = torch.full((w.B,), w.N - w.n_new, dtype=torch.int32, device=dev)
+    out = torch.empty((w.B, w.H, w.d), dtype=torch.float32, device=dev)
+    ws = L.kv_workspace(cache, args.splits)
+    stream = torch.cuda.current_stream()
+
+    def up(x, dtype):
+        x32 = np.asarray(x, np.float32)
+        if dtype == torch.float32:
+            return torch.from_numpy(x32).to(dev)
+        return torch.from_numpy(gen.f32_to_bf16_bits(x32).view(np.int16)).to(dev).view(tdt)
+
+    fill_stats = None
+    if fast:
+        store = L.LatentStore(w.variant, w.dtype, batch=w.B, layers=w.D, max_ctx=w.N,
+                              heads=w.H, d_head=w.d, loops=w.T, r_k=w.r_k, r_v=w.r_v,
+                              device=dev)
+        fill_hash_normal(store.tensor, store_key(w))
+        codec = Codec(w)
+        wk, wv, mk, mv, wdk, wdv, muk, muv = {}, {}, {}, {}, [], [], [], []
+        for l in range(w.D):
+            for t in range(w.T):
+                a, b_ = codec.w_up("k", l, t), codec.w_up("v", l, t)
+                wk[l, t] = up(a.reshape(-1, w.r_k) if is2d else a, tdt)
+                wv[l, t] = up(b_.reshape(-1, w.r_v) if is2d else b_, tdt)
+                m1 = codec.mu("k", l)[:, t * w.width:(t + 1) * w.width]
+                m2 = codec.mu("v", l)[:, t * w.width:(t + 1) * w.width]
+                mk[l, t] = up(m1.reshape(-1) if is2d else m1, torch.float32)
+                mv[l, t] = up(m2.reshape(-1) if is2d else m2, torch.float32)
+            wdk.append(up(codec.w_down("k", l)[0] if is2d else codec.w_down("k", l), tdt))
+            wdv.append(up(codec.w_down("v", l)[0] if is2d else codec.w_down("v", l), tdt))
+            muk.append(up(codec.mu("k", l)[0] if is2d else codec.mu("k", l), torch.float32))
+            muv.append(up(codec.mu("v", l)[0] if is2d else codec.mu("v", l), torch.float32))
+        K = w.T * w.width
+        xshape = (w.D, w.B, w.n_new, K) if is2d else (w.D, w.B, w.n_new, w.H, K)
+        xk = torch.empty(xshape, dtype=tdt, device=dev)
+        xv = torch.empty(xshape, dtype=tdt, device=dev)
+        fill_hash_normal(xk, gen.stream_key(w.seed, TID_X_K))
+        fill_hash_normal(xv, gen.stream_key(w.seed, TID_X_V))
+        encode = L.lla2d_encode_append if is2d else L.lla_encode_append
+        # prefill: every layer's and loop's K/V reconstructed from the latents once
+        torch.cuda.synchronize()
+        fe = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+        fe[0].record(stream)
+        for l in range(w.D):
+            for t in range(w.T):
+                L.lla_kv_fill_from_store(store, l, wk[l, t], wv[l, t], mk[l, t], mv[l, t], 0, w.N,
+                                         rope, cache, t)
+        fe[1].record(stream)
+        torch.cuda.synchronize()
+        fill_ms = fe[0].elapsed_time(fe[1]) / (w.D * w.T)
+        per_fill = cache_bytes // (w.D * w.T)
+        lat_read = L.lla_store_bytes(store) // w.D
+        fill_stats = {"kernel": "kv_fill_mfma (one lla_kv_fill_from_store call, all slots)",
+                      "launch_us": round(fill_ms * 1e3, 2), "bytes_written": per_fill,
+                      "bytes_read": lat_read,
+                      "GBps": round((per_fill + lat_read) / (fill_ms / 1e3) / 1e9, 1)}
+        log(f"[bench] reconstruct-to-cache: {fill_ms * 1e3:.1f} us per (layer, loop) fill, "
+            f"{fill_stats['GBps']} GB/s")
+    else:
+        fill_hash_normal(cache.tensor, gen.stream_key(w.seed, 50))
+        kv_new = torch.empty((2, w.D, w.B, w.n_new, w.H, w.d), dtype=torch.float32, device=dev)
+        fill_hash_normal(kv_new, gen.stream_key(w.seed, 51))
+    torch.cuda.synchronize()
+    log(f"[bench] splits={args.splits or L.lla_kv_decode_auto_splits(cache)}")
+
+    def step(timer=None):
+        for t in range(w.T):
+            for l in range(w.D):
+                if timer is not None:
+                    timer.start(stream)
+                L.lla_kv_decode_attn(cache, l, t if fast else 0, q[l, t], pos, rope, out, ws,
+                                     n_splits=args.splits)
+                if timer is not None:
+                    timer.stop(stream)
+        for l in range(w.D):
+            if fast:
+                encode(store, l, xk[l], xv[l], muk[l], muv[l], wdk[l], wdv[l], start)
+                for t in range(w.T):
+                    L.lla_kv_fill_from_store(store, l, wk[l, t], wv[l, t], mk[l, t], mv[l, t],
+                                             w.N - w.n_new, w.n_new, rope, cache, t)
+            else:
+                L.lla_kv_append(cache, l, 0, kv_new[0, l], kv_new[1, l], start, rope)
+
+    ms_eager, ms_step, call_ms = time_step(args, step, stream, torch, w.D * w.T)
+    bytes_call = kv_algorithmic_bytes(w, w.N)
+    achieved = bytes_call / (call_ms.mean() / 1e3) / 1e9
+    res.update({
+        "value": round(w.B / (ms_step / 1e3), 2), "ms_per_step": round(ms_step, 4),
+        "ms_per_step_eager": round(ms_eager, 4),
+        "launch": "eager" if args.eager else "hip_graph_replay",
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "traffic": traffic_for_current_kernel(w, args.path),
+                     "kernel": "kv_split (+ kv_merge) (one lla_kv_decode_attn call)",
+                     "bytes_per_launch": bytes_call,
+                     "launch_us": round(call_ms.mean() * 1e3, 2)}})
+    config["splits"] = args.splits or L.lla_kv_decode_auto_splits(cache)
+    if fill_stats:
+        res["reconstruct_to_cache"] = fill_stats
+    res["cpu_baseline"] = cpu_baseline_kv(w, args.cpu_seconds) if args.cpu_seconds > 0 else None
+    print(json.dumps(res), flush=True)
+
+
+class CallTimer:
+    """HIP events around every decode call of a pass, created up front (the
+    first creation of a timing event can stall the host for milliseconds)."""
+
+    def __init__(self, torch, n: int):
+        self.ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                   for _ in range(n)]
+        self.i = 0
+
+    def start(self, stream):
+        self.ev[self.i][0].record(stream)
+
+    def stop(self, stream):
+        self.ev[self.i][1].record(stream)
+        self.i += 1
+
+    def ms(self):
+        return np.array([a.elapsed_time(b) for a, b in self.ev[:self.i]])
+
+
+def time_step(args, step, stream, torch, calls_per_step: int):
+    """Warm-up; a plain eager pass (ms/step as launched from the host); a
+    pass with events around every decode call, queued behind a spin kernel
+    so that the GPU never waits for the host inside it (the events then
+    bracket the kernels alone); then, unless --eager, the step captured as a
+    HIP graph and replayed.  Returns (eager ms/step, reported ms/step,
+    per-call ms array)."""
+    for i in range(args.warmup):
+        step()
+        torch.cuda.synchronize()
+        log(f"[bench] warmup step {i + 1}/{args.warmup} done")
+
+    def timed(run):
+        torch.cuda.synchronize()
+        t_start = torch.cuda.Event(enable_timing=True)
+        t_end = torch.cuda.Event(enable_timing=True)
+        t_start.record(stream)
+        for _ in range(args.steps):
+            run()
+        t_end.record(stream)
+        torch.cuda.synchronize()
+        return t_start.elapsed_time(t_end) / args.steps
+
+    ms_eager = timed(step)
+    timer = CallTimer(torch, calls_per_step * args.steps)
+    torch.cuda.synchronize()
+    try:  # hold the queue for longer than the host needs to enqueue the pass
+        torch.cuda._sleep(int(3e6 * (2.0 * ms_eager * args.steps + 20.0)))
+    except (AttributeError, RuntimeError):
+        pass
+    for _ in range(args.steps):
+        step(timer)
+    torch.cuda.synchronize()
+    call_ms = timer.ms()
+    log(f"[bench] {args.steps} eager steps: {ms_eager:.3f} ms/step; decode call mean "
+        f"{call_ms.mean() * 1e3:.1f} us (min {call_ms.min() * 1e3:.1f}, "
+        f"max {call_ms.max() * 1e3:.1f})")
+    ms_step = ms_eager
+    if not args.eager:
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            step()
+        graph.replay()
+        torch.cuda.synchronize()
+        ms_step = timed(graph.replay)
+        log(f"[bench] {args.steps} graph replays: {ms_step:.3f} ms/step")
+    return ms_eager, ms_step, call_ms
+
+
 def main():
     args = parse()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
@@ -185,7 +456,10 @@ def main():
 
     if args.summarize_counters:
         from synth.workloads import WORKLOADS
-        print(json.dumps(summarize_counters(WORKLOADS[args.workload], *args.summarize_counters)))
+        w = WORKLOADS[args.workload]
+        if args.batch:
+            w = w.scaled(B=args.batch)
+        print(json.dumps(summarize_counters(w, *args.summarize_counters, args.path)))
         return
 
     import torch
@@ -213,8 +487,13 @@ def main():
     from synth.workloads import TID_Q, TID_X_K, TID_X_V, WORKLOADS, Codec, store_key
 
     w = WORKLOADS[args.workload]
+    if args.batch:
+        w = w.scaled(B=args.batch)
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+    if args.path != "lla":
+        run_kv_path(args, w, torch, L, dev)
+        return
     log(f"[bench] workload {w.name}: B={w.B} D={w.D} N={w.N} H={w.H} d={w.d} T={w.T} "
         f"r_k={w.r_k} r_v={w.r_v} {w.variant} {w.dtype}; store {w.store_bytes / 1e9:.2f} GB")
 
@@ -281,12 +560,11 @@ def main():
     log(f"[bench] path={L.lla_decode_path(store)} "
         f"splits={args.splits or L.lla_decode_auto_splits(store)}")
 
-    def step(events=None):
+    def step(timer=None):
         for t in range(w.T):
             for l in range(w.D):
-                if events is not None:
-                    events[0].append(torch.cuda.Event(enable_timing=True))
-                    events[0][-1].record(stream)
+                if timer is not None:
+                    timer.start(stream)
                 if args.inflight:
                     L.lla_decode_attn_inflight(store, l, t, qi[l, t], kvi[0, l, t], kvi[1, l, t],
                                                wk[l, t], wv[l, t], mk[l, t], mv[l, t], pos0,
@@ -294,49 +572,13 @@ def main():
                 else:
                     decode(store, l, t, q[l, t], wk[l, t], wv[l, t], mk[l, t], mv[l, t], pos,
                            rope, out, ws, n_splits=args.splits)
-                if events is not None:
-                    events[1].append(torch.cuda.Event(enable_timing=True))
-                    events[1][-1].record(stream)
+                if timer is not None:
+                    timer.stop(stream)
         if not args.no_encode:
             for l in range(w.D):
                 encode(store, l, xk[l], xv[l], muk[l], muv[l], wdk[l], wdv[l], start)
 
-    for i in range(args.warmup):
-        step()
-        torch.cuda.synchronize()
-        log(f"[bench] warmup step {i + 1}/{args.warmup} done")
-
-    def timed(run):
-        torch.cuda.synchronize()
-        t_start = torch.cuda.Event(enable_timing=True)
-        t_end = torch.cuda.Event(enable_timing=True)
-        t_start.record(stream)
-        for _ in range(args.steps):
-            run()
-        t_end.record(stream)
-        torch.cuda.synchronize()
-        return t_start.elapsed_time(t_end) / args.steps
-
-    # Eager pass: every call launched from the host, a pair of events around
-    # each decode call (its duration feeds the roofline).
-    ev = ([], [])
-    ms_eager = timed(lambda: step(ev))
-    call_ms = np.array([a.elapsed_time(b) for a, b in zip(*ev)])
-    log(f"[bench] {args.steps} eager steps: {ms_eager:.3f} ms/step; decode call mean "
-        f"{call_ms.mean() * 1e3:.1f} us (min {call_ms.min() * 1e3:.1f}, "
-        f"max {call_ms.max() * 1e3:.1f})")
-    # Graph pass: the same step captured once as a HIP graph and replayed, so
-    # that host launch overhead (ctypes marshalling of 100+ calls) does not
-    # leave the GPU idle between short calls.  This is the step time reported.
-    ms_step = ms_eager
-    if not args.eager:
-        graph = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(graph):
-            step()
-        graph.replay()
-        torch.cuda.synchronize()
-        ms_step = timed(graph.replay)
-        log(f"[bench] {args.steps} graph replays: {ms_step:.3f} ms/step")
+    ms_eager, ms_step, call_ms = time_step(args, step, stream, torch, w.D * w.T)
     value = w.B * nq / (ms_step / 1e3)   # generated tokens per second, all sequences
     bytes_call = algorithmic_bytes(w, w.N)
     if args.inflight:
@@ -382,6 +624,8 @@ def main():
                    "splits": args.splits or L.lla_decode_auto_splits(store),
                    "path": path},
         "roofline": roofline,
+        "memory": memory_summary(L.lla_store_bytes(store), w.B,
+                                 torch.cuda.mem_get_info(dev)[1]),
     }
     if args.cpu_seconds > 0:
         del store, q, xk, xv

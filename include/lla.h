@@ -222,6 +222,89 @@ lla_status_t lla_decode_attn_inflight(const lla_store_t *store, int32_t layer, i
  * for an invalid descriptor.  Host-only. */
 const char *lla_decode_path(const lla_store_t *store);
 
+/* ===========================================================================
+ * Uncompressed K/V cache: the two comparison paths the paper sets against
+ * the latent store.
+ *  - The serving "fast path" (technical summary, "Serving Capacity"):
+ *    reconstruct every loop's K/V from the latents once, cache them in full
+ *    and decode with plain flash attention.  It keeps the reconstruction off
+ *    the decode path but gives up the memory saving (cache loops L = T).
+ *  - The final-loop-reuse control (paper Sec. 3, matched-axis baselines):
+ *    cache only the last loop's K/V (L = 1) and let every loop's query
+ *    attend to it; at T = 4 its footprint equals that of a 4x latent store.
+ *
+ * Cache layout (element type = cache->dtype):
+ *     cache[b][layer][l][slot][h][0 = K | 1 = V][i],  shape [B, D, L, N, H, 2, d]
+ * row-major.  Keys are stored after RoPE at their slot's position (the
+ * same rotate-half convention as the latent path); values as they are.
+ * The RoPE table of lla_kv_rope_table_fill() (or that of a latent store
+ * with the same max_ctx, d_head and rope_base) serves every call.
+ * ========================================================================= */
+typedef struct {
+  int32_t dtype;     /* lla_dtype_t of K and V                               */
+  int32_t batch;     /* B sequences                                          */
+  int32_t layers;    /* D layers                                             */
+  int32_t loops;     /* L cached loops per layer (T: fast path; 1: control)  */
+  int32_t max_ctx;   /* N slots                                              */
+  int32_t heads;     /* H                                                    */
+  int32_t d_head;    /* d, even                                              */
+  float rope_base;   /* RoPE base                                            */
+  void *data;        /* device: lla_kv_cache_bytes() bytes, caller-owned     */
+} lla_kv_cache_t;
+
+/* LLA_OK or the first error found in the descriptor (not its data). */
+lla_status_t lla_kv_cache_check(const lla_kv_cache_t *cache);
+
+/* B*D*L*N*H*2*d*sizeof(dtype); 0 for an invalid descriptor or on overflow. */
+size_t lla_kv_cache_bytes(const lla_kv_cache_t *cache);
+
+/* RoPE table for the cache's (N, d, base); same contract as
+ * lla_rope_table_bytes / lla_rope_table_fill. */
+size_t lla_kv_rope_table_bytes(const lla_kv_cache_t *cache);
+lla_status_t lla_kv_rope_table_fill(const lla_kv_cache_t *cache, void *host_table, size_t bytes);
+
+/* Reconstruct-to-cache (the fast path's fill): for every sequence b, head h
+ * and slot j in [slot0, slot0 + n_slots) with j < N,
+ *   cache[b][layer][cache_loop][j][h][K] = RoPE(c_k,j W_up,k,t^T + mu_k,t, j)
+ *   cache[b][layer][cache_loop][j][h][V] = c_v,j W_up,v,t^T + mu_v,t
+ * (paper Sec. 3 Eq. 3, "RoPE and reconstruction"), rounded once to the
+ * cache type.  c is read from store[b][layer][j] (per-head: head h's latent;
+ * LLA-2D: the token's one latent).  w_up_*_t and mu_*_t are laid out exactly
+ * as for lla_decode_attn (per-head [H, d, r]; LLA-2D [H*d, r] -- the same
+ * memory order).  The store and the cache must agree on dtype, batch, layers,
+ * max_ctx, heads and d_head; 0 <= cache_loop < cache->loops.  n_slots == 0
+ * is a no-op.  The caller names the loop t only through w_up_*_t and mu_*_t.
+ * ------------------------------------------------------------------------- */
+lla_status_t lla_kv_fill_from_store(const lla_store_t *store, int32_t layer,
+                                    const void *w_up_k_t, const void *w_up_v_t,
+                                    const float *mu_k_t, const float *mu_v_t,
+                                    int32_t slot0, int32_t n_slots, const void *rope_table,
+                                    const lla_kv_cache_t *cache, int32_t cache_loop,
+                                    hipStream_t stream);
+
+/* Append raw K/V (e.g. the final loop's, for the control): for j < n_new,
+ *   cache[b][layer][cache_loop][start_pos[b] + j][h] = (RoPE(k[b][j][h], that slot), v[b][j][h])
+ * rounded to the cache type; slots outside [0, N) are not written.
+ *   k, v        device, float32, [B, n_new, H, d] (pre-RoPE)
+ *   start_pos   device, int32, [B] */
+lla_status_t lla_kv_append(const lla_kv_cache_t *cache, int32_t layer, int32_t cache_loop,
+                           const float *k, const float *v, const int32_t *start_pos,
+                           int32_t n_new, const void *rope_table, hipStream_t stream);
+
+/* Flash-decode over the cache: for every sequence b and head h,
+ *   out[b][h] = sum_{j <= pos[b]} softmax_j(scale * RoPE(q[b][h], pos[b]) . K_j) V_j
+ * with K_j, V_j = cache[b][layer][cache_loop][j][h].  The fast path calls it
+ * with cache_loop = t (the loop of q); the final-loop control with 0 for
+ * every loop.  q [B, H, d] fp32 pre-RoPE; pos [B] clamped into [0, N-1];
+ * out [B, H, d] fp32; softmax_scale as lla_decode_attn; workspace >=
+ * lla_kv_decode_workspace_bytes(cache, n_splits) (n_splits 0 = automatic). */
+size_t lla_kv_decode_workspace_bytes(const lla_kv_cache_t *cache, int32_t n_splits);
+int32_t lla_kv_decode_auto_splits(const lla_kv_cache_t *cache);
+lla_status_t lla_kv_decode_attn(const lla_kv_cache_t *cache, int32_t layer, int32_t cache_loop,
+                                const float *q, const int32_t *pos, const void *rope_table,
+                                float softmax_scale, float *out, void *workspace,
+                                size_t ws_bytes, int32_t n_splits, hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

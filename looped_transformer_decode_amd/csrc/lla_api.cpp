@@ -222,6 +222,78 @@ lla_status_t encode_impl(const lla_store_t *st, int32_t want_variant, int32_t la
   return he == hipSuccess ? LLA_OK : LLA_E_HIP;
 }
 
+
+// The RoPE table for (N, d, base), layout lla::RopeLayout.
+lla_status_t fill_rope_table(int32_t N, int32_t d, float rope_base, void *host_table,
+                             size_t bytes) {
+  if (!host_table) return LLA_E_NULL;
+  const lla::RopeLayout L = lla::rope_layout(N, d);
+  if (bytes < L.total) return LLA_E_WORKSPACE;
+  const int32_t half = d / 2;
+  const double base = (double)rope_base;
+  float *f = reinterpret_cast<float *>(host_table);
+  for (int32_t j = 0; j < N; ++j)
+    for (int32_t i = 0; i < half; ++i) {
+      const double ang = (double)j * std::pow(base, -2.0 * i / d);
+      f[((size_t)j * half + i) * 2] = (float)std::cos(ang);
+      f[((size_t)j * half + i) * 2 + 1] = (float)std::sin(ang);
+    }
+  std::memset(reinterpret_cast<char *>(host_table) + L.f32_bytes, 0, L.bf16_off - L.f32_bytes);
+  if (L.bf16_bytes) {
+    uint16_t *h = reinterpret_cast<uint16_t *>(reinterpret_cast<char *>(host_table) + L.bf16_off);
+    const int32_t ksteps = d / 16, tiles = (N + 31) / 32;
+    for (int32_t t = 0; t < tiles; ++t)
+      for (int32_t st = 0; st < ksteps; ++st)
+        for (int32_t lane = 0; lane < 64; ++lane)
+          for (int32_t e8 = 0; e8 < 8; ++e8) {
+            const int32_t j = 32 * t + lane % 32;
+            const int32_t i = 16 * st + 8 * (lane / 32) + e8;
+            const int32_t ii = i < half ? i : i - half;
+            const double ang = (double)j * std::pow(base, -2.0 * ii / d);
+            const double v = i < half ? std::cos(ang) : std::sin(ang);
+            h[(((size_t)t * ksteps + st) * 64 + lane) * 8 + e8] = f64_to_bf16(v);
+          }
+  }
+  return LLA_OK;
+}
+
+// ---- uncompressed K/V cache -------------------------------------------------
+size_t kv_elems(const lla_kv_cache_t *c) {
+  size_t n = 1;
+  const size_t dims[7] = {(size_t)c->batch, (size_t)c->layers, (size_t)c->loops,
+                          (size_t)c->max_ctx, (size_t)c->heads, 2, (size_t)c->d_head};
+  for (size_t v : dims)
+    if (!mul_ok(n, v, &n)) return 0;
+  return n;
+}
+
+int32_t kv_auto_splits(const lla_kv_cache_t *c) {
+  // about four workgroups per CU, each split at least 128 slots long
+  const int32_t hg = lla::kv_heads_per_group(c->d_head, c->dtype);
+  const int64_t per_split = (int64_t)c->batch * ((c->heads + hg - 1) / hg);
+  int64_t S = (1024 + per_split - 1) / per_split;
+  const int64_t max_s = std::max<int64_t>(1, c->max_ctx / 128);
+  if (S > max_s) S = max_s;
+  if (S < 1) S = 1;
+  return (int32_t)S;
+}
+
+lla::KvParams kv_params(const lla_kv_cache_t *c, int32_t layer, int32_t cache_loop,
+                        const void *rope) {
+  lla::KvParams p{};
+  p.cache = c->data;
+  p.B = c->batch;
+  p.D = c->layers;
+  p.L = c->loops;
+  p.N = c->max_ctx;
+  p.H = c->heads;
+  p.d = c->d_head;
+  p.layer = layer;
+  p.cache_loop = cache_loop;
+  p.rope_f32 = reinterpret_cast<const float *>(rope);
+  return p;
+}
+
 }  // namespace
 
 extern "C" {
@@ -293,35 +365,7 @@ size_t lla_rope_table_bytes(const lla_store_t *s) {
 lla_status_t lla_rope_table_fill(const lla_store_t *s, void *host_table, size_t bytes) {
   const lla_status_t e = lla_store_check(s);
   if (e != LLA_OK) return e;
-  if (!host_table) return LLA_E_NULL;
-  const lla::RopeLayout L = lla::rope_layout(s->max_ctx, s->d_head);
-  if (bytes < L.total) return LLA_E_WORKSPACE;
-  const int32_t d = s->d_head, half = d / 2, N = s->max_ctx;
-  const double base = (double)s->rope_base;
-  float *f = reinterpret_cast<float *>(host_table);
-  for (int32_t j = 0; j < N; ++j)
-    for (int32_t i = 0; i < half; ++i) {
-      const double ang = (double)j * std::pow(base, -2.0 * i / d);
-      f[((size_t)j * half + i) * 2] = (float)std::cos(ang);
-      f[((size_t)j * half + i) * 2 + 1] = (float)std::sin(ang);
-    }
-  std::memset(reinterpret_cast<char *>(host_table) + L.f32_bytes, 0, L.bf16_off - L.f32_bytes);
-  if (L.bf16_bytes) {
-    uint16_t *h = reinterpret_cast<uint16_t *>(reinterpret_cast<char *>(host_table) + L.bf16_off);
-    const int32_t ksteps = d / 16, tiles = (N + 31) / 32;
-    for (int32_t t = 0; t < tiles; ++t)
-      for (int32_t st = 0; st < ksteps; ++st)
-        for (int32_t lane = 0; lane < 64; ++lane)
-          for (int32_t e8 = 0; e8 < 8; ++e8) {
-            const int32_t j = 32 * t + lane % 32;
-            const int32_t i = 16 * st + 8 * (lane / 32) + e8;
-            const int32_t ii = i < half ? i : i - half;
-            const double ang = (double)j * std::pow(base, -2.0 * ii / d);
-            const double v = i < half ? std::cos(ang) : std::sin(ang);
-            h[(((size_t)t * ksteps + st) * 64 + lane) * 8 + e8] = f64_to_bf16(v);
-          }
-  }
-  return LLA_OK;
+  return fill_rope_table(s->max_ctx, s->d_head, s->rope_base, host_table, bytes);
 }
 
 lla_status_t lla_encode_append(const lla_store_t *store, int32_t layer, const void *x_k,
@@ -399,6 +443,139 @@ lla_status_t lla_decode_attn_inflight(const lla_store_t *store, int32_t layer, i
 const char *lla_decode_path(const lla_store_t *s) {
   if (lla_store_check(s) != LLA_OK) return nullptr;
   return use_mfma(s) ? "mfma" : "valu";
+}
+
+lla_status_t lla_kv_cache_check(const lla_kv_cache_t *c) {
+  if (!c) return LLA_E_NULL;
+  if (c->dtype != LLA_DT_F32 && c->dtype != LLA_DT_BF16) return LLA_E_DTYPE;
+  if (c->batch <= 0 || c->layers <= 0 || c->loops <= 0 || c->max_ctx <= 0 || c->heads <= 0 ||
+      c->d_head <= 0 || c->d_head % 2 != 0)
+    return LLA_E_SHAPE;
+  if (!(c->rope_base > 1.0f) || std::isinf(c->rope_base)) return LLA_E_RANGE;
+  size_t bytes;
+  const size_t n = kv_elems(c);
+  if (n == 0 || !mul_ok(n, elt_size(c->dtype), &bytes) || bytes > (size_t)INT64_MAX)
+    return LLA_E_OVERFLOW;
+  return LLA_OK;
+}
+
+size_t lla_kv_cache_bytes(const lla_kv_cache_t *c) {
+  if (lla_kv_cache_check(c) != LLA_OK) return 0;
+  return kv_elems(c) * elt_size(c->dtype);
+}
+
+size_t lla_kv_rope_table_bytes(const lla_kv_cache_t *c) {
+  if (lla_kv_cache_check(c) != LLA_OK) return 0;
+  return lla::rope_layout(c->max_ctx, c->d_head).total;
+}
+
+lla_status_t lla_kv_rope_table_fill(const lla_kv_cache_t *c, void *host_table, size_t bytes) {
+  const lla_status_t e = lla_kv_cache_check(c);
+  if (e != LLA_OK) return e;
+  return fill_rope_table(c->max_ctx, c->d_head, c->rope_base, host_table, bytes);
+}
+
+lla_status_t lla_kv_fill_from_store(const lla_store_t *st, int32_t layer, const void *w_up_k_t,
+                                    const void *w_up_v_t, const float *mu_k_t,
+                                    const float *mu_v_t, int32_t slot0, int32_t n_slots,
+                                    const void *rope_table, const lla_kv_cache_t *c,
+                                    int32_t cache_loop, hipStream_t stream) {
+  lla_status_t e = lla_store_check(st);
+  if (e != LLA_OK) return e;
+  if ((e = lla_kv_cache_check(c)) != LLA_OK) return e;
+  if (st->dtype != c->dtype) return LLA_E_DTYPE;
+  if (st->batch != c->batch || st->layers != c->layers || st->max_ctx != c->max_ctx ||
+      st->heads != c->heads || st->d_head != c->d_head)
+    return LLA_E_SHAPE;
+  if (layer < 0 || layer >= st->layers || cache_loop < 0 || cache_loop >= c->loops)
+    return LLA_E_RANGE;
+  if (slot0 < 0 || n_slots < 0 || (int64_t)slot0 + n_slots > st->max_ctx) return LLA_E_RANGE;
+  if (n_slots == 0) return LLA_OK;
+  if (!st->data || !c->data || !w_up_k_t || !w_up_v_t || !mu_k_t || !mu_v_t || !rope_table)
+    return LLA_E_NULL;
+  lla::KvParams p = kv_params(c, layer, cache_loop, rope_table);
+  p.store = st->data;
+  p.Hs = store_heads(st);
+  p.rk = st->r_k;
+  p.rv = st->r_v;
+  p.R = st->r_k + st->r_v;
+  p.wk = w_up_k_t;
+  p.wv = w_up_v_t;
+  p.muk = mu_k_t;
+  p.muv = mu_v_t;
+  p.slot0 = slot0;
+  p.n = n_slots;
+  const bool mfma = st->dtype == LLA_DT_BF16 &&
+                    lla::kv_fill_mfma_supported(st->d_head, st->r_k, st->r_v) &&
+                    aligned16(st->data) && aligned16(c->data) && aligned16(w_up_k_t) &&
+                    aligned16(w_up_v_t);
+  return lla::launch_kv_fill(p, st->dtype, mfma, stream) == hipSuccess ? LLA_OK : LLA_E_HIP;
+}
+
+lla_status_t lla_kv_append(const lla_kv_cache_t *c, int32_t layer, int32_t cache_loop,
+                           const float *k, const float *v, const int32_t *start_pos,
+                           int32_t n_new, const void *rope_table, hipStream_t stream) {
+  const lla_status_t e = lla_kv_cache_check(c);
+  if (e != LLA_OK) return e;
+  if (layer < 0 || layer >= c->layers || cache_loop < 0 || cache_loop >= c->loops)
+    return LLA_E_RANGE;
+  if (n_new < 0 || n_new > c->max_ctx) return LLA_E_RANGE;
+  if (n_new == 0) return LLA_OK;
+  if (!c->data || !k || !v || !start_pos || !rope_table) return LLA_E_NULL;
+  lla::KvParams p = kv_params(c, layer, cache_loop, rope_table);
+  p.k = k;
+  p.v = v;
+  p.start = start_pos;
+  p.n = n_new;
+  return lla::launch_kv_append(p, c->dtype, stream) == hipSuccess ? LLA_OK : LLA_E_HIP;
+}
+
+size_t lla_kv_decode_workspace_bytes(const lla_kv_cache_t *c, int32_t n_splits) {
+  if (lla_kv_cache_check(c) != LLA_OK || n_splits < 0) return 0;
+  if (!lla::kv_decode_supported(c->d_head, c->dtype)) return 0;
+  const int32_t S = n_splits ? n_splits : kv_auto_splits(c);
+  size_t n = (size_t)c->batch * c->heads;
+  if (!mul_ok(n, (size_t)S, &n) || !mul_ok(n, (size_t)c->d_head + 2, &n) || !mul_ok(n, 4, &n))
+    return 0;
+  return n;
+}
+
+int32_t lla_kv_decode_auto_splits(const lla_kv_cache_t *c) {
+  if (lla_kv_cache_check(c) != LLA_OK || !lla::kv_decode_supported(c->d_head, c->dtype))
+    return 0;
+  return kv_auto_splits(c);
+}
+
+lla_status_t lla_kv_decode_attn(const lla_kv_cache_t *c, int32_t layer, int32_t cache_loop,
+                                const float *q, const int32_t *pos, const void *rope_table,
+                                float softmax_scale, float *out, void *workspace,
+                                size_t ws_bytes, int32_t n_splits, hipStream_t stream) {
+  const lla_status_t e = lla_kv_cache_check(c);
+  if (e != LLA_OK) return e;
+  if (!c->data || !q || !pos || !rope_table || !out) return LLA_E_NULL;
+  if (layer < 0 || layer >= c->layers || cache_loop < 0 || cache_loop >= c->loops)
+    return LLA_E_RANGE;
+  if (n_splits < 0 || n_splits > c->max_ctx) return LLA_E_RANGE;
+  if (std::isnan(softmax_scale) || std::isinf(softmax_scale)) return LLA_E_RANGE;
+  if (!lla::kv_decode_supported(c->d_head, c->dtype) || !aligned16(c->data))
+    return LLA_E_UNSUPPORTED;
+  const int32_t S = n_splits ? n_splits : kv_auto_splits(c);
+  const int32_t hg = lla::kv_heads_per_group(c->d_head, c->dtype);
+  if ((int64_t)c->batch * ((c->heads + hg - 1) / hg) * S > INT32_MAX) return LLA_E_OVERFLOW;
+  const size_t need = lla_kv_decode_workspace_bytes(c, S);
+  if (!workspace) return LLA_E_WORKSPACE;
+  if (need == 0 || ws_bytes < need) return LLA_E_WORKSPACE;
+  lla::KvParams p = kv_params(c, layer, cache_loop, rope_table);
+  p.q = q;
+  p.pos = pos;
+  const float sc =
+      softmax_scale > 0.f ? softmax_scale : (float)(1.0 / std::sqrt((double)c->d_head));
+  p.scale_log2 = (float)((double)sc * 1.4426950408889634);
+  p.ws = reinterpret_cast<float *>(workspace);
+  p.S = S;
+  p.split_len = (c->max_ctx + S - 1) / S;
+  p.out = out;
+  return lla::launch_kv_decode(p, c->dtype, stream) == hipSuccess ? LLA_OK : LLA_E_HIP;
 }
 
 }  // extern "C"

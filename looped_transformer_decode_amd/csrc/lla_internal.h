@@ -92,6 +92,31 @@ __host__ __device__ inline int32_t merge_heads_per_block(int32_t d, int32_t rv) 
   return h < 1 ? 1 : h;
 }
 
+// Uncompressed K/V cache [B, D, L, N, H, 2, d]: geometry and one call's
+// arguments (decode, reconstruct-to-cache or raw append).
+struct KvParams {
+  void *cache;
+  int32_t B, D, L, N, H, d;
+  int32_t layer, cache_loop;
+  const float *rope_f32;   // [N][d/2][2]
+  // decode
+  const float *q;          // [B, H, d]
+  const int32_t *pos;      // [B]
+  float scale_log2;
+  float *ws;               // partials [B, H, S, d + 2]
+  int32_t S, split_len;
+  float *out;              // [B, H, d]
+  // reconstruct-to-cache: slots [slot0, slot0 + n) of the latent store
+  const void *store;
+  int32_t Hs, rk, rv, R;
+  const void *wk, *wv;     // [H*d, rk], [H*d, rv]
+  const float *muk, *muv;  // [H*d]
+  int32_t slot0, n;
+  // raw append
+  const float *k, *v;      // [B, n, H, d]
+  const int32_t *start;    // [B]
+};
+
 // Launchers (return the launch status).  dtype is lla_dtype_t.
 hipError_t launch_decode_valu(const DecodeParams &p, int dtype, hipStream_t s);
 hipError_t launch_decode_merge(const DecodeParams &p, int dtype, hipStream_t s);
@@ -110,5 +135,11 @@ hipError_t launch_decode_mfma(const DecodeParams &p, hipStream_t s);
 hipError_t launch_encode_valu(const EncodeParams &p, int dtype, hipStream_t s);
 bool encode_mfma_supported(const EncodeParams &p, int dtype);
 hipError_t launch_encode_mfma(const EncodeParams &p, hipStream_t s);
+bool kv_decode_supported(int32_t d, int dtype);
+int32_t kv_heads_per_group(int32_t d, int dtype);
+hipError_t launch_kv_decode(const KvParams &p, int dtype, hipStream_t s);
+bool kv_fill_mfma_supported(int32_t d, int32_t rk, int32_t rv);
+hipError_t launch_kv_fill(const KvParams &p, int dtype, bool mfma, hipStream_t s);
+hipError_t launch_kv_append(const KvParams &p, int dtype, hipStream_t s);
 
 }  // namespace lla

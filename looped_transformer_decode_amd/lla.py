@@ -63,6 +63,15 @@ _SIGS = {
     "lla_decode_inflight_workspace_bytes": ([_P, _I32, _I32], _SZ),
     "lla_decode_attn_inflight": ([_P, _I32, _I32, _I32, _P, _P, _P, _P, _P, _P, _P, _P, _P, _F,
                                   _P, _P, _SZ, _I32, _P], _I32),
+    "lla_kv_cache_check": ([_P], _I32),
+    "lla_kv_cache_bytes": ([_P], _SZ),
+    "lla_kv_rope_table_bytes": ([_P], _SZ),
+    "lla_kv_rope_table_fill": ([_P, _P, _SZ], _I32),
+    "lla_kv_fill_from_store": ([_P, _I32, _P, _P, _P, _P, _I32, _I32, _P, _P, _I32, _P], _I32),
+    "lla_kv_append": ([_P, _I32, _I32, _P, _P, _P, _I32, _P, _P], _I32),
+    "lla_kv_decode_workspace_bytes": ([_P, _I32], _SZ),
+    "lla_kv_decode_auto_splits": ([_P], _I32),
+    "lla_kv_decode_attn": ([_P, _I32, _I32, _P, _P, _P, _F, _P, _P, _SZ, _I32, _P], _I32),
 }
 EXPORTS = tuple(_SIGS)
 
@@ -99,6 +108,14 @@ def _stream(stream) -> int | None:
     if stream is None:
         return torch.cuda.current_stream().cuda_stream if torch.cuda.is_available() else None
     return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+
+
+class KvCacheDesc(ctypes.Structure):
+    _fields_ = [("dtype", ctypes.c_int32), ("batch", ctypes.c_int32),
+                ("layers", ctypes.c_int32), ("loops", ctypes.c_int32),
+                ("max_ctx", ctypes.c_int32), ("heads", ctypes.c_int32),
+                ("d_head", ctypes.c_int32), ("rope_base", ctypes.c_float),
+                ("data", ctypes.c_void_p)]
 
 
 class LatentStore:
@@ -331,4 +348,130 @@ def lla_decode_attn_inflight(store, layer, loop, q, k_new, v_new, w_up_k_t, w_up
              _ptr(rope_table), float(softmax_scale), _ptr(out), _ptr(workspace),
              0 if workspace is None else workspace.numel() * workspace.element_size(), n_splits,
              _stream(stream)), "lla_decode_attn_inflight")
+    return out
+
+
+# ------------------------------------------------- uncompressed K/V cache
+class KvCache:
+    """An uncompressed K/V cache [B, D, L, N, H, 2, d] (keys stored after
+    RoPE): L = T loops for the serving fast path, 1 for the final-loop-reuse
+    control.  ``tensor`` as for LatentStore."""
+
+    def __init__(self, dtype="bf16", *, batch, layers, loops, max_ctx, heads, d_head,
+                 rope_base=10000.0, tensor=None, device=None):
+        self.dtype = _DT_NAME.get(dtype, dtype)
+        self.batch, self.layers, self.loops, self.max_ctx = batch, layers, loops, max_ctx
+        self.heads, self.d_head, self.rope_base = heads, d_head, rope_base
+        self.shape = (batch, layers, loops, max_ctx, heads, 2, d_head)
+        if tensor is None and device is not None:
+            tensor = torch.empty(self.shape, dtype=_TORCH_DT[self.dtype], device=device)
+        if tensor is not None:
+            if tuple(tensor.shape) != self.shape or not tensor.is_contiguous():
+                raise ValueError(f"cache tensor must be contiguous {self.shape}")
+            if tensor.dtype != _TORCH_DT[self.dtype]:
+                raise ValueError(f"cache tensor dtype must be {_TORCH_DT[self.dtype]}")
+        self.tensor = tensor
+
+    @property
+    def torch_dtype(self):
+        return _TORCH_DT[self.dtype]
+
+    def desc(self) -> KvCacheDesc:
+        return KvCacheDesc(self.dtype, self.batch, self.layers, self.loops, self.max_ctx,
+                           self.heads, self.d_head, self.rope_base, _ptr(self.tensor))
+
+
+def lla_kv_cache_check(cache: KvCache) -> None:
+    d = cache.desc()
+    _check(lib().lla_kv_cache_check(ctypes.byref(d)), "lla_kv_cache_check")
+
+
+def lla_kv_cache_bytes(cache: KvCache) -> int:
+    d = cache.desc()
+    return lib().lla_kv_cache_bytes(ctypes.byref(d))
+
+
+def lla_kv_rope_table_bytes(cache: KvCache) -> int:
+    d = cache.desc()
+    return lib().lla_kv_rope_table_bytes(ctypes.byref(d))
+
+
+def lla_kv_rope_table_fill(cache: KvCache) -> torch.Tensor:
+    """Host (CPU) uint8 tensor holding the cache's RoPE table."""
+    d = cache.desc()
+    n = lib().lla_kv_rope_table_bytes(ctypes.byref(d))
+    if n == 0:
+        raise LlaError(lib().lla_kv_cache_check(ctypes.byref(d)) or 2, "lla_kv_rope_table_bytes")
+    host = torch.empty(n, dtype=torch.uint8)
+    _check(lib().lla_kv_rope_table_fill(ctypes.byref(d), host.data_ptr(), n),
+           "lla_kv_rope_table_fill")
+    return host
+
+
+def lla_kv_decode_workspace_bytes(cache: KvCache, n_splits: int = 0) -> int:
+    d = cache.desc()
+    return lib().lla_kv_decode_workspace_bytes(ctypes.byref(d), n_splits)
+
+
+def lla_kv_decode_auto_splits(cache: KvCache) -> int:
+    d = cache.desc()
+    return lib().lla_kv_decode_auto_splits(ctypes.byref(d))
+
+
+def kv_workspace(cache: KvCache, n_splits: int = 0, device=None) -> torch.Tensor:
+    n = lla_kv_decode_workspace_bytes(cache, n_splits)
+    dev = device if device is not None else cache.tensor.device
+    return torch.empty(max(n, 4), dtype=torch.uint8, device=dev)
+
+
+def lla_kv_fill_from_store(store, layer, w_up_k_t, w_up_v_t, mu_k_t, mu_v_t, slot0, n_slots,
+                           rope_table, cache, cache_loop, stream=None):
+    """Reconstruct loop t (given by w_up_*_t, mu_*_t) of store slots
+    [slot0, slot0 + n_slots) into cache[:, layer, cache_loop]."""
+    s = store
+    H, d = s.heads, s.d_head
+    shp = {"k": (H, d, s.r_k), "v": (H, d, s.r_v)} if s.variant == LLA_PER_HEAD else \
+          {"k": (H * d, s.r_k), "v": (H * d, s.r_v)}
+    _need(w_up_k_t, s.torch_dtype, shp["k"], "w_up_k_t")
+    _need(w_up_v_t, s.torch_dtype, shp["v"], "w_up_v_t")
+    mshape = (H, d) if s.variant == LLA_PER_HEAD else (H * d,)
+    _need(mu_k_t, torch.float32, mshape, "mu_k_t")
+    _need(mu_v_t, torch.float32, mshape, "mu_v_t")
+    sd, cd = s.desc(), cache.desc()
+    _check(lib().lla_kv_fill_from_store(ctypes.byref(sd), layer, _ptr(w_up_k_t), _ptr(w_up_v_t),
+                                        _ptr(mu_k_t), _ptr(mu_v_t), slot0, n_slots,
+                                        _ptr(rope_table), ctypes.byref(cd), cache_loop,
+                                        _stream(stream)), "lla_kv_fill_from_store")
+
+
+def lla_kv_append(cache, layer, cache_loop, k, v, start_pos, rope_table, n_new=None,
+                  stream=None):
+    """Rotate k at its slot and write (k, v) [B, n_new, H, d] float32 into
+    cache[:, layer, cache_loop, start_pos[b] + j]."""
+    c = cache
+    if n_new is None:
+        n_new = k.shape[1]
+    _need(k, torch.float32, (c.batch, n_new, c.heads, c.d_head), "k")
+    _need(v, torch.float32, (c.batch, n_new, c.heads, c.d_head), "v")
+    _need(start_pos, torch.int32, (c.batch,), "start_pos")
+    cd = c.desc()
+    _check(lib().lla_kv_append(ctypes.byref(cd), layer, cache_loop, _ptr(k), _ptr(v),
+                               _ptr(start_pos), n_new, _ptr(rope_table), _stream(stream)),
+           "lla_kv_append")
+
+
+def lla_kv_decode_attn(cache, layer, cache_loop, q, pos, rope_table, out, workspace,
+                       softmax_scale=0.0, n_splits=0, stream=None):
+    """Flash-decode over cache[:, layer, cache_loop] for queries q [B, H, d]."""
+    c = cache
+    _need(q, torch.float32, (c.batch, c.heads, c.d_head), "q")
+    _need(pos, torch.int32, (c.batch,), "pos")
+    _need(out, torch.float32, (c.batch, c.heads, c.d_head), "out")
+    cd = c.desc()
+    _check(lib().lla_kv_decode_attn(ctypes.byref(cd), layer, cache_loop, _ptr(q), _ptr(pos),
+                                    _ptr(rope_table), float(softmax_scale), _ptr(out),
+                                    _ptr(workspace),
+                                    0 if workspace is None
+                                    else workspace.numel() * workspace.element_size(),
+                                    n_splits, _stream(stream)), "lla_kv_decode_attn")
     return out

@@ -204,3 +204,114 @@ def test_launching_calls_validate_first(fn):
         assert call(good, data=False) == 1
         assert call(good, ptrs=(P,) * 6 + (None,)) == 1
         assert call(good, ptrs=(None,) + (P,) * 6) == 1
+
+
+# ------------------------------------------------------ uncompressed K/V cache
+def kv_for(w, loops=None):
+    return L.KvCache(w.dtype, batch=w.B, layers=w.D, loops=w.T if loops is None else loops,
+                     max_ctx=w.N, heads=w.H, d_head=w.d)
+
+
+@pytest.mark.parametrize("name", sorted(WORKLOADS))
+def test_kv_cache_sizes(name):
+    """The fast path's cache is the teacher cache (all T loops, K and V);
+    the final-loop control's is 1/T of it, so at T = 4 it matches a 4x
+    latent store."""
+    w = WORKLOADS[name]
+    full = L.lla_kv_cache_bytes(kv_for(w))
+    assert full == O.teacher_cache_scalars(w.T, w.D, w.H, w.d, w.N) * w.B * w.elt_bytes
+    assert L.lla_kv_cache_bytes(kv_for(w, 1)) * w.T == full
+    assert Fraction(full, L.lla_store_bytes(store_for(w))) == L.lla_compression_ratio(
+        store_for(w))
+
+
+def test_kv_cache_extreme_batch_does_not_fit_one_gpu():
+    w = WORKLOADS["extreme_batch_b768_ctx4k"]
+    assert L.lla_kv_cache_bytes(kv_for(w)) == 2_473_901_162_496     # 2.47 TB > 288 GB
+    assert L.lla_kv_cache_bytes(kv_for(WORKLOADS["bf16_b32_ctx4k"])) == 103_079_215_104
+
+
+def test_kv_cache_invalid_descriptors():
+    base = dict(batch=2, layers=2, loops=4, max_ctx=64, heads=4, d_head=16)
+    for k in base:
+        with pytest.raises(L.LlaError) as e:
+            L.lla_kv_cache_check(L.KvCache("f32", **dict(base, **{k: 0})))
+        assert e.value.status == 2
+    with pytest.raises(L.LlaError) as e:
+        L.lla_kv_cache_check(L.KvCache("f32", **dict(base, d_head=15)))
+    assert e.value.status == 2
+    with pytest.raises(L.LlaError) as e:
+        L.lla_kv_cache_check(L.KvCache(9, **base))
+    assert e.value.status == 3
+    with pytest.raises(L.LlaError) as e:
+        L.lla_kv_cache_check(L.KvCache("f32", rope_base=0.5, **base))
+    assert e.value.status == 4
+    huge = dict(base, batch=2 ** 31 - 1, layers=2 ** 31 - 1, max_ctx=2 ** 31 - 1)
+    assert L.lla_kv_cache_bytes(L.KvCache("f32", **huge)) == 0
+
+
+def test_kv_rope_table_is_the_store_table():
+    s = L.LatentStore("per_head", "bf16", batch=1, layers=1, max_ctx=100, heads=1, d_head=128,
+                      loops=1, r_k=16, r_v=32)
+    c = L.KvCache("bf16", batch=1, layers=1, loops=1, max_ctx=100, heads=1, d_head=128)
+    assert np.array_equal(L.lla_kv_rope_table_fill(c).numpy(), L.lla_rope_table_fill(s).numpy())
+
+
+def test_kv_decode_splits_and_workspace():
+    c = kv_for(WORKLOADS["bf16_b32_ctx4k"])
+    S = L.lla_kv_decode_auto_splits(c)
+    assert 1 <= S <= 4096 // 128
+    assert L.lla_kv_decode_workspace_bytes(c, 0) == 32 * 16 * S * (128 + 2) * 4
+    assert L.lla_kv_decode_workspace_bytes(c, 3) == 32 * 16 * 3 * 130 * 4
+    odd = L.KvCache("bf16", batch=1, layers=1, loops=1, max_ctx=64, heads=2, d_head=40)
+    assert L.lla_kv_decode_auto_splits(odd) == 0          # no kernel for d = 40
+    assert L.lla_kv_decode_workspace_bytes(odd, 1) == 0
+
+
+def test_kv_calls_validate_first():
+    lib = L.lib()
+    P = 4096  # stands for a device pointer; never dereferenced
+    c = L.KvCache("bf16", batch=2, layers=3, loops=4, max_ctx=64, heads=16, d_head=128)
+    s = L.LatentStore("per_head", "bf16", batch=2, layers=3, max_ctx=64, heads=16, d_head=128,
+                      loops=4, r_k=16, r_v=32)
+
+    def dec(cache=c, layer=0, cl=0, q=P, pos=P, rope=P, out=P, ws=P, ws_bytes=1 << 30,
+            n_splits=0, scale=0.0, data=True):
+        d = cache.desc()
+        if data:
+            d.data = P
+        return lib.lla_kv_decode_attn(ctypes.byref(d), layer, cl, q, pos, rope, scale, out, ws,
+                                      ws_bytes, n_splits, None)
+    assert dec(data=False) == 1
+    assert dec(q=None) == 1 and dec(pos=None) == 1 and dec(rope=None) == 1 and dec(out=None) == 1
+    assert dec(layer=3) == 4 and dec(cl=4) == 4 and dec(cl=-1) == 4
+    assert dec(n_splits=-1) == 4 and dec(n_splits=65) == 4
+    assert dec(scale=float("nan")) == 4
+    assert dec(ws=None) == 5 and dec(ws_bytes=8) == 5
+    odd = L.KvCache("bf16", batch=2, layers=3, loops=4, max_ctx=64, heads=16, d_head=40)
+    assert dec(cache=odd) == 6
+    assert lib.lla_kv_decode_attn(None, 0, 0, P, P, P, 0.0, P, P, 1 << 30, 0, None) == 1
+
+    def fill(store=s, cache=c, layer=0, slot0=0, n=8, cl=0, ptrs=(P,) * 4, rope=P, data=True):
+        sd, cd = store.desc(), cache.desc()
+        if data:
+            sd.data, cd.data = P, P
+        return lib.lla_kv_fill_from_store(ctypes.byref(sd), layer, *ptrs, slot0, n, rope,
+                                          ctypes.byref(cd), cl, None)
+    assert fill(layer=3) == 4 and fill(cl=4) == 4
+    assert fill(slot0=-1) == 4 and fill(slot0=60, n=5) == 4 and fill(n=-1) == 4
+    assert fill(n=0) == 0                                   # empty range: a no-op
+    assert fill(data=False) == 1 and fill(ptrs=(P, P, P, None)) == 1 and fill(rope=None) == 1
+    assert fill(cache=L.KvCache("f32", batch=2, layers=3, loops=4, max_ctx=64, heads=16,
+                                d_head=128)) == 3
+    assert fill(cache=L.KvCache("bf16", batch=2, layers=3, loops=4, max_ctx=32, heads=16,
+                                d_head=128)) == 2
+
+    def app(cache=c, layer=0, cl=0, k=P, v=P, start=P, n=1, rope=P, data=True):
+        d = cache.desc()
+        if data:
+            d.data = P
+        return lib.lla_kv_append(ctypes.byref(d), layer, cl, k, v, start, n, rope, None)
+    assert app(layer=-1) == 4 and app(cl=4) == 4 and app(n=-1) == 4 and app(n=65) == 4
+    assert app(n=0) == 0
+    assert app(data=False) == 1 and app(k=None) == 1 and app(start=None) == 1
