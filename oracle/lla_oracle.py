@@ -350,3 +350,37 @@ def final_loop_control(k_last: np.ndarray, v_last: np.ndarray, q_t: np.ndarray, 
     are cached, and the query of every loop t attends to them.  q_t: [d]."""
     K, V = cache_rows(k_last, v_last, np.arange(np.asarray(k_last).shape[0]), base)
     return decode_cache(K, V, q_t, pos, scale, base)
+
+
+# --------------------------------------------------------------------------
+# SVD codec initialisation ([paper] Sec. 3, initialisation and conversion)
+# --------------------------------------------------------------------------
+def svd_init(x: np.ndarray, loops: int, width: int, r: int):
+    """Initialise one codec from calibration rows x: [n_cal, T*width] of its
+    stacked loop vectors (Eq. 1): centre by the per-loop mean (the column
+    mean of the stacked rows), take W_down as the r leading right singular
+    vectors of the centred matrix, and W_up,t as W_down's loop-t rows.
+    Singular vectors are defined up to sign; each column is signed so that
+    its entry of largest magnitude is positive (a named choice, mirrored by
+    the kernels).  Returns (mu [K], W_down [K, r], [W_up,t [width, r]],
+    sigma [r])."""
+    X = np.asarray(x, np.float64)
+    mu = X.mean(axis=0)
+    _, S, Vt = np.linalg.svd(X - mu, full_matrices=False)
+    W = Vt[:r].T.copy()
+    lead = np.argmax(np.abs(W), axis=0)
+    W *= np.where(W[lead, np.arange(r)] < 0, -1.0, 1.0)
+    W_up = [W[t * width:(t + 1) * width] for t in range(loops)]
+    return mu, W, W_up, S[:r]
+
+
+def codec_error(x: np.ndarray, mu: np.ndarray, W_down: np.ndarray, W_up: list) -> float:
+    """Relative squared reconstruction error of rows x: [n, T*width] through
+    the codec: encode by Eq. 2, rebuild every loop by Eq. 3, and compare with
+    the centred energy: sum ||x - x_hat||^2 / sum ||x - mu||^2."""
+    X = np.asarray(x, np.float64)
+    c = encode(X, mu, W_down)
+    width = np.asarray(W_up[0]).shape[0]
+    X_hat = np.concatenate([reconstruct(c, W_up[t], loop_slice(mu, t, width))
+                            for t in range(len(W_up))], axis=1)
+    return float(((X - X_hat) ** 2).sum() / ((X - mu) ** 2).sum())

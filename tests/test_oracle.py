@@ -408,10 +408,68 @@ def pin_kv_cache():
             assert rel(ctl, lla) > 1e-3
 
 
+def pin_svd_init():
+    """SVD codec initialisation ([paper] Sec. 3, initialisation and
+    conversion), pinned by what the mathematics fixes:
+    (a) mu's loop-t slice is the mean of the loop-t vectors;
+    (b) Eckart-Young: the codec's error on its calibration rows is the
+        discarded energy, and no other rank-r orthonormal basis (random ones,
+        small rotations of the optimum) does better;
+    (c) rows of exact rank r (after centring) are rebuilt exactly;
+    (d) rank one: x_n = mu0 + a_n u gives W_down = u, sigma = ||a - mean(a)||;
+    (e) a constant offset moves mu only; W_down and sigma are unchanged;
+    (f) W_down is orthonormal, sigma non-increasing, W_up,t its loop-t rows."""
+    rng = np.random.default_rng(31)
+    T, width, n, r = 3, 4, 60, 3
+    K = T * width
+    x = rng.standard_normal((n, 2)) @ rng.standard_normal((2, K)) * 3 \
+        + 0.3 * rng.standard_normal((n, K)) + rng.standard_normal(K)
+    mu, W, W_up, sig = O.svd_init(x, T, width, r)
+    # (a)
+    for t in range(T):
+        assert np.abs(mu[t * width:(t + 1) * width] - x[:, t * width:(t + 1) * width].mean(0)).max() < 1e-12
+    # (b)
+    Xc = x - x.mean(0)
+    tot = (Xc ** 2).sum()
+    err = O.codec_error(x, mu, W, W_up)
+    assert abs(err * tot - (tot - (sig ** 2).sum())) < 1e-9 * tot
+    for _ in range(20):
+        Qr, _ = np.linalg.qr(rng.standard_normal((K, r)))
+        assert O.codec_error(x, mu, Qr, [Qr[t * width:(t + 1) * width] for t in range(T)]) >= err - 1e-12
+        A = rng.standard_normal((K, K)) * 1e-3
+        Rot = np.linalg.qr(np.eye(K) + A - A.T)[0]
+        Wp = Rot @ W
+        assert O.codec_error(x, mu, Wp, [Wp[t * width:(t + 1) * width] for t in range(T)]) >= err - 1e-12
+    # (c)
+    xe = rng.standard_normal((n, r)) @ rng.standard_normal((r, K)) + 5.0
+    m2, W2, U2, _ = O.svd_init(xe, T, width, r)
+    assert O.codec_error(xe, m2, W2, U2) < 1e-20
+    # (d)
+    u = rng.standard_normal(K)
+    u /= np.linalg.norm(u)
+    a = rng.standard_normal(n) * 2 + 1
+    x1 = 0.7 + a[:, None] * u[None, :]
+    _, W1, _, s1 = O.svd_init(x1, T, width, 1)
+    uu = u * (1 if u[np.argmax(np.abs(u))] > 0 else -1)
+    assert np.abs(W1[:, 0] - uu).max() < 1e-10
+    assert abs(s1[0] - np.linalg.norm(a - a.mean())) < 1e-9
+    # (e)
+    off = rng.standard_normal(K) * 10
+    mu3, W3, _, s3 = O.svd_init(x + off, T, width, r)
+    assert np.abs(mu3 - mu - off).max() < 1e-10
+    assert np.abs(W3 - W).max() < 1e-8 and np.abs(s3 - sig).max() < 1e-8
+    # (f)
+    assert np.abs(W.T @ W - np.eye(r)).max() < 1e-12
+    assert np.all(np.diff(sig) <= 0)
+    for t in range(T):
+        assert np.array_equal(W_up[t], W[t * width:(t + 1) * width])
+
+
 PINS = [pin_ratio_closed_form, pin_serving_capacity_example, pin_store_offset,
         pin_exact_reconstruction, pin_decode_equals_teacher_attention,
         pin_decode_equals_materialised_cache, pin_special_cases, pin_rope,
-        pin_2d_reduces_to_per_head, pin_bf16_round, pin_inflight, pin_kv_cache]
+        pin_2d_reduces_to_per_head, pin_bf16_round, pin_inflight, pin_kv_cache,
+        pin_svd_init]
 
 
 @pytest.mark.parametrize("pin", PINS, ids=[p.__name__ for p in PINS])

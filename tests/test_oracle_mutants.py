@@ -113,7 +113,24 @@ def _fast_path_variant(rotate_before_mu=False, rotate_values=False):
     return fast_path_rows
 
 
+def _svd_variant(centre=True, smallest=False, slice_shift=0, row_mean=False):
+    def svd_init(x, loops, width, r):
+        X = np.asarray(x, np.float64)
+        mu = X.mean(axis=1, keepdims=True).repeat(X.shape[1], 1).mean(0) if row_mean else X.mean(0)
+        _, S, Vt = np.linalg.svd(X - mu if centre else X, full_matrices=False)
+        W = (Vt[-r:] if smallest else Vt[:r]).T.copy()
+        K = W.shape[0]
+        W_up = [W[((t + slice_shift) % loops) * width:((t + slice_shift) % loops + 1) * width]
+                for t in range(loops)]
+        return mu, W, W_up, (S[-r:] if smallest else S[:r])
+    return svd_init
+
+
 MUTANTS = {
+    "svd_uncentred": ("svd_init", _svd_variant(centre=False)),
+    "svd_smallest_vectors": ("svd_init", _svd_variant(smallest=True)),
+    "svd_up_slices_shifted": ("svd_init", _svd_variant(slice_shift=1)),
+    "svd_mean_over_features": ("svd_init", _svd_variant(row_mean=True)),
     "cache_keys_not_rotated": ("cache_rows", lambda k, v, positions, base=O.ROPE_BASE:
                                (np.asarray(k, np.float64), np.asarray(v, np.float64))),
     "cache_values_rotated": ("cache_rows", lambda k, v, positions, base=O.ROPE_BASE:
