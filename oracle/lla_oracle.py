@@ -366,7 +366,11 @@ def svd_init(x: np.ndarray, loops: int, width: int, r: int):
     sigma [r])."""
     X = np.asarray(x, np.float64)
     mu = X.mean(axis=0)
-    _, S, Vt = np.linalg.svd(X - mu, full_matrices=False)
+    # With fewer rows than r the centred matrix has fewer than r singular
+    # values: the rest are zero and their vectors complete an orthonormal basis.
+    full = r > min(X.shape)
+    _, S, Vt = np.linalg.svd(X - mu, full_matrices=full)
+    S = np.concatenate([S, np.zeros(max(0, r - S.shape[0]))])
     W = Vt[:r].T.copy()
     lead = np.argmax(np.abs(W), axis=0)
     W *= np.where(W[lead, np.arange(r)] < 0, -1.0, 1.0)

@@ -458,6 +458,11 @@ def pin_svd_init():
     mu3, W3, _, s3 = O.svd_init(x + off, T, width, r)
     assert np.abs(mu3 - mu - off).max() < 1e-10
     assert np.abs(W3 - W).max() < 1e-8 and np.abs(s3 - sig).max() < 1e-8
+    # (c') fewer rows than r: exact, orthonormal, the missing singular values zero
+    xf = rng.standard_normal((5, K))
+    mf, Wf, Uf, sf = O.svd_init(xf, T, width, 8)
+    assert O.codec_error(xf, mf, Wf, Uf) < 1e-20
+    assert np.abs(Wf.T @ Wf - np.eye(8)).max() < 1e-12 and np.abs(sf[4:]).max() < 1e-12
     # (f)
     assert np.abs(W.T @ W - np.eye(r)).max() < 1e-12
     assert np.all(np.diff(sig) <= 0)
