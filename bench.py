@@ -60,6 +60,10 @@ def parse():
                          "final_loop: the final-loop-reuse control")
     ap.add_argument("--batch", type=int, default=0,
                     help="sequences (0 = the workload's own batch)")
+    ap.add_argument("--svd-init", action="store_true",
+                    help="time the SVD codec initialisation of one layer's codecs (K and V, all "
+                         "heads) on synthetic calibration trajectories of the workload's shape")
+    ap.add_argument("--n-cal", type=int, default=4096, help="calibration rows for --svd-init")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="budget of the oracle timing sample (0 disables it)")
     ap.add_argument("--splits", type=int, default=0,
@@ -231,6 +235,80 @@ def cpu_baseline_kv(w, budget_s: float):
             "sample": f"{done} sequence(s) x {w.H} heads of one flash-decode call at pos "
                       f"{w.N - 1}, {spent:.1f} s; scaled x{w.B}/{done} sequences x {calls} "
                       f"calls per step"}
+
+
+def run_svd_init(args, w, torch, L, dev):
+    """SVD initialisation of one layer's codecs (every head, K then V axis)
+    from n_cal synthetic calibration rows per codec: rank-8 loop trajectories
+    plus N(0, 0.05^2) noise, the long-recurrence recipe.  Reports codecs per
+    second and the fp32 GEMM work per second against the vector-ALU peak."""
+    from synth import gen
+    G, K, n = w.store_heads, w.T * w.width, args.n_cal
+    log(f"[bench] svd init: workload {w.name}, {G} codecs per axis, K={K}, n_cal={n}, "
+        f"r_k={w.r_k}, r_v={w.r_v}")
+    x = np.stack([gen.low_rank_trajectory(w.seed, 9000 + g, n, K) for g in range(G)], axis=1)
+    xd = torch.from_numpy(gen.f32_to_bf16_bits(x.astype(np.float32)).view(np.int16)).to(dev)
+    xd = xd.view(torch.bfloat16) if w.dtype == "bf16" else xd.view(torch.bfloat16).float()
+    tdt = xd.dtype
+    outs = {}
+    for r in (w.r_k, w.r_v):
+        outs[r] = (torch.empty((G, K), dtype=torch.float32, device=dev),
+                   torch.empty((G, K, r), dtype=tdt, device=dev),
+                   torch.empty((w.T, G, w.width, r), dtype=tdt, device=dev),
+                   torch.empty((G, r), dtype=torch.float32, device=dev),
+                   torch.empty(L.lla_svd_init_workspace_bytes(G, w.T, w.width, r),
+                               dtype=torch.uint8, device=dev))
+
+    def step(timer=None):
+        for r in (w.r_k, w.r_v):
+            mu, wd, wu, sg, ws = outs[r]
+            if timer is not None:
+                timer.start(torch.cuda.current_stream())
+            L.lla_svd_init(xd, w.T, w.width, r, mu, wd, wu, sg, ws)
+            if timer is not None:
+                timer.stop(torch.cuda.current_stream())
+
+    args.eager = True
+    ms_eager, ms_step, call_ms = time_step(args, step, torch.cuda.current_stream(), torch, 2)
+    # work per call: the centred Gram matrix, then per iteration C Q and two
+    # CholeskyQR passes, then the Rayleigh-Ritz products (fp32 GEMMs)
+    iters = 16
+    flops = {}
+    for r in (w.r_k, w.r_v):
+        m = min(r + 16, 128, K)
+        gram = 2 * n * K * K
+        orth = 2 * (2 * K * m * m + 2 * K * m * m)          # two CholeskyQR passes
+        flops[r] = G * (gram + (iters + 1) * (2 * K * K * m + orth) + 2 * K * m * m
+                        + 2 * K * m * r)
+    total_flops = sum(flops.values())
+    achieved = total_flops / (ms_step / 1e3) / 1e12
+    # error of the codec on its calibration rows (Eckart-Young: discarded energy)
+    xc = xd.float() - xd.float().mean(0, keepdim=True)
+    energy = (xc * xc).sum(dim=(0, 2)).double()
+    # Eckart-Young: with the leading singular values of the larger-rank call,
+    # the error of every smaller rank is the energy beyond its first r values
+    rmax = max(w.r_k, w.r_v)
+    sg2 = outs[rmax][3].double() ** 2
+    err = {}
+    for r in sorted({1, 2, 4, 6, 7, 8, 9, 10, 12, 16, 24, 32, 48, 64, 80, w.r_k, w.r_v}):
+        if r <= rmax:
+            err[str(r)] = float(((energy - sg2[:, :r].sum(1)) / energy).mean())
+    peak = 78.6
+    res = {"metric": "SVD codec initialisation: codecs/s (one layer's K and V codecs of every head)",
+           "value": round(2 * G / (ms_step / 1e3), 2), "unit": "codecs/s", "n_gpus": 1,
+           "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_step, 3),
+           "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32",
+           "data": "synthetic",
+           "config": {"workload": w.name, "codecs_per_axis": G, "K": K, "n_cal": n,
+                      "ranks": [w.r_k, w.r_v], "iterations": iters,
+                      "input": "rank-8 loop trajectories + N(0, 0.05^2), " + w.dtype},
+           "roofline": {"bound": "alu", "achieved": round(achieved, 2), "peak": peak,
+                        "unit": "TFLOP/s", "frac": round(achieved / peak, 4), "traffic": None,
+                        "kernel": "all lla_svd_init kernels (fp32 GEMMs dominate)",
+                        "flops_per_step": total_flops,
+                        "call_ms": [round(float(v), 3) for v in call_ms[:2]]},
+           "calibration_error_vs_r": err, "cpu_baseline": None}
+    print(json.dumps(res), flush=True)
 
 
 def run_kv_path(args, w, torch, L, dev):
@@ -491,6 +569,9 @@ def main():
         w = w.scaled(B=args.batch)
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+    if args.svd_init:
+        run_svd_init(args, w, torch, L, dev)
+        return
     if args.path != "lla":
         run_kv_path(args, w, torch, L, dev)
         return

@@ -305,6 +305,36 @@ lla_status_t lla_kv_decode_attn(const lla_kv_cache_t *cache, int32_t layer, int3
                                 float softmax_scale, float *out, void *workspace,
                                 size_t ws_bytes, int32_t n_splits, hipStream_t stream);
 
+/* ===========================================================================
+ * SVD codec initialisation (paper Sec. 3, initialisation and conversion): for
+ * each of G independent codecs (one per layer, head and axis), from n_cal
+ * calibration rows of its stacked loop vector x = [x_1; ...; x_T] (Eq. 1):
+ *   mu      = the mean row (the per-loop means, stacked)
+ *   W_down  = the r leading right singular vectors of the centred matrix
+ *             X - 1 mu^T (orthonormal columns, by decreasing singular value;
+ *             each column's entry of largest magnitude is positive)
+ *   W_up,t  = rows [t*width, (t+1)*width) of W_down, the loop-t slice.
+ * Computed on the GPU: the Gram matrix of the centred rows, block subspace
+ * iteration (r plus up to 16 extra vectors, CholeskyQR2 in fp64) and a
+ * Rayleigh-Ritz step solved by cyclic Jacobi rotations in fp64.
+ *   dtype      type of x, w_down and w_up (lla_dtype_t)
+ *   groups     G, 1 .. 65535;  loops T, width (d per-head, H*d for LLA-2D)
+ *   r          1 .. min(T*width, 128)
+ *   x          device, [n_cal, G, T*width] (token-major, as the encoders take it)
+ *   mu         device, float32, [G, T*width]
+ *   w_down     device, [G, T*width, r]      (the encoders' W_down layout)
+ *   w_up       device, [T, G, width, r]     (for loop t, the decode calls' W_up,t)
+ *   sigma      device, float32, [G, r] singular values, or NULL
+ *   iters      subspace iterations (0 = 16)
+ *   workspace  device, >= lla_svd_init_workspace_bytes(); the call is
+ *              asynchronous on the stream like every other launching call.
+ * ------------------------------------------------------------------------- */
+size_t lla_svd_init_workspace_bytes(int32_t groups, int32_t loops, int32_t width, int32_t r);
+lla_status_t lla_svd_init(int32_t dtype, int32_t groups, int32_t n_cal, int32_t loops,
+                          int32_t width, int32_t r, const void *x, float *mu, void *w_down,
+                          void *w_up, float *sigma, int32_t iters, void *workspace,
+                          size_t ws_bytes, hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

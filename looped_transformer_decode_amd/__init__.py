@@ -13,4 +13,5 @@ from .lla import (LLA_2D, LLA_DT_BF16, LLA_DT_F32, LLA_PER_HEAD, EXPORTS, KvCach
                   lla_decode_auto_splits, lla_decode_inflight_workspace_bytes, lla_decode_path,
                   lla_decode_workspace_bytes, lla_encode_append, lla_rope_table_bytes,
                   lla_rope_table_fill, lla_store_bytes, lla_store_check, lla_store_offset,
-                  rope_table, status_string, workspace)
+                  lla_svd_init, lla_svd_init_workspace_bytes, rope_table, status_string,
+                  workspace)

@@ -30,7 +30,8 @@ COMMON = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",
           "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
           "-I", INCLUDE, "-I", CSRC]
 SOURCES = ["lla_api.cpp", "decode_valu.hip", "decode_mfma.hip", "encode_valu.hip",
-           "encode_mfma.hip", "decode2d_mfma.hip", "kvcache.hip"]
+           "encode_mfma.hip", "decode2d_mfma.hip", "kvcache.hip",
+           "svd_init.hip"]
 
 
 def _run(cmd):

@@ -200,22 +200,46 @@ __global__ __launch_bounds__(kThreads) void kv_split(KvParams p) {
 }
 
 // Block (h, b): out = sum_s 2^(m_s - M) acc_s / sum_s 2^(m_s - M) l_s.
-__global__ __launch_bounds__(128) void kv_merge(KvParams p) {
-  const int h = blockIdx.x, b = blockIdx.y, d = p.d;
-  const float *part = p.ws + (int64_t)(b * p.H + h) * p.S * (d + 2);
+// The split weights 2^(m_s - M) are formed once into LDS (up to kMergeMaxS
+// splits; more splits recompute them per element).
+constexpr int kMergeThreads = 128;
+constexpr int kMergeMaxS = 1024;
+__global__ __launch_bounds__(kMergeThreads) void kv_merge(KvParams p) {
+  __shared__ float wsh[kMergeMaxS];
+  __shared__ float red[2][kMergeThreads / 64];
+  const int h = blockIdx.x, b = blockIdx.y, d = p.d, S = p.S;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const float *part = p.ws + (int64_t)(b * p.H + h) * S * (d + 2);
   float M = -INFINITY;
-  for (int s = 0; s < p.S; ++s) M = fmaxf(M, part[(int64_t)s * (d + 2)]);
+  for (int s = tid; s < S; s += kMergeThreads) M = fmaxf(M, part[(int64_t)s * (d + 2)]);
+  M = wave_max(M);
+  if (lane == 0) red[0][wave] = M;
+  __syncthreads();
+  M = red[0][0];
+#pragma unroll
+  for (int w = 1; w < kMergeThreads / 64; ++w) M = fmaxf(M, red[0][w]);
   float L = 0.f;
-  for (int s = 0; s < p.S; ++s) {
+  for (int s = tid; s < S; s += kMergeThreads) {
     const float ms = part[(int64_t)s * (d + 2)];
-    if (ms != -INFINITY) L = fmaf(part[(int64_t)s * (d + 2) + 1], exp2f(ms - M), L);
+    const float wgt = ms == -INFINITY ? 0.f : exp2f(ms - M);
+    if (s < kMergeMaxS) wsh[s] = wgt;
+    L = fmaf(part[(int64_t)s * (d + 2) + 1], wgt, L);
   }
+  L = wave_sum(L);
+  if (lane == 0) red[1][wave] = L;
+  __syncthreads();
+  L = red[1][0];
+#pragma unroll
+  for (int w = 1; w < kMergeThreads / 64; ++w) L += red[1][w];
   const float inv = 1.0f / L;
-  for (int i = threadIdx.x; i < d; i += blockDim.x) {
+  for (int i = tid; i < d; i += kMergeThreads) {
     float a = 0.f;
-    for (int s = 0; s < p.S; ++s) {
+    const int s_lds = S < kMergeMaxS ? S : kMergeMaxS;
+#pragma unroll 8
+    for (int s = 0; s < s_lds; ++s) a = fmaf(part[(int64_t)s * (d + 2) + 2 + i], wsh[s], a);
+    for (int s = s_lds; s < S; ++s) {
       const float ms = part[(int64_t)s * (d + 2)];
-      if (ms != -INFINITY) a = fmaf(part[(int64_t)s * (d + 2) + 2 + i], exp2f(ms - M), a);
+      a = fmaf(part[(int64_t)s * (d + 2) + 2 + i], ms == -INFINITY ? 0.f : exp2f(ms - M), a);
     }
     p.out[((int64_t)b * p.H + h) * d + i] = a * inv;
   }
@@ -411,7 +435,7 @@ hipError_t launch_kv_decode(const KvParams &p, int dtype, hipStream_t st) {
   const hipError_t e = dtype == LLA_DT_F32 ? launch_split<float>(p, grid, st)
                                            : launch_split<bf16_t>(p, grid, st);
   if (e != hipSuccess || p.S == 1) return e;
-  hipLaunchKernelGGL(kv_merge, dim3(p.H, p.B), dim3(128), 0, st, p);
+  hipLaunchKernelGGL(kv_merge, dim3(p.H, p.B), dim3(kMergeThreads), 0, st, p);
   return hipGetLastError();
 }
 

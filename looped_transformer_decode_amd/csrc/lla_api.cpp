@@ -294,6 +294,21 @@ lla::KvParams kv_params(const lla_kv_cache_t *c, int32_t layer, int32_t cache_lo
   return p;
 }
 
+// ---- SVD codec initialisation -----------------------------------------------
+constexpr int32_t kSvdMaxBlock = 128;   // iterated block m (Jacobi / Cholesky in LDS)
+constexpr int32_t kSvdOversample = 16;
+constexpr int32_t kSvdDefaultIters = 16;
+constexpr int32_t kSvdSweeps = 10;
+
+// The iterated block size m for rank r (0 if r is out of range).
+int32_t svd_block(int32_t K, int32_t r) {
+  if (r < 1 || r > K || r > kSvdMaxBlock) return 0;
+  int32_t m = r + kSvdOversample;
+  if (m > kSvdMaxBlock) m = kSvdMaxBlock;
+  if (m > K) m = K;
+  return m;
+}
+
 }  // namespace
 
 extern "C" {
@@ -576,6 +591,50 @@ lla_status_t lla_kv_decode_attn(const lla_kv_cache_t *c, int32_t layer, int32_t 
   p.split_len = (c->max_ctx + S - 1) / S;
   p.out = out;
   return lla::launch_kv_decode(p, c->dtype, stream) == hipSuccess ? LLA_OK : LLA_E_HIP;
+}
+
+size_t lla_svd_init_workspace_bytes(int32_t groups, int32_t loops, int32_t width, int32_t r) {
+  if (groups < 1 || groups > 65535 || loops < 1 || width < 1) return 0;
+  const int64_t K = (int64_t)loops * width;
+  if (K > 65536) return 0;
+  const int32_t m = svd_block((int32_t)K, r);
+  if (m == 0) return 0;
+  return lla::svd_layout(groups, (int32_t)K, m, r).total;
+}
+
+lla_status_t lla_svd_init(int32_t dtype, int32_t groups, int32_t n_cal, int32_t loops,
+                          int32_t width, int32_t r, const void *x, float *mu, void *w_down,
+                          void *w_up, float *sigma, int32_t iters, void *workspace,
+                          size_t ws_bytes, hipStream_t stream) {
+  if (dtype != LLA_DT_F32 && dtype != LLA_DT_BF16) return LLA_E_DTYPE;
+  if (groups < 1 || n_cal < 1 || loops < 1 || width < 1) return LLA_E_SHAPE;
+  if (groups > 65535) return LLA_E_UNSUPPORTED;
+  const int64_t K = (int64_t)loops * width;
+  if (K > 65536) return LLA_E_UNSUPPORTED;
+  if (r < 1 || r > K) return LLA_E_RANGE;
+  if (r > kSvdMaxBlock) return LLA_E_UNSUPPORTED;
+  if (iters < 0 || iters > 1000) return LLA_E_RANGE;
+  if ((int64_t)n_cal * groups * K > ((int64_t)1 << 40)) return LLA_E_OVERFLOW;
+  if (!x || !mu || !w_down || !w_up) return LLA_E_NULL;
+  const size_t need = lla_svd_init_workspace_bytes(groups, loops, width, r);
+  if (!workspace || need == 0 || ws_bytes < need) return LLA_E_WORKSPACE;
+  lla::SvdParams p{};
+  p.G = groups;
+  p.N = n_cal;
+  p.K = (int32_t)K;
+  p.T = loops;
+  p.width = width;
+  p.r = r;
+  p.m = svd_block((int32_t)K, r);
+  p.iters = iters ? iters : kSvdDefaultIters;
+  p.sweeps = kSvdSweeps;
+  p.x = x;
+  p.mu = mu;
+  p.w_down = w_down;
+  p.w_up = w_up;
+  p.sigma = sigma;
+  p.ws = workspace;
+  return lla::launch_svd_init(p, dtype, stream) == hipSuccess ? LLA_OK : LLA_E_HIP;
 }
 
 }  // extern "C"

@@ -117,6 +117,24 @@ struct KvParams {
   const int32_t *start;    // [B]
 };
 
+// SVD codec initialisation: G codecs, N calibration rows of K = T * width.
+struct SvdParams {
+  int32_t G, N, K, T, width, r, m;  // m = r + oversampling: the iterated block
+  int32_t iters, sweeps;
+  const void *x;        // [N, G, K]
+  float *mu;            // [G, K]
+  void *w_down;         // [G, K, r]
+  void *w_up;           // [T, G, width, r]
+  float *sigma;         // [G, r] or null
+  void *ws;
+};
+// Byte offsets of the SVD workspace regions.
+struct SvdLayout {
+  size_t gram, q, y, small, rinv, u, evals, order, usel, w, total;
+};
+SvdLayout svd_layout(int32_t G, int32_t K, int32_t m, int32_t r);
+hipError_t launch_svd_init(const SvdParams &p, int dtype, hipStream_t s);
+
 // Launchers (return the launch status).  dtype is lla_dtype_t.
 hipError_t launch_decode_valu(const DecodeParams &p, int dtype, hipStream_t s);
 hipError_t launch_decode_merge(const DecodeParams &p, int dtype, hipStream_t s);

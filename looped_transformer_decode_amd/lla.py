@@ -72,6 +72,9 @@ _SIGS = {
     "lla_kv_decode_workspace_bytes": ([_P, _I32], _SZ),
     "lla_kv_decode_auto_splits": ([_P], _I32),
     "lla_kv_decode_attn": ([_P, _I32, _I32, _P, _P, _P, _F, _P, _P, _SZ, _I32, _P], _I32),
+    "lla_svd_init_workspace_bytes": ([_I32, _I32, _I32, _I32], _SZ),
+    "lla_svd_init": ([_I32, _I32, _I32, _I32, _I32, _I32, _P, _P, _P, _P, _P, _I32, _P, _SZ, _P],
+                     _I32),
 }
 EXPORTS = tuple(_SIGS)
 
@@ -475,3 +478,36 @@ def lla_kv_decode_attn(cache, layer, cache_loop, q, pos, rope_table, out, worksp
                                     else workspace.numel() * workspace.element_size(),
                                     n_splits, _stream(stream)), "lla_kv_decode_attn")
     return out
+
+
+# ------------------------------------------------------ SVD initialisation
+def lla_svd_init_workspace_bytes(groups: int, loops: int, width: int, r: int) -> int:
+    return lib().lla_svd_init_workspace_bytes(groups, loops, width, r)
+
+
+def lla_svd_init(x, loops, width, r, mu, w_down, w_up, sigma=None, workspace=None, iters=0,
+                 stream=None):
+    """SVD codec initialisation of G codecs from calibration rows x
+    [n_cal, G, loops*width] (float32 or bfloat16): writes mu [G, K] (float32),
+    w_down [G, K, r], w_up [loops, G, width, r] (x's type) and, if given,
+    sigma [G, r] (float32).  Allocates the workspace if none is passed."""
+    if x.dim() != 3:
+        raise ValueError("x must be [n_cal, G, loops*width]")
+    n_cal, G, K = x.shape
+    if K != loops * width:
+        raise ValueError("x's last dimension must be loops * width")
+    dt = {torch.float32: LLA_DT_F32, torch.bfloat16: LLA_DT_BF16}.get(x.dtype)
+    if dt is None:
+        raise ValueError("x must be float32 or bfloat16")
+    _need(x, x.dtype, None, "x")
+    _need(mu, torch.float32, (G, K), "mu")
+    _need(w_down, x.dtype, (G, K, r), "w_down")
+    _need(w_up, x.dtype, (loops, G, width, r), "w_up")
+    _need(sigma, torch.float32, (G, r), "sigma")
+    if workspace is None:
+        n = lla_svd_init_workspace_bytes(G, loops, width, r)
+        workspace = torch.empty(max(n, 4), dtype=torch.uint8, device=x.device)
+    _check(lib().lla_svd_init(dt, G, n_cal, loops, width, r, _ptr(x), _ptr(mu), _ptr(w_down),
+                              _ptr(w_up), _ptr(sigma), iters, _ptr(workspace),
+                              workspace.numel() * workspace.element_size(), _stream(stream)),
+           "lla_svd_init")

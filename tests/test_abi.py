@@ -315,3 +315,25 @@ def test_kv_calls_validate_first():
     assert app(layer=-1) == 4 and app(cl=4) == 4 and app(n=-1) == 4 and app(n=65) == 4
     assert app(n=0) == 0
     assert app(data=False) == 1 and app(k=None) == 1 and app(start=None) == 1
+
+
+# --------------------------------------------------------- SVD initialisation
+def test_svd_init_sizes_and_validation():
+    lib = L.lib()
+    P = 4096  # stands for a device pointer; never dereferenced
+    assert L.lla_svd_init_workspace_bytes(16, 16, 128, 48) > 16 * 2048 * 2048 * 4
+    assert L.lla_svd_init_workspace_bytes(0, 4, 128, 8) == 0
+    assert L.lla_svd_init_workspace_bytes(1, 4, 8, 33) == 0       # r > K
+    assert L.lla_svd_init_workspace_bytes(1, 4, 128, 129) == 0    # r above the block limit
+
+    def call(dtype=1, G=2, n=100, T=4, width=32, r=8, x=P, mu=P, wd=P, wu=P, iters=0,
+             ws=P, ws_bytes=1 << 40):
+        return lib.lla_svd_init(dtype, G, n, T, width, r, x, mu, wd, wu, None, iters, ws,
+                                ws_bytes, None)
+    assert call(dtype=4) == 3
+    assert call(G=0) == 2 and call(n=0) == 2 and call(T=0) == 2 and call(width=0) == 2
+    assert call(r=0) == 4 and call(r=129, width=64) == 6 and call(r=200) == 4
+    assert call(iters=-1) == 4
+    assert call(x=None) == 1 and call(mu=None) == 1 and call(wd=None) == 1 and call(wu=None) == 1
+    assert call(ws=None) == 5 and call(ws_bytes=1024) == 5
+    assert call(G=70000) == 6
