@@ -31,7 +31,7 @@ COMMON = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",
           "-I", INCLUDE, "-I", CSRC]
 SOURCES = ["lla_api.cpp", "decode_valu.hip", "decode_mfma.hip", "encode_valu.hip",
            "encode_mfma.hip", "decode2d_mfma.hip", "kvcache.hip",
-           "svd_init.hip"]
+           "svd_init.hip", "decode_mq.hip"]
 
 
 def _run(cmd):

@@ -171,8 +171,11 @@ lla_status_t decode_impl(const lla_store_t *st, int32_t want_variant, int32_t la
 
   const bool is2d = st->variant == LLA_2D;
   p.write_out = (mfma && !is2d && S == 1 && !inflight) ? 1 : 0;
+  const bool mq = mfma && !is2d && inflight && n_q > 1 &&
+                  lla::decode_mq_supported(st->d_head, st->r_k, st->r_v, p.Hs, p.H, n_q);
   hipError_t he = !mfma ? lla::launch_decode_valu(p, st->dtype, stream)
                   : is2d ? lla::launch_decode2d_mfma(p, stream)
+                  : mq   ? lla::launch_decode_mq(p, stream)
                          : lla::launch_decode_mfma(p, stream);
   if (he != hipSuccess) return LLA_E_HIP;
   if (p.write_out) return LLA_OK;  // the split kernel applied W_up,v,t itself

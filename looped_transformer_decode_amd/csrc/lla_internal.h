@@ -150,6 +150,10 @@ bool decode_mfma_supported(int32_t H, int32_t d, int32_t rk, int32_t rv, int32_t
 // Heads one fast-path workgroup covers (0 if the ranks have no instance).
 int32_t decode_mfma_group_heads(int32_t rk, int32_t rv);
 hipError_t launch_decode_mfma(const DecodeParams &p, hipStream_t s);
+// Multi-query store pass (reconstruct first): all n_q <= 16 queries of a
+// sequence per workgroup; writes the same partials as launch_decode_mfma.
+bool decode_mq_supported(int32_t d, int32_t rk, int32_t rv, int32_t Hs, int32_t H, int32_t n_q);
+hipError_t launch_decode_mq(const DecodeParams &p, hipStream_t s);
 hipError_t launch_encode_valu(const EncodeParams &p, int dtype, hipStream_t s);
 bool encode_mfma_supported(const EncodeParams &p, int dtype);
 hipError_t launch_encode_mfma(const EncodeParams &p, hipStream_t s);

@@ -224,6 +224,7 @@ def test_garbage_beyond_pos_is_ignored(device, tmpl):
 INFLIGHT_SHAPES = [
     ("long_recurrence_t16_ctx8k", dict(B=2, D=2, N=300, H=8), 16),   # fast path, n_q = 16
     ("extreme_batch_b768_ctx4k", dict(B=3, D=1, N=200), 4),
+    ("bf16_b32_ctx4k", dict(B=2, D=1, N=260, H=6), 7),                # heads not a multiple of 4
     ("tiny_fp32", dict(B=3, N=128), 3),                              # generic fp32 path
     ("lla2d_b256_ctx4k", dict(B=2, D=1, N=170), 4),                  # LLA-2D fast path
 ]
