@@ -25,7 +25,10 @@
 //    slots), P through LDS, C_v gathered from a staged tile whose row pitch
 //    spreads the four slot groups over distinct banks.
 // Latent rows are read with direct 16-byte global loads, the next tile's
-// issued as soon as the current one's reconstruction has consumed them.
+// issued as soon as the current one's have been consumed.  The rotation of
+// each (slot, dim) comes from the RoPE table's bf16 phi tile of the 32 slots,
+// copied HBM-to-LDS once per workgroup (a quarter by each wave, two buffers,
+// one barrier per tile); every other LDS region is private to a wave.
 #include "lla_device.h"
 #include "lla_internal.h"
 
@@ -45,6 +48,8 @@ constexpr int kWaves = 4;
 constexpr int kThreads = 64 * kWaves;
 constexpr int kQ = 16;               // query rows of the MFMA tiles
 constexpr float kRescaleGap = 8.0f;  // log2 domain
+constexpr int kPhiTileBytes = kTile * kD * 2;  // bf16 phi rows of one 32-slot tile
+#define LDS_AS __attribute__((address_space(3)))
 
 template <int RK, int RV>
 struct Cfg {
@@ -58,7 +63,8 @@ struct Cfg {
   static constexpr int V_OFF = kTile * kD * 2;
   static constexpr int P_OFF = V_OFF + (kTile * VPITCH * 2 + 15) / 16 * 16;
   static constexpr int WAVE_BYTES = P_OFF + kQ * PPITCH * 2;
-  static constexpr int LDS = WAVE_BYTES * kWaves;
+  static constexpr int PHI_OFF = WAVE_BYTES * kWaves;     // two shared phi tiles
+  static constexpr int LDS = PHI_OFF + 2 * kPhiTileBytes;
 };
 
 // DPP row operations within groups of 16 lanes (see kvcache.hip).
@@ -81,6 +87,14 @@ __device__ __forceinline__ float row16_sum(float v) {
 }
 
 __device__ __forceinline__ int kswz(int slot, int chunk) { return chunk ^ (slot & 15); }
+
+// Every LDS region here is private to one wave, so lanes of the same wave
+// exchange data through it without a workgroup barrier: wait for this
+// wave's LDS writes, and keep the compiler from moving LDS accesses across.
+__device__ __forceinline__ void wave_lds_sync() {
+  __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0); vmcnt, expcnt not waited
+  __builtin_amdgcn_wave_barrier();
+}
 
 template <int RK, int RV>
 __global__ __launch_bounds__(kThreads) void decode_mq_split(DecodeParams p) {
@@ -172,12 +186,14 @@ __global__ __launch_bounds__(kThreads) void decode_mq_split(DecodeParams p) {
   const uint16_t *lat = reinterpret_cast<const uint16_t *>(p.store) +
                         ((int64_t)b * p.D + p.layer) * p.N * srow + (int64_t)h * R;
   u32x4_t kb[C::KS], vch[C::VLOADS];
-  auto load_tile = [&](int tb) {
+  auto load_k = [&](int tb) {
     const int js = min(tb + l32, t1 - 1);
 #pragma unroll
     for (int ks = 0; ks < C::KS; ++ks)
       kb[ks] = __builtin_nontemporal_load(
           reinterpret_cast<const u32x4_t *>(lat + js * srow + 16 * ks + 8 * h2));
+  };
+  auto load_v = [&](int tb) {
 #pragma unroll
     for (int u = 0; u < C::VLOADS; ++u) {
       const int c = lane + 64 * u;
@@ -186,6 +202,26 @@ __global__ __launch_bounds__(kThreads) void decode_mq_split(DecodeParams p) {
       if (c < kTile * C::VCH)
         vch[u] = __builtin_nontemporal_load(
             reinterpret_cast<const u32x4_t *>(lat + j * srow + RK + 8 * q));
+    }
+  };
+  auto load_tile = [&](int tb) {
+    load_k(tb);
+    load_v(tb);
+  };
+
+  // bf16 phi rows of tile tb (the RoPE table's MFMA tiles): the workgroup's
+  // four waves each copy a quarter into LDS buffer `buf`, HBM to LDS directly
+  const __amdgpu_buffer_rsrc_t rphi = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint16_t *>(p.rope_bf16), (short)0,
+      ((p.N + kTile - 1) / kTile) * kPhiTileBytes, 0x00020000);
+  auto issue_phi = [&](int tb, int buf) {
+    char *pb = lds + C::PHI_OFF + buf * kPhiTileBytes;
+    const uint32_t off = (uint32_t)(tb / kTile) * kPhiTileBytes;
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const int blk = 2 * wave + u;  // 1 KB blocks 0..7
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rphi, (LDS_AS void *)(pb + blk * 1024), 16,
+                                               off + (uint32_t)(blk * 64 + lane) * 16, 0, 0, 0);
     }
   };
 
@@ -200,8 +236,16 @@ __global__ __launch_bounds__(kThreads) void decode_mq_split(DecodeParams p) {
   for (int v = 0; v < C::VB; ++v) acc[v] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
   load_tile(t0);
-  for (int tb = t0; tb < t1; tb += kTile) {
-    // V chunks of this tile into the staged tile
+  issue_phi(t0, 0);
+  for (int tb = t0, it = 0; tb < t1; tb += kTile, ++it) {
+    const bool more = tb + kTile < t1;
+    // this tile's latents (registers) and phi rows (LDS) have landed, and
+    // every wave is done with the phi buffer the next copy overwrites
+    __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
+    __syncthreads();
+    const char *phb = lds + C::PHI_OFF + (it & 1) * kPhiTileBytes;
+    // V chunks of this tile into the staged tile, then the next tile's V
+    // chunks and phi rows on their way
 #pragma unroll
     for (int u = 0; u < C::VLOADS; ++u) {
       const int c = lane + 64 * u;
@@ -212,14 +256,15 @@ __global__ __launch_bounds__(kThreads) void decode_mq_split(DecodeParams p) {
         dst[1] = u32x2_t{vch[u][2], vch[u][3]};
       }
     }
+    if (more) issue_phi(tb + kTile, (it + 1) & 1);
     // K^T of the tile, two dim-tile pairs (T, T + 2) at a time
     bf16x8_t kbf[C::KS];
 #pragma unroll
     for (int ks = 0; ks < C::KS; ++ks) kbf[ks] = __builtin_bit_cast(bf16x8_t, kb[ks]);
-    const int slot = tb + l32;
-    const float *cs = p.rope_f32 + (int64_t)min(slot, p.N - 1) * kD;
 #pragma unroll
     for (int T = 0; T < 2; ++T) {
+      // one pair of accumulator tiles live at a time
+      __builtin_amdgcn_sched_barrier(0);
       f32x16_t a0 = {}, a1 = {};
 #pragma unroll
       for (int ks = 0; ks < C::KS; ++ks) {
@@ -231,10 +276,14 @@ __global__ __launch_bounds__(kThreads) void decode_mq_split(DecodeParams p) {
 #pragma unroll
       for (int c = 0; c < 4; ++c) {
         const int i0 = 32 * T + 8 * c + 4 * h2;  // first of four consecutive dims (< 64)
-        const f32x4_t c01 = *reinterpret_cast<const f32x4_t *>(cs + 2 * i0);
-        const f32x4_t c23 = *reinterpret_cast<const f32x4_t *>(cs + 2 * i0 + 4);
-        const float co[4] = {c01[0], c01[2], c23[0], c23[2]};
-        const float sn[4] = {c01[1], c01[3], c23[1], c23[3]};
+        // phi tile element (step 2T + c/2, lane l32 + 32 (c%2), 4 h2 + e): cos at dim
+        // i0 + e, and 4 steps further sin
+        const uint16_t *ph = reinterpret_cast<const uint16_t *>(phb) +
+                             ((2 * T + c / 2) * 64 + l32 + 32 * (c % 2)) * 8 + 4 * h2;
+        const u32x2_t cw = *reinterpret_cast<const u32x2_t *>(ph);
+        const u32x2_t sw = *reinterpret_cast<const u32x2_t *>(ph + 4 * 64 * 8);
+        const float co[4] = {bf16_lo(cw[0]), bf16_hi(cw[0]), bf16_lo(cw[1]), bf16_hi(cw[1])};
+        const float sn[4] = {bf16_lo(sw[0]), bf16_hi(sw[0]), bf16_lo(sw[1]), bf16_hi(sw[1])};
         float r0[4], r1[4];
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
@@ -249,8 +298,11 @@ __global__ __launch_bounds__(kThreads) void decode_mq_split(DecodeParams p) {
             u32x2_t{pack_bf16x2(r1[0], r1[1]), pack_bf16x2(r1[2], r1[3])};
       }
     }
-    if (tb + kTile < t1) load_tile(tb + kTile);  // registers free: prefetch the next tile
-    __syncthreads();
+    if (more) {  // the latents' registers are free again: the next tile's
+      load_k(tb + kTile);
+      load_v(tb + kTile);
+    }
+    wave_lds_sync();
 
     // S = Q K^T: queries 4 g4 + i, slots 16 nt + l16
     f32x4_t sc[2];
@@ -285,7 +337,7 @@ __global__ __launch_bounds__(kThreads) void decode_mq_split(DecodeParams p) {
       Pt[q * C::PPITCH + l16] = p0;
       Pt[q * C::PPITCH + 16 + l16] = p1;
     }
-    __syncthreads();
+    wave_lds_sync();
 
     // acc += P C_v (queries x value columns, K = 32 slots)
     const bf16x8_t pa = *reinterpret_cast<const bf16x8_t *>(Pt + l16 * C::PPITCH + 8 * g4);

@@ -259,19 +259,23 @@ __global__ __launch_bounds__(256) void decode_merge_batched(DecodeParams p) {
 //   out = [e^(M_s - M) (W_up,v,t A + mu_v,t L_s) + sum_m e^(s_m - M) v_m]
 //         / [e^(M_s - M) L_s + sum_m e^(s_m - M)],
 //   s_m = scale * RoPE(q_i, pos0 + i) . RoPE(k_m, pos0 + m)   (log2 domain).
-// One block per (head, sequence); one thread per element of d.
+// One block per (head, sequence); one thread per element of d.  Every
+// query's store partials are merged at once, W_up,v,t is applied to all
+// query averages in one pass over its row, and the exact in-flight term is
+// added per query.
+constexpr int kMaxQ = 32;  // in-flight queries per call
+
 template <typename E>
 __global__ __launch_bounds__(256) void decode_merge_inflight(DecodeParams p, const float *k_new,
                                                             const float *v_new) {
   const int h = blockIdx.x, b = blockIdx.y, t = threadIdx.x, nt = blockDim.x;
   const int d = p.d, half = d / 2, rv = p.rv, S = p.S, nq = p.qps, H = p.H;
-  const int lane = t & 63, wave = t >> 6, nw = nt >> 6;
   extern __shared__ float sm[];
-  float *kr = sm;                 // [nq][d]  rotated in-flight keys
+  float *kr = sm;                 // [nq][d]  rotated in-flight keys, then their values
   float *qr = kr + nq * d;        // [nq][d]  rotated, scaled queries
   float *sc = qr + nq * d;        // [nq][nq] in-flight scores (m <= i)
-  float *abar = sc + nq * nq;     // [rv]     store latent numerator of one query
-  float *st = abar + rv;          // [2]      store M, L of one query
+  float *abar = sc + nq * nq;     // [nq][rv] store latent numerators
+  float *st = abar + nq * rv;     // [nq][2]  store M, L; then [nq][S] split weights
   const int first = min(max(p.pos[b], 0), p.N);
   const bool act = t < d;
 
@@ -283,57 +287,92 @@ __global__ __launch_bounds__(256) void decode_merge_inflight(DecodeParams p, con
     return x[t] * cs[2 * u] + x[u] * cs[2 * u + 1];
   };
   if (act) {
+#pragma unroll 4
     for (int m = 0; m < nq; ++m) {
       const int64_t row = ((int64_t)(b * nq + m) * H + h) * d;
       kr[m * d + t] = rot(k_new + row, first + m);
       qr[m * d + t] = rot(p.q + row, first + m) * p.scale_log2;
     }
   }
+  // store partials of every query, merged over the splits
+  // split weights 2^(m_s - M) of every query, then the numerators
+  float *wsp = st + 2 * nq;       // [nq][S]
+  for (int i = t; i < nq; i += nt) {
+    const float *part = p.ws + (int64_t)((b * nq + i) * H + h) * S * (rv + 2);
+    float M = -INFINITY;
+    for (int s2 = 0; s2 < S; ++s2) M = fmaxf(M, part[s2 * (rv + 2)]);
+    float L = 0.f;
+    for (int s2 = 0; s2 < S; ++s2) {
+      const float ms = part[s2 * (rv + 2)];
+      const float w = ms == -INFINITY ? 0.f : exp2f(ms - M);
+      wsp[i * S + s2] = w;
+      L = fmaf(part[s2 * (rv + 2) + 1], w, L);
+    }
+    st[2 * i] = M;
+    st[2 * i + 1] = L;
+  }
   __syncthreads();
-  // scores s[i][m], m <= i: one wave per dot product, lanes over d
-  for (int pr = wave; pr < nq * nq; pr += nw) {
+  for (int e = t; e < nq * rv; e += nt) {
+    const int i = e / rv, r = e % rv;
+    const float *part = p.ws + (int64_t)((b * nq + i) * H + h) * S * (rv + 2) + 2 + r;
+    float a = 0.f;
+#pragma unroll 4
+    for (int s2 = 0; s2 < S; ++s2) a = fmaf(part[s2 * (rv + 2)], wsp[i * S + s2], a);
+    abar[i * rv + r] = a;
+  }
+  __syncthreads();
+  // scores s[i][m], m <= i: one thread per pair, the element order rotated
+  // per thread so that threads of a wave read different banks
+  for (int pr = t; pr < nq * nq; pr += nt) {
     const int i = pr / nq, m = pr % nq;
     if (m > i) continue;
     float v = 0.f;
-    for (int e = lane; e < d; e += 64) v = fmaf(qr[i * d + e], kr[m * d + e], v);
-    v = wave_sum(v);
-    if (lane == 0) sc[i * nq + m] = v;
-  }
-  const E *wrow = reinterpret_cast<const E *>(p.wv) + ((int64_t)h * d + (act ? t : 0)) * rv;
-  const float mu = act ? p.muv[(int64_t)h * d + t] : 0.f;
-  for (int i = 0; i < nq; ++i) {
-    const int vb = b * nq + i;
-    const float *part = p.ws + (int64_t)(vb * H + h) * S * (rv + 2);
-    __syncthreads();  // scores ready; previous query's abar / st consumed
-    for (int r = t; r < rv + 2; r += nt) {
-      float M = -INFINITY;
-      for (int s2 = 0; s2 < S; ++s2) M = fmaxf(M, part[s2 * (rv + 2)]);
-      float a = 0.f;
-      if (r > 0) {
-        for (int s2 = 0; s2 < S; ++s2) {
-          const float *ps = part + s2 * (rv + 2);
-          if (ps[0] != -INFINITY) a = fmaf(ps[r], exp2f(ps[0] - M), a);
-        }
-      }
-      if (r == 0) st[0] = M;
-      else if (r == 1) st[1] = a;
-      else abar[r - 2] = a;
+    const int e0 = pr % d;
+    for (int k = 0; k < d; ++k) {
+      const int e = (e0 + k) % d;
+      v = fmaf(qr[i * d + e], kr[m * d + e], v);
     }
-    __syncthreads();
-    if (!act) continue;
-    const float Ms = st[0], Ls = st[1];
+    sc[i * nq + m] = v;
+  }
+  __syncthreads();
+  if (act)  // the keys are done with: stage the in-flight values instead
+    for (int m = 0; m < nq; ++m) kr[m * d + t] = v_new[((int64_t)(b * nq + m) * H + h) * d + t];
+  // W_up,v,t row t against every query's latent average
+  float wa[kMaxQ];
+#pragma unroll
+  for (int i = 0; i < kMaxQ; ++i) wa[i] = 0.f;
+  if (act) {
+    const E *wrow = reinterpret_cast<const E *>(p.wv) + ((int64_t)h * d + t) * rv;
+    for (int r0 = 0; r0 < rv; r0 += 8) {
+      float w[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) w[e] = r0 + e < rv ? load_elem(wrow, r0 + e) : 0.f;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        if (r0 + e >= rv) break;
+#pragma unroll
+        for (int i = 0; i < kMaxQ; ++i)
+          if (i < nq) wa[i] = fmaf(w[e], abar[i * rv + r0 + e], wa[i]);
+      }
+    }
+  }
+  __syncthreads();
+  if (!act) return;
+  const float mu = p.muv[(int64_t)h * d + t];
+#pragma unroll
+  for (int i = 0; i < kMaxQ; ++i) {
+    if (i >= nq) break;
+    const float Ms = st[2 * i], Ls = st[2 * i + 1];
     float M = Ms;
     for (int m = 0; m <= i; ++m) M = fmaxf(M, sc[i * nq + m]);
     const float fs = (Ms == -INFINITY) ? 0.f : exp2f(Ms - M);
-    float wa = 0.f;
-    for (int r = 0; r < rv; ++r) wa = fmaf(load_elem(wrow, r), abar[r], wa);
-    float num = fs * fmaf(mu, Ls, wa), den = fs * Ls;
+    float num = fs * fmaf(mu, Ls, wa[i]), den = fs * Ls;
     for (int m = 0; m <= i; ++m) {
       const float e = exp2f(sc[i * nq + m] - M);
       den += e;
-      num = fmaf(e, v_new[((int64_t)(b * nq + m) * H + h) * d + t], num);
+      num = fmaf(e, kr[m * d + t], num);
     }
-    p.out[((int64_t)vb * H + h) * d + t] = num / den;
+    p.out[((int64_t)(b * nq + i) * H + h) * d + t] = num / den;
   }
 }
 
@@ -374,9 +413,17 @@ hipError_t launch_decode_merge_batched(const DecodeParams &p, int dtype, hipStre
 
 hipError_t launch_decode_merge_inflight(const DecodeParams &p, int32_t B_real, const float *k_new,
                                         const float *v_new, int dtype, hipStream_t st) {
-  const int threads = (p.d + 63) / 64 * 64;
-  const size_t sm = sizeof(float) * ((size_t)2 * p.qps * p.d + (size_t)p.qps * p.qps + p.rv + 2);
+  if (p.qps > kMaxQ) return hipErrorInvalidValue;
+  const int threads = 256 > p.d ? 256 : (p.d + 63) / 64 * 64;
+  const size_t sm = sizeof(float) * ((size_t)2 * p.qps * p.d + (size_t)p.qps * p.qps +
+                                     (size_t)p.qps * p.rv + 2 * (size_t)p.qps +
+                                     (size_t)p.qps * p.S);
+  if (sm > 160 * 1024) return hipErrorInvalidValue;
   dim3 grid(p.H, B_real);
+  const void *fn = dtype == LLA_DT_F32 ? reinterpret_cast<const void *>(decode_merge_inflight<float>)
+                                       : reinterpret_cast<const void *>(decode_merge_inflight<bf16_t>);
+  const hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)sm);
+  if (e != hipSuccess) return e;
   if (dtype == LLA_DT_F32)
     hipLaunchKernelGGL(decode_merge_inflight<float>, grid, dim3(threads), sm, st, p, k_new, v_new);
   else
