@@ -66,34 +66,53 @@ uint16_t f64_to_bf16(double v) {
   return (uint16_t)(u >> 16);
 }
 
-int32_t auto_splits(const lla_store_t *s, bool mfma) {
-  // Per-head fast path: enough workgroups to cover the 256 CUs three times
-  // (one workgroup fills a CU's LDS).  LLA-2D fast path (bound by the matrix
-  // cores): one workgroup per CU.  Each split at least 256 slots long so that
-  // the per-workgroup setup stays amortised.
-  const bool is2d = s->variant == LLA_2D;
-  int64_t per_split, target;
-  if (mfma && is2d) {
-    per_split = s->batch;
-    target = 256;
-  } else if (mfma) {
-    per_split = (int64_t)s->batch * (s->heads / lla::decode_mfma_group_heads(s->r_k, s->r_v));
-    target = 768;
-  } else {
-    per_split = (int64_t)s->batch * s->heads;
-    target = 2048;
+// Context splits that fill whole rounds of resident workgroups: the S in
+// [1, max_s] with the least ceil(per_split * S / slots) / S (the work one
+// workgroup slot sees per unit of context), ties going to the fewest splits
+// (less setup and merging).  `slots` = workgroups the GPU runs at once.
+int32_t fill_rounds(int64_t per_split, int64_t slots, int64_t max_s) {
+  int64_t best = 1;
+  double best_cost = 1e300;
+  for (int64_t S = 1; S <= max_s; ++S) {
+    const double cost = (double)((per_split * S + slots - 1) / slots) / (double)S;
+    if (cost < best_cost * (1.0 - 1e-9)) {
+      best_cost = cost;
+      best = S;
+    }
   }
-  int64_t S = (target + per_split - 1) / per_split;
+  return (int32_t)best;
+}
+
+bool mq_path(const lla_store_t *s, int32_t n_q);
+
+int32_t auto_splits(const lla_store_t *s, bool mfma, int32_t n_q = 1) {
+  // The fast-path kernels hold one workgroup per CU (the LLA-2D one and the
+  // per-head one fill the LDS), the multi-query one two; each split at least
+  // 256 slots long.  The generic path: about eight workgroups per CU.
+  constexpr int64_t kCUs = 256;
+  const bool is2d = s->variant == LLA_2D;
   const int64_t max_s = std::max<int64_t>(1, s->max_ctx / 256);
+  if (mfma && is2d) return fill_rounds(s->batch, kCUs, max_s);
+  if (mfma && n_q > 1 && mq_path(s, n_q))
+    return fill_rounds((int64_t)s->batch * ((s->heads + 3) / 4), 2 * kCUs, max_s);
+  if (mfma)
+    return fill_rounds((int64_t)s->batch * (s->heads / lla::decode_mfma_group_heads(s->r_k, s->r_v)),
+                       kCUs, max_s);
+  const int64_t per_split = (int64_t)s->batch * s->heads;
+  int64_t S = (2048 + per_split - 1) / per_split;
   if (S > max_s) S = max_s;
-  if (S < 1) S = 1;
-  return (int32_t)S;
+  return (int32_t)std::max<int64_t>(1, S);
 }
 
 bool use_mfma(const lla_store_t *s) {
   if (s->dtype != LLA_DT_BF16) return false;
   if (s->variant == LLA_2D) return lla::decode2d_mfma_supported(s->heads, s->d_head, s->r_k, s->r_v);
   return lla::decode_mfma_supported(s->heads, s->d_head, s->r_k, s->r_v, store_heads(s));
+}
+
+bool mq_path(const lla_store_t *s, int32_t n_q) {
+  return s->variant == LLA_PER_HEAD && n_q > 1 &&
+         lla::decode_mq_supported(s->d_head, s->r_k, s->r_v, store_heads(s), s->heads, n_q);
 }
 
 bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
@@ -132,7 +151,7 @@ lla_status_t decode_impl(const lla_store_t *st, int32_t want_variant, int32_t la
     const uint64_t slab = (uint64_t)st->max_ctx * store_heads(st) * (st->r_k + st->r_v) * 2;
     if (slab >= (1ull << 31)) return LLA_E_UNSUPPORTED;
   }
-  const int32_t S = n_splits ? n_splits : auto_splits(st, mfma);
+  const int32_t S = n_splits ? n_splits : auto_splits(st, mfma, inflight ? n_q : 1);
   if (inflight) {  // the in-flight merge keeps every query's rows in LDS (160 KB)
     const size_t lds = 4 * ((size_t)2 * n_q * st->d_head + (size_t)n_q * n_q +
                             (size_t)n_q * st->r_v + 2 * (size_t)n_q + (size_t)n_q * S);
@@ -176,8 +195,7 @@ lla_status_t decode_impl(const lla_store_t *st, int32_t want_variant, int32_t la
 
   const bool is2d = st->variant == LLA_2D;
   p.write_out = (mfma && !is2d && S == 1 && !inflight) ? 1 : 0;
-  const bool mq = mfma && !is2d && inflight && n_q > 1 &&
-                  lla::decode_mq_supported(st->d_head, st->r_k, st->r_v, p.Hs, p.H, n_q);
+  const bool mq = mfma && inflight && mq_path(st, n_q);
   hipError_t he = !mfma ? lla::launch_decode_valu(p, st->dtype, stream)
                   : is2d ? lla::launch_decode2d_mfma(p, stream)
                   : mq   ? lla::launch_decode_mq(p, stream)
@@ -276,14 +294,10 @@ size_t kv_elems(const lla_kv_cache_t *c) {
 }
 
 int32_t kv_auto_splits(const lla_kv_cache_t *c) {
-  // about four workgroups per CU, each split at least 128 slots long
+  // one round of one workgroup per CU, each split at least 128 slots long
   const int32_t hg = lla::kv_heads_per_group(c->d_head, c->dtype);
   const int64_t per_split = (int64_t)c->batch * ((c->heads + hg - 1) / hg);
-  int64_t S = (1024 + per_split - 1) / per_split;
-  const int64_t max_s = std::max<int64_t>(1, c->max_ctx / 128);
-  if (S > max_s) S = max_s;
-  if (S < 1) S = 1;
-  return (int32_t)S;
+  return fill_rounds(per_split, 256, std::max<int64_t>(1, c->max_ctx / 128));
 }
 
 lla::KvParams kv_params(const lla_kv_cache_t *c, int32_t layer, int32_t cache_loop,
@@ -442,8 +456,8 @@ lla_status_t lla2d_decode_attn(const lla_store_t *store, int32_t layer, int32_t 
 }
 
 size_t lla_decode_inflight_workspace_bytes(const lla_store_t *s, int32_t n_q, int32_t n_splits) {
-  if (n_q < 1) return 0;
-  size_t n = lla_decode_workspace_bytes(s, n_splits);
+  if (n_q < 1 || lla_store_check(s) != LLA_OK) return 0;
+  size_t n = lla_decode_workspace_bytes(s, n_splits ? n_splits : auto_splits(s, use_mfma(s), n_q));
   if (!mul_ok(n, (size_t)n_q, &n)) return 0;
   return n;
 }
