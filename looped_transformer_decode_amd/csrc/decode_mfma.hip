@@ -257,8 +257,10 @@ __global__ __launch_bounds__(NW * 64, 1) void decode_mfma_split(DecodeParams p) 
     for (int r = 0; r < RV; ++r) acc[pp][r] = 0.f;
   }
 
-  // Issue order: iteration it issues phi(it+1), then store(it+NS-1).  The
-  // prologue replays the issues of the iterations before 0.
+  // Issue order: iteration it issues phi(it+1), then store(it+NS-1), right
+  // after the barrier that shows every wave is done with tile it-1 (whose
+  // buffers they reuse).  The prologue issues the stores before tile NS-1
+  // and phi(0), in the order the iterations would have.
   for (int k = 0; k + 2 < C::NS; ++k)
     if (k < ntiles) issue_store(k);
   issue_phi(0);
@@ -267,19 +269,13 @@ __global__ __launch_bounds__(NW * 64, 1) void decode_mfma_split(DecodeParams p) 
   const int tj = lane & 31;
   const int swz = tj & 7;
   for (int it = 0; it < ntiles; ++it) {
+    // Wait for store(it) and phi(it): what was issued after phi(it) may stay
+    // outstanding (loads complete in issue order): store(it+NS-2), issued
+    // right after it.
+    wait_vm(it + C::NS - 2 < ntiles && C::NS >= 3 ? C::LS : 0);
+    __builtin_amdgcn_s_barrier();
     if (it + 1 < ntiles) issue_phi(it + 1);
     if (it + C::NS - 1 < ntiles) issue_store(it + C::NS - 1);
-    // Wait for store(it) and phi(it): count what was issued after the later
-    // of the two (loads complete in issue order).
-    int after = 0;
-    if (C::NS >= 3) {
-      after = (it + C::NS - 2 < ntiles ? C::LS : 0) + (it + 1 < ntiles ? C::LP : 0) +
-              (it + C::NS - 1 < ntiles ? C::LS : 0);
-    } else {
-      after = (it + 1 < ntiles ? C::LP + C::LS : 0);
-    }
-    wait_vm(after);
-    __builtin_amdgcn_s_barrier();
 
     const char *sb = lds + (it % C::NS) * C::TILE_BYTES;
     const char *phb = lds + C::PHI_OFF + (it & 1) * kPhiTileBytes;
@@ -347,11 +343,11 @@ __global__ __launch_bounds__(NW * 64, 1) void decode_mfma_split(DecodeParams p) 
         }
       }
     }
-    __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
-    __builtin_amdgcn_s_barrier();
   }
 
   // ---- combine the 32 lane states of every head and write the partial ----
+  __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
+  __syncthreads();  // every wave is done reading the last tile's buffers
   float *red = reinterpret_cast<float *>(lds);  // [NW][PAIRS][64][RV + 2]
 #pragma unroll
   for (int pp = 0; pp < C::PAIRS; ++pp) {
