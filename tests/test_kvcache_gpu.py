@@ -56,6 +56,7 @@ FILL_CASES = [
     ("bf16_b32_ctx4k", dict(B=2, D=2, N=100, H=2, d=64), 10, 90),      # d = 64 (2 waves)
     ("bf16_b32_ctx4k", dict(B=1, D=2, N=70, H=2, d=256, r_k=16, r_v=32), 0, 70),  # d = 256
     ("bf16_b32_ctx4k", dict(B=2, D=1, N=90, H=2, r_k=8, r_v=24), 20, 50),  # ranks off 16
+    ("extreme_batch_b768_ctx4k", dict(B=2, D=1, N=1), 0, 1),            # a single slot
 ]
 
 
@@ -134,6 +135,7 @@ DECODE_CASES = [
     ("bf16", 2, 1, 1, 257, 20, 64, 1),
     ("bf16", 2, 1, 1, 200, 4, 256, 3),
     ("bf16", 2, 1, 1, 96, 2, 32, 96),           # one split per slot
+    ("bf16", 3, 1, 1, 1, 16, 128, 0),           # a single slot
 ]
 
 
@@ -143,7 +145,7 @@ def test_decode(device, dtype, B, D, Lp, N, H, d, S):
     rng = np.random.default_rng(B * 1000 + N)
     layer, cl = D - 1, Lp - 1
     exact = gen.as_storage(rng.standard_normal((B, N, H, 2, d)), dtype)[1]
-    pos = np.array([N - 1, 0, 1, N // 2][:B], np.int32)
+    pos = np.minimum(np.array([N - 1, 0, 1, N // 2][:B], np.int32), N - 1)
     # slots past each query hold values that would dominate any unmasked score
     for b in range(B):
         exact[b, pos[b] + 1:] = 24.0

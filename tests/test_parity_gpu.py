@@ -530,3 +530,38 @@ def test_device_fill_matches_host_generator(device):
     fill_hash_normal(t32, key, first=5, scale=0.1)
     want32 = (gen.hash_normal(key, 5, 4097).astype(np.float32) * np.float32(0.1))
     assert np.array_equal(t32.cpu().numpy(), want32)
+
+
+# ------------------------------------------------------------ degenerate sizes
+@pytest.mark.parametrize("tmpl,kw", [
+    ("extreme_batch_b768_ctx4k", dict(B=2, D=1, N=1)),     # one slot: out = v_hat_0
+    ("extreme_batch_b768_ctx4k", dict(B=1, D=1, N=33)),    # one full tile + one slot
+    ("long_recurrence_t16_ctx8k", dict(B=1, D=1, N=1)),
+    ("lla2d_b256_ctx4k", dict(B=1, D=1, N=1)),
+    ("lla2d_b256_ctx4k", dict(B=2, D=1, N=33)),
+    ("tiny_fp32", dict(B=1, N=1)),
+], ids=["per_head_N1", "per_head_N33", "long_rec_N1", "lla2d_N1", "lla2d_N33", "fp32_N1"])
+def test_smallest_stores(device, tmpl, kw):
+    """Stores of one slot (the query attends only itself) and of one tile plus
+    one slot, at every query position, on the paths the shapes select."""
+    w = small(tmpl, **kw)
+    for p0 in sorted({0, w.N - 1, w.N // 2}):
+        got, ref, path = decode_case(w, w.D - 1, w.T - 1, np.full(w.B, p0), device)
+        err = row_rel_l2(got, ref).max()
+        say(f"  pos {p0} ({path}): max row rel L2 {err:.3e}")
+        assert err <= TOL[w.dtype]
+
+
+@pytest.mark.parametrize("tmpl,kw,n_q,pos0", [
+    ("long_recurrence_t16_ctx8k", dict(B=2, D=1, N=20, H=4), 16, [4, 0]),
+    ("extreme_batch_b768_ctx4k", dict(B=2, D=1, N=16), 16, [0, 0]),
+    ("lla2d_b256_ctx4k", dict(B=1, D=1, N=18), 16, [2]),
+], ids=["store_of_four", "empty_store", "lla2d_store_of_two"])
+def test_inflight_short_stores(device, tmpl, kw, n_q, pos0):
+    """In-flight tokens that fill the context up to its last slot, over
+    stores of a few slots or none."""
+    w = small(tmpl, **kw)
+    got, ref = inflight_case(w, n_q, np.array(pos0), device)
+    err = row_rel_l2(got, ref)
+    say(f"  max row rel L2 {err.max():.3e}")
+    assert err.max() <= TOL[w.dtype]
