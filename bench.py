@@ -42,6 +42,8 @@ sys.path.insert(0, ROOT)
 
 METRIC = "LLA decode-attn tokens/s at B=768, 4k ctx, ρ=21.3 + % of HBM roofline"
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
+# (r_k, r_v) pairs of the multi-query store pass (d = 128, at most 16 queries)
+MQ_RANKS = {(16, 32), (32, 64), (48, 80)}
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 matrix cores
 CSRC = os.path.join(ROOT, "looped_transformer_decode_amd", "csrc")
 # FETCH_SIZE / WRITE_SIZE of a plain 8 GB device copy (one dispatch) read 3,906,278 KiB
@@ -684,8 +686,11 @@ def main():
         roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                     "traffic": traffic_for_current_kernel(w),
-                    "kernel": ("decode_mfma_split + decode_merge_inflight (one "
-                               "lla_decode_attn_inflight call)") if args.inflight else
+                    "kernel": (("decode_mq_split" if path == "mfma" and 1 < nq <= 16 and w.d == 128
+                                and w.variant == "per_head" and (w.r_k, w.r_v) in MQ_RANKS
+                                else "decode split kernel")
+                               + " + decode_merge_inflight (one lla_decode_attn_inflight call)")
+                              if args.inflight else
                               ("decode_mfma_split (one lla_decode_attn call"
                                + (")" if splits == 1 and path == "mfma" else " + decode_merge)")),
                     "bytes_per_launch": bytes_call, "launch_us": round(call_ms.mean() * 1e3, 2)}

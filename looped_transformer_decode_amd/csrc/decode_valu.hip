@@ -17,6 +17,7 @@ namespace detail {
 
 constexpr int kThreads = 256;
 constexpr int kWaves = kThreads / 64;
+typedef __attribute__((__vector_size__(4 * sizeof(uint32_t)))) uint32_t u32x4_t;
 
 template <typename E, int RKM>
 __global__ __launch_bounds__(kThreads) void decode_valu_split(DecodeParams p) {
@@ -259,49 +260,113 @@ __global__ __launch_bounds__(256) void decode_merge_batched(DecodeParams p) {
 //   out = [e^(M_s - M) (W_up,v,t A + mu_v,t L_s) + sum_m e^(s_m - M) v_m]
 //         / [e^(M_s - M) L_s + sum_m e^(s_m - M)],
 //   s_m = scale * RoPE(q_i, pos0 + i) . RoPE(k_m, pos0 + m)   (log2 domain).
-// One block per (head, sequence); one thread per element of d.  Every
-// query's store partials are merged at once, W_up,v,t is applied to all
-// query averages in one pass over its row, and the exact in-flight term is
-// added per query.
-constexpr int kMaxQ = 32;  // in-flight queries per call
+// One block per (head, sequence).  Every query's store partials are merged
+// at once, and W_up,v,t is applied to the latent averages of kQGroup queries
+// per pass over its row: with R = blockDim / d whole rows of d threads,
+// thread t < R d owns output element t % d of query groups t / d, t / d + R,
+// ...
+//
+// The block's work is a chain of short phases, so its time is set by the
+// round trips to memory in that chain.  Every phase issues its global loads
+// in batches of kLoadBatch independent ones before using any, the latent
+// averages are stored query-minor (the queries of a group are one 32-byte
+// LDS read) with the query count padded to a whole group, and no loop over
+// queries or value components holds a branch that would split its LDS reads
+// into separate waits.  W_up,v,t of the head is copied to LDS when it fits,
+// rows padded to an odd number of dwords so that consecutive rows start in
+// different banks.
+constexpr int kMaxQ = 32;       // in-flight queries per call
+constexpr int kLoadBatch = 8;   // loads a thread issues before it waits
+constexpr int kQGroup = 8;      // queries per W_up,v,t pass
 
 template <typename E>
 __global__ __launch_bounds__(256) void decode_merge_inflight(DecodeParams p, const float *k_new,
                                                             const float *v_new) {
   const int h = blockIdx.x, b = blockIdx.y, t = threadIdx.x, nt = blockDim.x;
   const int d = p.d, half = d / 2, rv = p.rv, S = p.S, nq = p.qps, H = p.H;
+  const InflightMergeLds lay = inflight_merge_lds(nq, d, rv, S, (int)sizeof(E));
+  const int nqp = lay.nq_pad;
   extern __shared__ float sm[];
   float *kr = sm;                 // [nq][d]  rotated in-flight keys, then their values
   float *qr = kr + nq * d;        // [nq][d]  rotated, scaled queries
   float *sc = qr + nq * d;        // [nq][nq] in-flight scores (m <= i)
-  float *abar = sc + nq * nq;     // [nq][rv] store latent numerators
-  float *st = abar + nq * rv;     // [nq][2]  store M, L; then [nq][S] split weights
+  float *abar = sc + nq * nq;     // [rv][nqp] store latent numerators, query-minor
+  float *st = abar + rv * nqp;    // [nq][2]  store M, L
+  float *wsp = st + 2 * nq;       // [nq][S]  split weights
+  uint32_t *wl = reinterpret_cast<uint32_t *>(sm + lay.w_off);  // [d][lay.w_pitch] dwords
   const int first = min(max(p.pos[b], 0), p.N);
   const bool act = t < d;
 
-  // rotate-half RoPE of element t of x at position pp
-  auto rot = [&](const float *x, int pp) -> float {
-    const float *cs = p.rope_f32 + (int64_t)min(pp, p.N - 1) * d;  // [d/2][2]
-    if (t < half) return x[t] * cs[2 * t] - x[t + half] * cs[2 * t + 1];
-    const int u = t - half;
-    return x[t] * cs[2 * u] + x[u] * cs[2 * u + 1];
-  };
-  if (act) {
-#pragma unroll 4
-    for (int m = 0; m < nq; ++m) {
-      const int64_t row = ((int64_t)(b * nq + m) * H + h) * d;
-      kr[m * d + t] = rot(k_new + row, first + m);
-      qr[m * d + t] = rot(p.q + row, first + m) * p.scale_log2;
+  // W_up,v,t of head h into LDS, 16-byte loads (used when its rows allow them)
+  const E *wg = reinterpret_cast<const E *>(p.wv) + (int64_t)h * d * rv;
+  const int row_bytes = rv * (int)sizeof(E);
+  const bool w_vec =
+      p.w_lds != 0 && row_bytes % 16 == 0 && (reinterpret_cast<uintptr_t>(wg) & 15) == 0;
+  if (w_vec) {
+    const u32x4_t *src = reinterpret_cast<const u32x4_t *>(wg);
+    const int rc = row_bytes / 16, n = d * rc;  // 16-byte chunks per row, in all
+    for (int c0 = t; c0 < n; c0 += kLoadBatch * nt) {
+      u32x4_t v[kLoadBatch];
+#pragma unroll
+      for (int u = 0; u < kLoadBatch; ++u) v[u] = src[min(c0 + u * nt, n - 1)];
+#pragma unroll
+      for (int u = 0; u < kLoadBatch; ++u) {
+        const int c = c0 + u * nt;
+        if (c < n) {
+          uint32_t *dst = wl + (c / rc) * lay.w_pitch + 4 * (c % rc);
+#pragma unroll
+          for (int w = 0; w < 4; ++w) dst[w] = v[u][w];
+        }
+      }
     }
   }
-  // store partials of every query, merged over the splits
-  // split weights 2^(m_s - M) of every query, then the numerators
-  float *wsp = st + 2 * nq;       // [nq][S]
+
+  // rotate-half RoPE of the in-flight keys and the queries at pos0 + m
+  if (act) {
+    const int u = t < half ? t : t - half;   // pair index
+    const int pt = t < half ? t + half : u;  // the other element of the pair
+    for (int m0 = 0; m0 < nq; m0 += kLoadBatch) {
+      float xk[kLoadBatch], yk[kLoadBatch], xq[kLoadBatch], yq[kLoadBatch], c[kLoadBatch],
+          s[kLoadBatch];
+#pragma unroll
+      for (int j = 0; j < kLoadBatch; ++j) {
+        const int m = min(m0 + j, nq - 1);
+        const int64_t row = ((int64_t)(b * nq + m) * H + h) * d;
+        const float *cs = p.rope_f32 + (int64_t)min(first + m, p.N - 1) * d;  // [d/2][2]
+        xk[j] = k_new[row + t];
+        yk[j] = k_new[row + pt];
+        xq[j] = p.q[row + t];
+        yq[j] = p.q[row + pt];
+        c[j] = cs[2 * u];
+        s[j] = cs[2 * u + 1];
+      }
+#pragma unroll
+      for (int j = 0; j < kLoadBatch; ++j) {
+        const int m = m0 + j;
+        if (m < nq) {
+          float rk, rq;
+          if (t < half) {
+            rk = xk[j] * c[j] - yk[j] * s[j];
+            rq = xq[j] * c[j] - yq[j] * s[j];
+          } else {
+            rk = xk[j] * c[j] + yk[j] * s[j];
+            rq = xq[j] * c[j] + yq[j] * s[j];
+          }
+          kr[m * d + t] = rk;
+          qr[m * d + t] = rq * p.scale_log2;
+        }
+      }
+    }
+  }
+  // store partials of every query, merged over the splits: split weights
+  // 2^(m_s - M) of every query, then the numerators
   for (int i = t; i < nq; i += nt) {
     const float *part = p.ws + (int64_t)((b * nq + i) * H + h) * S * (rv + 2);
     float M = -INFINITY;
+#pragma unroll 4
     for (int s2 = 0; s2 < S; ++s2) M = fmaxf(M, part[s2 * (rv + 2)]);
     float L = 0.f;
+#pragma unroll 4
     for (int s2 = 0; s2 < S; ++s2) {
       const float ms = part[s2 * (rv + 2)];
       const float w = ms == -INFINITY ? 0.f : exp2f(ms - M);
@@ -312,13 +377,29 @@ __global__ __launch_bounds__(256) void decode_merge_inflight(DecodeParams p, con
     st[2 * i + 1] = L;
   }
   __syncthreads();
-  for (int e = t; e < nq * rv; e += nt) {
-    const int i = e / rv, r = e % rv;
-    const float *part = p.ws + (int64_t)((b * nq + i) * H + h) * S * (rv + 2) + 2 + r;
-    float a = 0.f;
-#pragma unroll 4
-    for (int s2 = 0; s2 < S; ++s2) a = fmaf(part[s2 * (rv + 2)], wsp[i * S + s2], a);
-    abar[i * rv + r] = a;
+  const int na = nqp * rv;  // padded queries get zero numerators
+  for (int e0 = t; e0 < na; e0 += kLoadBatch * nt) {
+    float a[kLoadBatch];
+#pragma unroll
+    for (int u = 0; u < kLoadBatch; ++u) a[u] = 0.f;
+    for (int s2 = 0; s2 < S; ++s2) {
+      float v[kLoadBatch];
+#pragma unroll
+      for (int u = 0; u < kLoadBatch; ++u) {
+        const int e = min(e0 + u * nt, na - 1), i = min(e / rv, nq - 1), r = e % rv;
+        v[u] = p.ws[(int64_t)((b * nq + i) * H + h) * S * (rv + 2) + s2 * (rv + 2) + 2 + r];
+      }
+#pragma unroll
+      for (int u = 0; u < kLoadBatch; ++u) {
+        const int i = min(min(e0 + u * nt, na - 1) / rv, nq - 1);
+        a[u] = fmaf(v[u], wsp[i * S + s2], a[u]);
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < kLoadBatch; ++u) {
+      const int e = e0 + u * nt, i = e / rv, r = e % rv;
+      if (e < na) abar[r * nqp + i] = i < nq ? a[u] : 0.f;
+    }
   }
   __syncthreads();
   // scores s[i][m], m <= i: one thread per pair, the element order rotated
@@ -328,51 +409,66 @@ __global__ __launch_bounds__(256) void decode_merge_inflight(DecodeParams p, con
     if (m > i) continue;
     float v = 0.f;
     const int e0 = pr % d;
-    for (int k = 0; k < d; ++k) {
-      const int e = (e0 + k) % d;
-      v = fmaf(qr[i * d + e], kr[m * d + e], v);
-    }
+    const float *qi = qr + i * d, *km = kr + m * d;
+    for (int e = e0; e < d; ++e) v = fmaf(qi[e], km[e], v);
+    for (int e = 0; e < e0; ++e) v = fmaf(qi[e], km[e], v);
     sc[i * nq + m] = v;
   }
   __syncthreads();
-  if (act)  // the keys are done with: stage the in-flight values instead
-    for (int m = 0; m < nq; ++m) kr[m * d + t] = v_new[((int64_t)(b * nq + m) * H + h) * d + t];
-  // W_up,v,t row t against every query's latent average
-  float wa[kMaxQ];
-#pragma unroll
-  for (int i = 0; i < kMaxQ; ++i) wa[i] = 0.f;
+  // the keys are done with: stage the in-flight values instead
   if (act) {
-    const E *wrow = reinterpret_cast<const E *>(p.wv) + ((int64_t)h * d + t) * rv;
-    for (int r0 = 0; r0 < rv; r0 += 8) {
-      float w[8];
+    for (int m0 = 0; m0 < nq; m0 += kLoadBatch) {
+      float v[kLoadBatch];
 #pragma unroll
-      for (int e = 0; e < 8; ++e) w[e] = r0 + e < rv ? load_elem(wrow, r0 + e) : 0.f;
+      for (int j = 0; j < kLoadBatch; ++j)
+        v[j] = v_new[((int64_t)(b * nq + min(m0 + j, nq - 1)) * H + h) * d + t];
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        if (r0 + e >= rv) break;
-#pragma unroll
-        for (int i = 0; i < kMaxQ; ++i)
-          if (i < nq) wa[i] = fmaf(w[e], abar[i * rv + r0 + e], wa[i]);
-      }
+      for (int j = 0; j < kLoadBatch; ++j)
+        if (m0 + j < nq) kr[(m0 + j) * d + t] = v[j];
     }
   }
   __syncthreads();
-  if (!act) return;
-  const float mu = p.muv[(int64_t)h * d + t];
+
+  // W_up,v,t row `el` against the latent averages of a group of queries,
+  // then the in-flight term of each query of the group
+  const int rows = nt / d;  // whole rows of d threads; the rest sit this out
+  if (t >= rows * d) return;
+  const int el = t % d;
+  const uint32_t *wrow = wl + el * lay.w_pitch;
+  const E *wgrow = wg + (int64_t)el * rv;
+  const float mu = p.muv[(int64_t)h * d + el];
+  for (int i0 = (t / d) * kQGroup; i0 < nq; i0 += rows * kQGroup) {
+    float wa[kQGroup];
 #pragma unroll
-  for (int i = 0; i < kMaxQ; ++i) {
-    if (i >= nq) break;
-    const float Ms = st[2 * i], Ls = st[2 * i + 1];
-    float M = Ms;
-    for (int m = 0; m <= i; ++m) M = fmaxf(M, sc[i * nq + m]);
-    const float fs = (Ms == -INFINITY) ? 0.f : exp2f(Ms - M);
-    float num = fs * fmaf(mu, Ls, wa[i]), den = fs * Ls;
-    for (int m = 0; m <= i; ++m) {
-      const float e = exp2f(sc[i * nq + m] - M);
-      den += e;
-      num = fmaf(e, kr[m * d + t], num);
+    for (int j = 0; j < kQGroup; ++j) wa[j] = 0.f;
+    for (int r = 0; r < rv; ++r) {
+      float w;
+      if (!w_vec)
+        w = load_elem(wgrow, r);
+      else if (sizeof(E) == 4)
+        w = __uint_as_float(wrow[r]);
+      else
+        w = (r & 1) ? bf16_hi(wrow[r >> 1]) : bf16_lo(wrow[r >> 1]);
+      const float *ar = abar + r * nqp + i0;
+#pragma unroll
+      for (int j = 0; j < kQGroup; ++j) wa[j] = fmaf(w, ar[j], wa[j]);
     }
-    p.out[((int64_t)(b * nq + i) * H + h) * d + t] = num / den;
+#pragma unroll
+    for (int j = 0; j < kQGroup; ++j) {
+      const int i = i0 + j;
+      if (i >= nq) break;
+      const float Ms = st[2 * i], Ls = st[2 * i + 1];
+      float M = Ms;
+      for (int m = 0; m <= i; ++m) M = fmaxf(M, sc[i * nq + m]);
+      const float fs = (Ms == -INFINITY) ? 0.f : exp2f(Ms - M);
+      float num = fs * fmaf(mu, Ls, wa[j]), den = fs * Ls;
+      for (int m = 0; m <= i; ++m) {
+        const float e = exp2f(sc[i * nq + m] - M);
+        den += e;
+        num = fmaf(e, kr[m * d + el], num);
+      }
+      p.out[((int64_t)(b * nq + i) * H + h) * d + el] = num / den;
+    }
   }
 }
 
@@ -414,20 +510,23 @@ hipError_t launch_decode_merge_batched(const DecodeParams &p, int dtype, hipStre
 hipError_t launch_decode_merge_inflight(const DecodeParams &p, int32_t B_real, const float *k_new,
                                         const float *v_new, int dtype, hipStream_t st) {
   if (p.qps > kMaxQ) return hipErrorInvalidValue;
-  const int threads = 256 > p.d ? 256 : (p.d + 63) / 64 * 64;
-  const size_t sm = sizeof(float) * ((size_t)2 * p.qps * p.d + (size_t)p.qps * p.qps +
-                                     (size_t)p.qps * p.rv + 2 * (size_t)p.qps +
-                                     (size_t)p.qps * p.S);
-  if (sm > 160 * 1024) return hipErrorInvalidValue;
+  if (p.d < 1 || p.d > 256) return hipErrorInvalidValue;
+  const int threads = 256;
+  const int esize = dtype == LLA_DT_F32 ? 4 : 2;
+  const InflightMergeLds lay = inflight_merge_lds(p.qps, p.d, p.rv, p.S, esize);
+  DecodeParams q = p;
+  q.w_lds = lay.with_w <= kInflightMergeLdsMax ? 1 : 0;  // else W_up,v,t is read from HBM
+  const size_t sm = q.w_lds ? lay.with_w : lay.base;
+  if (sm > kInflightMergeLdsMax) return hipErrorInvalidValue;
   dim3 grid(p.H, B_real);
   const void *fn = dtype == LLA_DT_F32 ? reinterpret_cast<const void *>(decode_merge_inflight<float>)
                                        : reinterpret_cast<const void *>(decode_merge_inflight<bf16_t>);
   const hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)sm);
   if (e != hipSuccess) return e;
   if (dtype == LLA_DT_F32)
-    hipLaunchKernelGGL(decode_merge_inflight<float>, grid, dim3(threads), sm, st, p, k_new, v_new);
+    hipLaunchKernelGGL(decode_merge_inflight<float>, grid, dim3(threads), sm, st, q, k_new, v_new);
   else
-    hipLaunchKernelGGL(decode_merge_inflight<bf16_t>, grid, dim3(threads), sm, st, p, k_new, v_new);
+    hipLaunchKernelGGL(decode_merge_inflight<bf16_t>, grid, dim3(threads), sm, st, q, k_new, v_new);
   return hipGetLastError();
 }
 

@@ -153,9 +153,9 @@ lla_status_t decode_impl(const lla_store_t *st, int32_t want_variant, int32_t la
   }
   const int32_t S = n_splits ? n_splits : auto_splits(st, mfma, inflight ? n_q : 1);
   if (inflight) {  // the in-flight merge keeps every query's rows in LDS (160 KB)
-    const size_t lds = 4 * ((size_t)2 * n_q * st->d_head + (size_t)n_q * n_q +
-                            (size_t)n_q * st->r_v + 2 * (size_t)n_q + (size_t)n_q * S);
-    if (lds > 160 * 1024) return LLA_E_UNSUPPORTED;
+    const lla::InflightMergeLds lay = lla::inflight_merge_lds(
+        n_q, st->d_head, st->r_v, S, st->dtype == LLA_DT_F32 ? 4 : 2);
+    if (lay.base > lla::kInflightMergeLdsMax) return LLA_E_UNSUPPORTED;
   }
   size_t need = lla_decode_workspace_bytes(st, S);
   if (!mul_ok(need, (size_t)n_q, &need)) return LLA_E_OVERFLOW;

@@ -53,6 +53,7 @@ struct DecodeParams {
   int32_t qps;
   int32_t inflight;
   int32_t write_out;       // the split kernel applies W_up,v,t itself (one split)
+  int32_t w_lds;           // in-flight merge: W_up,v,t of the head staged in LDS
 };
 
 // Which store sequence a (virtual) query reads, its rotary position, and the
@@ -69,6 +70,32 @@ __device__ __forceinline__ QuerySlot query_slot(const DecodeParams &p, int32_t v
   }
   const int32_t q = min(max(base, 0), p.N - 1);
   return {b, q, q};
+}
+
+// LDS of the in-flight merge (floats unless noted): rotated keys and queries
+// [2][nq][d], in-flight scores [nq][nq], store numerators [rv][nq_pad] (query
+// count padded to whole groups of 8), M and L [nq][2], split weights [nq][S];
+// then, 16-byte aligned, W_up,v,t of the head as [d] rows of w_pitch dwords
+// (an odd count, so that consecutive rows start in different banks).
+// base: bytes without the W rows; with_w: bytes with them.
+struct InflightMergeLds {
+  int32_t nq_pad;
+  int32_t w_off;    // floats before the W rows
+  int32_t w_pitch;  // dwords per W row
+  size_t base, with_w;
+};
+constexpr size_t kInflightMergeLdsMax = 160 * 1024;
+__host__ __device__ inline InflightMergeLds inflight_merge_lds(int32_t nq, int32_t d, int32_t rv,
+                                                               int32_t S, int32_t esize) {
+  InflightMergeLds l;
+  l.nq_pad = (nq + 7) / 8 * 8;
+  const size_t f = (size_t)2 * nq * d + (size_t)nq * nq + (size_t)l.nq_pad * rv +
+                   2 * (size_t)nq + (size_t)nq * S;
+  l.base = 4 * f;
+  l.w_off = (int32_t)((f + 3) / 4 * 4);
+  l.w_pitch = ((rv * esize + 3) / 4) | 1;
+  l.with_w = 4 * ((size_t)l.w_off + (size_t)d * l.w_pitch);
+  return l;
 }
 
 struct EncodeParams {

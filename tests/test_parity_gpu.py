@@ -227,6 +227,8 @@ INFLIGHT_SHAPES = [
     ("bf16_b32_ctx4k", dict(B=2, D=1, N=260, H=6), 7),                # heads not a multiple of 4
     ("tiny_fp32", dict(B=3, N=128), 3),                              # generic fp32 path
     ("lla2d_b256_ctx4k", dict(B=2, D=1, N=170), 4),                  # LLA-2D fast path
+    ("tiny_fp32", dict(B=2, N=128, d=96), 5),                        # d not dividing the block
+    ("bf16_b32_ctx4k", dict(B=2, D=1, N=200, H=2), 32),              # most queries: 4 groups of 8
 ]
 
 
