@@ -30,10 +30,10 @@
 //    the weights rounded to bf16 and published in LDS.
 //  * P C_v on v_mfma_f32_16x16x32_bf16: wave w owns value columns
 //    16w..16w+15 of all heads (rows = heads, K = 32 slots).
-// The three stages run as a software pipeline, tile it's scores with tile
-// it-1's softmax and tile it-2's P C_v in one iteration, and the two waves
-// of a SIMD take them in opposite orders so that matrix and vector work
-// overlap.
+// The three stages run as a software pipeline: one iteration computes the
+// scores of tile it, the softmax of tile it-1 and P C_v of tile it-2, and
+// the two waves of a SIMD take them in opposite orders so that matrix and
+// vector work overlap.
 // G is formed once per workgroup in LDS (32 latent components of every head
 // at a time, transposed so that d is contiguous) and each lane then loads
 // its 16-byte A fragments.
@@ -62,6 +62,9 @@ constexpr int kPhiTileBytes = kTile * kD * 2;
 constexpr int kLdsMax = 160 * 1024;
 constexpr float kRescaleGap = 8.0f;
 constexpr int kPPitch = 40;  // bf16 elements per head row of the P tile (80 B: bank spread)
+// Store loads are nontemporal (nt): each latent is read once per call, the
+// phi rows (default policy) by every workgroup.
+constexpr int kCachePolicyStream = 2;
 
 template <int RK, int RV>
 struct Cfg {
@@ -285,7 +288,8 @@ __global__ __launch_bounds__(512, 1) void decode2d_split(DecodeParams p) {
     for (int u = 0; u < C::LW_MAX; ++u)
       if (u < LW)
         __builtin_amdgcn_raw_ptr_buffer_load_lds(
-            rs, (LDS_AS void *)(sb + (wave + u * NW) * 1024), 16, voff[u] + toff, 0, 0, 0);
+            rs, (LDS_AS void *)(sb + (wave + u * NW) * 1024), 16, voff[u] + toff, 0, 0,
+            kCachePolicyStream);
   };
   // phi tile (8 KB = 8 wave loads): wave w loads blocks w + NW u
   auto issue_phi = [&](int t) {
