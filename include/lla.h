@@ -52,7 +52,8 @@ typedef enum {
   LLA_E_UNSUPPORTED = 6, /* valid request that no kernel here implements    */
   LLA_E_VARIANT = 7,     /* per-head call on an LLA-2D store or vice versa   */
   LLA_E_HIP = 8,         /* a HIP runtime call or kernel launch failed       */
-  LLA_E_OVERFLOW = 9     /* a byte count does not fit in size_t / int64      */
+  LLA_E_OVERFLOW = 9     /* a size does not fit (bytes in size_t / int64, or  */
+                         /* batch x queries x heads in int32)                */
 } lla_status_t;
 
 typedef enum { LLA_DT_F32 = 0, LLA_DT_BF16 = 1 } lla_dtype_t;

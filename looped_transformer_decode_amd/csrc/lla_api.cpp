@@ -136,7 +136,8 @@ lla_status_t decode_impl(const lla_store_t *st, int32_t want_variant, int32_t la
   if (n_q < 1) return LLA_E_RANGE;
   if (n_q > kMaxInflight || (!inflight && n_q != 1)) return LLA_E_UNSUPPORTED;
   if (inflight && st->d_head > 256) return LLA_E_UNSUPPORTED;
-  if ((int64_t)st->batch * n_q > INT32_MAX) return LLA_E_OVERFLOW;
+  // (query, head) row indices are 32-bit in the kernels
+  if ((int64_t)st->batch * n_q * st->heads > INT32_MAX) return LLA_E_OVERFLOW;
   if (layer < 0 || layer >= st->layers || loop < 0 || loop >= st->loops) return LLA_E_RANGE;
   if (n_splits < 0 || n_splits > st->max_ctx) return LLA_E_RANGE;
   if (std::isnan(scale) || std::isinf(scale)) return LLA_E_RANGE;
@@ -599,6 +600,7 @@ lla_status_t lla_kv_decode_attn(const lla_kv_cache_t *c, int32_t layer, int32_t 
   const int32_t S = n_splits ? n_splits : kv_auto_splits(c);
   const int32_t hg = lla::kv_heads_per_group(c->d_head, c->dtype);
   if ((int64_t)c->batch * ((c->heads + hg - 1) / hg) * S > INT32_MAX) return LLA_E_OVERFLOW;
+  if ((int64_t)c->batch * c->heads > INT32_MAX) return LLA_E_OVERFLOW;  // 32-bit (b, h) rows
   const size_t need = lla_kv_decode_workspace_bytes(c, S);
   if (!workspace) return LLA_E_WORKSPACE;
   if (need == 0 || ws_bytes < need) return LLA_E_WORKSPACE;

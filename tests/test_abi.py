@@ -187,6 +187,10 @@ def test_launching_calls_validate_first(fn):
         assert call(good, scale=float("nan")) == 4
         assert call(good, scale=float("inf")) == 4
         assert f(None, 0, 0, *(P,) * 7, 0.0, P, P, 1 << 30, 0, None) == 1
+        # batch x heads beyond the kernels' 32-bit (query, head) rows
+        wide = L.LatentStore("per_head" if fn == "decode" else "2d", "bf16", batch=1 << 17,
+                             layers=1, max_ctx=1, heads=1 << 15, d_head=2, loops=1, r_k=2, r_v=2)
+        assert call(wide) == 9
     else:
         f = lib.lla_encode_append if fn == "encode" else lib.lla2d_encode_append
         good, other = (ph, d2) if fn == "encode" else (d2, ph)
@@ -291,6 +295,9 @@ def test_kv_calls_validate_first():
     odd = L.KvCache("bf16", batch=2, layers=3, loops=4, max_ctx=64, heads=16, d_head=40)
     assert dec(cache=odd) == 6
     assert lib.lla_kv_decode_attn(None, 0, 0, P, P, P, 0.0, P, P, 1 << 30, 0, None) == 1
+    wide = L.KvCache("bf16", batch=1 << 17, layers=1, loops=1, max_ctx=1, heads=1 << 15,
+                     d_head=128)
+    assert dec(cache=wide, n_splits=1) == 9   # 32-bit (b, h) rows
 
     def fill(store=s, cache=c, layer=0, slot0=0, n=8, cl=0, ptrs=(P,) * 4, rope=P, data=True):
         sd, cd = store.desc(), cache.desc()
