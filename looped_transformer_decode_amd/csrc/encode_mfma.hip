@@ -12,8 +12,8 @@
 //
 // Work split.  A workgroup of four waves owns (row block, stored head, axis,
 // column group); each wave owns MT tiles of 16 rows (rows = (sequence, new
-// token)).  With few row blocks (LLA-2D, small batches) a column group is
-// one 16-column tile, so that W_down is spread over many workgroups.  The
+// token)).  With few row blocks (LLA-2D, small batches) the variant at the
+// end of this file splits the contraction over the waves instead.  The
 // stacked length K is walked in chunks of 128.  Rows of x stream from HBM
 // straight into registers: within a chunk, lane group g = lane/16 reads 64
 // contiguous bytes of its row, and the contraction index is permuted
@@ -260,6 +260,164 @@ hipError_t launch(const EncodeParams &p, hipStream_t st) {
   return hipGetLastError();
 }
 
+// ---- few row blocks: the contraction split over the waves ----
+// With few row blocks (LLA-2D, small batches) a workgroup of the kernel
+// above walks all K / 128 chunks one after another, and that chain of load
+// round trips sets its time.  Here a workgroup owns one tile of 16 rows and
+// one 16-column tile; wave w of kSkWaves takes chunks w, w + kSkWaves, ...,
+// stages each W_down chunk (transposed) and its mu parts in LDS of its own,
+// keeps its own partial products, and the partials are summed through LDS at
+// the end.  Each wave's chain is kSkWaves times shorter.  (Eight waves
+// measured 7% faster than four at the LLA-2D shape; what remains is the
+// re-reading of x by every column tile and of W_down by every row tile.)
+constexpr int kSkWaves = 8;
+constexpr int kSkStages = 3;  // chunks of x / W_down / mu a wave has in flight
+
+__host__ __device__ constexpr size_t encode_sk_wave_lds() {
+  return 2 * 16 * kPitch * 2    // W_down chunk, transposed, two buffers
+         + 2 * 3 * kKc * 2;     // hi / mid / lo parts of the mu chunk, two buffers
+}
+
+__global__ __launch_bounds__(64 * kSkWaves) void encode_mfma_splitk(EncodeParams p, int gk) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  extern __shared__ __attribute__((aligned(16))) char lds[];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int g = lane >> 4, rr = lane & 15;
+  const int z = blockIdx.z, axis = z < gk ? 0 : 1;
+  const int col0 = (axis ? z - gk : z) * 16;
+  const int hs = blockIdx.y;
+  const int M = p.B * p.n_new, K = p.K, nc = K / kKc;
+  const int rfull = axis ? p.rv : p.rk;
+  const int row = min((int)blockIdx.x * 16 + rr, M - 1);  // rows past M: read, never stored
+  const u32x4_t *xrow = reinterpret_cast<const u32x4_t *>(
+                            reinterpret_cast<const uint16_t *>(p.x[axis]) +
+                            ((int64_t)row * p.Hs + hs) * K) + 4 * g;
+  const uint16_t *wd =
+      reinterpret_cast<const uint16_t *>(p.wd[axis]) + (int64_t)hs * K * rfull + col0;
+  const float *mu = p.mu[axis] + (int64_t)hs * K;
+  uint16_t *wt = reinterpret_cast<uint16_t *>(lds + wave * encode_sk_wave_lds());  // [2][16][kPitch]
+  uint16_t *mus = wt + 2 * 16 * kPitch;                                          // [2][3][kKc]
+
+  // this wave's chunks: c = wave + kSkWaves i, i < nw
+  const int nw = nc > wave ? (nc - wave + kSkWaves - 1) / kSkWaves : 0;
+  f32x4_t acc = {0.f, 0.f, 0.f, 0.f}, accb = {0.f, 0.f, 0.f, 0.f};
+  if (nw > 0) {  // wave-uniform
+    // Stage s holds chunk i: the 64 bytes of x this lane multiplies (row rr,
+    // k = 32 g + 8 q + e), W_down rows 2 lane and 2 lane + 1 of the 16
+    // columns, and mu at k = 2 lane, 2 lane + 1.  Past the wave's last chunk
+    // the loads repeat it (no branch around a load).
+    u32x4_t xs[kSkStages][4], ws[kSkStages][4];
+    float2 ms[kSkStages];
+    auto fetch = [&](int i, int st) {
+      const int c = wave + kSkWaves * min(i, nw - 1);
+#pragma unroll
+      for (int q = 0; q < 4; ++q) xs[st][q] = xrow[c * 16 + q];
+      const u32x4_t *src =
+          reinterpret_cast<const u32x4_t *>(wd + (int64_t)(c * kKc + 2 * lane) * rfull);
+      ws[st][0] = src[0];
+      ws[st][1] = src[1];
+      ws[st][2] = src[rfull / 8];
+      ws[st][3] = src[rfull / 8 + 1];
+      ms[st] = *reinterpret_cast<const float2 *>(mu + c * kKc + 2 * lane);
+    };
+    auto stage_lds = [&](int buf, int st) {  // W_down transposed ([column][k]) and mu parts
+      uint16_t *w = wt + buf * 16 * kPitch;
+#pragma unroll
+      for (int n = 0; n < 16; ++n) {
+        const int sh = (n & 1) * 16;
+        const uint32_t lo = (ws[st][n / 8][(n % 8) / 2] >> sh) & 0xFFFFu;
+        const uint32_t hi = (ws[st][2 + n / 8][(n % 8) / 2] >> sh) & 0xFFFFu;
+        *reinterpret_cast<uint32_t *>(w + n * kPitch + 2 * lane) = lo | (hi << 16);
+      }
+#pragma unroll
+      for (int part = 0; part < 3; ++part)
+        *reinterpret_cast<uint32_t *>(mus + (buf * 3 + part) * kKc + 2 * lane) =
+            split3(ms[st].x, part) | ((uint32_t)split3(ms[st].y, part) << 16);
+    };
+    auto compute = [&](int buf, int st) {
+      const uint16_t *w = wt + buf * 16 * kPitch;
+      const uint16_t *mrow = mus + (buf * 3 + (rr < 3 ? rr : 0)) * kKc;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const u32x4_t mz = {0u, 0u, 0u, 0u};
+        const bf16x8_t amu =
+            as_bf16x8(rr < 3 ? *reinterpret_cast<const u32x4_t *>(mrow + 32 * g + 8 * q) : mz);
+        const bf16x8_t bw =
+            *reinterpret_cast<const bf16x8_t *>(w + rr * kPitch + 32 * g + 8 * q);
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(xs[st][q]), bw, acc, 0, 0, 0);
+        accb = __builtin_amdgcn_mfma_f32_16x16x32_bf16(amu, bw, accb, 0, 0, 0);
+      }
+    };
+    // every LDS region is the wave's own: a wave-level wait orders its
+    // writes before its reads, and LDS operations of one wave run in order
+    auto step = [&](int i, int st) {
+      stage_lds(i & 1, st);
+      __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
+      __builtin_amdgcn_wave_barrier();
+      compute(i & 1, st);
+      fetch(i + kSkStages, st);
+    };
+#pragma unroll
+    for (int st = 0; st < kSkStages; ++st) fetch(st, st);
+    // whole groups of kSkStages steps without a branch (a branch inside
+    // would leave the compiler's count of outstanding loads inexact and make
+    // it wait for all of them), then the remainder
+    const int full = nw / kSkStages * kSkStages;
+    for (int i0 = 0; i0 < full; i0 += kSkStages) {
+#pragma unroll
+      for (int j = 0; j < kSkStages; ++j) step(i0 + j, j);
+    }
+#pragma unroll
+    for (int j = 0; j + 1 < kSkStages; ++j)
+      if (full + j < nw) step(full + j, j);
+  }
+
+  // ---- sum the partials; c = x W - mu W, rounded once ----
+  __syncthreads();  // every wave is done with its staging buffers
+  float *red = reinterpret_cast<float *>(lds);   // [waves][64 lanes][4]
+  float *redb = red + kSkWaves * 64 * 4;         // [waves][16 columns]
+#pragma unroll
+  for (int i = 0; i < 4; ++i) red[(wave * 64 + lane) * 4 + i] = acc[i];
+  // mu W_down: rows 0..2 of the mu tile (hi, mid, lo parts) sit in lanes 0..15
+  if (g == 0) redb[wave * 16 + rr] = (accb[2] + accb[1]) + accb[0];
+  __syncthreads();
+  if (wave != 0) return;
+  float bias = 0.f;
+#pragma unroll
+  for (int w = 0; w < kSkWaves; ++w) bias += redb[w * 16 + rr];
+  uint16_t *st = reinterpret_cast<uint16_t *>(p.store);
+  const int koff = (axis ? p.rk : 0) + col0;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    float a = 0.f;
+#pragma unroll
+    for (int w = 0; w < kSkWaves; ++w) a += red[(w * 64 + lane) * 4 + i];
+    const int r = (int)blockIdx.x * 16 + 4 * g + i;
+    if (r >= M) continue;
+    const int b = r / p.n_new, jn = r % p.n_new;
+    const int slot = p.start[b] + jn;
+    if (slot < 0 || slot >= p.N) continue;
+    st[((((int64_t)b * p.D + p.layer) * p.N + slot) * p.Hs + hs) * p.R + koff + rr] =
+        f32_to_bf16_bits(a - bias);
+  }
+#endif
+}
+
+hipError_t launch_splitk(const EncodeParams &p, hipStream_t st) {
+  const int M = p.B * p.n_new;
+  const int gk = p.rk / 16, gv = p.rv / 16;
+  const size_t lds = kSkWaves * encode_sk_wave_lds();
+  static_assert(kSkWaves * encode_sk_wave_lds() >= kSkWaves * 64 * 4 * 4 + kSkWaves * 16 * 4,
+                "the partial sums reuse the staging LDS");
+  const void *fn = reinterpret_cast<const void *>(&encode_mfma_splitk);
+  const hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+  if (e != hipSuccess) return e;
+  const dim3 grid((M + 15) / 16, p.Hs, gk + gv);
+  hipLaunchKernelGGL(encode_mfma_splitk, grid, dim3(64 * kSkWaves), lds, st, p, gk);
+  return hipGetLastError();
+}
+
 }  // namespace detail
 
 using namespace detail;
@@ -275,10 +433,9 @@ hipError_t launch_encode_mfma(const EncodeParams &p, hipStream_t st) {
   const int M = p.B * p.n_new;
   const int k = p.rk / 16, v = p.rv / 16;
   const int64_t blocks1 = (int64_t)((M + 63) / 64) * p.Hs;  // workgroups per column group
-  // Few row blocks (small batch, LLA-2D): give each workgroup one 16-column
-  // tile so that W_down is split over more workgroups instead of being
-  // re-read whole by each of a handful of them.
-  if (blocks1 * 2 < 128) return launch<1, 1, 1>(p, st);
+  // Few row blocks (small batch, LLA-2D): one 16-row, 16-column tile per
+  // workgroup, the contraction split over its waves.
+  if (blocks1 * 2 < 128) return launch_splitk(p, st);
   // Two row tiles per wave when that still gives a full wave of workgroups
   // (only the smallest ranks: larger ones would spill at two waves per SIMD).
   const bool two = (int64_t)((M + 127) / 128) * p.Hs * 2 >= 256;
