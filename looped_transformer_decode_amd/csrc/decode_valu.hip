@@ -179,49 +179,136 @@ __global__ __launch_bounds__(256) void decode_merge(DecodeParams p) {
 // Merge for LLA-2D stores: the same log-sum-exp merge, batched over
 // sequences so that each W_up,v,t head block (d x r_v) is read once per
 // kBT sequences instead of once per sequence.  Block = (head, sequence
-// tile); one thread per output element of the head.
+// tile); one thread per output element of the head.  As in the in-flight
+// merge below, a block is a short chain of phases whose time is its number
+// of round trips to memory: W_up,v,t of the head is copied to LDS at the
+// start with batched 16-byte loads (rows padded to an odd number of dwords,
+// so that thread i reading row i hits its own bank), and the partials are
+// read in batches of kLoadBatch independent loads.
 constexpr int kBT = 8;
+static_assert(kBT == 8, "batched_merge_lds() sizes the LDS for tiles of 8 sequences");
+constexpr int kLoadBatch = 8;   // loads a thread issues before it waits
+
+// Copies the d x rv block of W_up,v,t at wg (16-byte aligned, rows of a
+// whole number of 16-byte chunks) into LDS rows of `pitch` dwords.
+template <typename E>
+__device__ __forceinline__ void w_rows_to_lds(const E *wg, int d, int rv, int pitch, uint32_t *wl,
+                                              int t, int nt) {
+  const u32x4_t *src = reinterpret_cast<const u32x4_t *>(wg);
+  const int rc = rv * (int)sizeof(E) / 16, n = d * rc;  // 16-byte chunks per row, in all
+  for (int c0 = t; c0 < n; c0 += kLoadBatch * nt) {
+    u32x4_t v[kLoadBatch];
+#pragma unroll
+    for (int u = 0; u < kLoadBatch; ++u) v[u] = src[min(c0 + u * nt, n - 1)];
+#pragma unroll
+    for (int u = 0; u < kLoadBatch; ++u) {
+      const int c = c0 + u * nt;
+      if (c < n) {
+        uint32_t *dst = wl + (c / rc) * pitch + 4 * (c % rc);
+#pragma unroll
+        for (int w = 0; w < 4; ++w) dst[w] = v[u][w];
+      }
+    }
+  }
+}
+
+// Element r of an LDS row written by w_rows_to_lds.
+template <typename E>
+__device__ __forceinline__ float w_lds_elem(const uint32_t *row, int r) {
+  if (sizeof(E) == 4) return __uint_as_float(row[r]);
+  return (r & 1) ? bf16_hi(row[r >> 1]) : bf16_lo(row[r >> 1]);
+}
 
 template <typename E>
 __global__ __launch_bounds__(256) void decode_merge_batched(DecodeParams p) {
-  const int h = blockIdx.x, b0 = blockIdx.y * kBT, tid = threadIdx.x;
+  const int h = blockIdx.x, b0 = blockIdx.y * kBT, tid = threadIdx.x, nt = blockDim.x;
   const int rv = p.rv, d = p.d, S = p.S;
-  extern __shared__ float abar[];  // [kBT][rv]
-  for (int t = tid; t < kBT * rv; t += blockDim.x) {
-    const int bl = t / rv, r = t % rv, b = b0 + bl;
+  const BatchedMergeLds lay = batched_merge_lds(d, rv, S, (int)sizeof(E));
+  extern __shared__ float sm[];
+  float *abar = sm;                  // [kBT][rv] merged latent averages
+  float *fs = abar + kBT * rv;       // [kBT][S] split weights
+  float *ls = fs + kBT * S;          // [kBT] merged softmax sums
+  uint32_t *wl = reinterpret_cast<uint32_t *>(sm + lay.w_off);  // [d][w_pitch] dwords
+  const E *wg = reinterpret_cast<const E *>(p.wv) + (int64_t)h * d * rv;
+  const bool w_vec = p.w_lds != 0 && (rv * (int)sizeof(E)) % 16 == 0 &&
+                     (reinterpret_cast<uintptr_t>(wg) & 15) == 0;
+  if (w_vec) w_rows_to_lds(wg, d, rv, lay.w_pitch, wl, tid, nt);
+
+  // split weights 2^(m_s - M) and merged sum L of every sequence of the tile
+  for (int bl = tid; bl < kBT; bl += nt) {
+    const int b = b0 + bl;
     if (b >= p.B) {
-      abar[t] = 0.f;
+      for (int s2 = 0; s2 < S; ++s2) fs[bl * S + s2] = 0.f;
+      ls[bl] = 1.f;
       continue;
     }
     const float *part = p.ws + (int64_t)(b * p.H + h) * S * (rv + 2);
     float M = -INFINITY;
-    for (int s = 0; s < S; ++s) M = fmaxf(M, part[s * (rv + 2)]);
-    float L = 0.f, A = 0.f;
-    for (int s = 0; s < S; ++s) {
-      const float *ps = part + s * (rv + 2);
-      if (ps[0] == -INFINITY) continue;
-      const float f = exp2f(ps[0] - M);
-      L = fmaf(ps[1], f, L);
-      A = fmaf(ps[2 + r], f, A);
+#pragma unroll 4
+    for (int s2 = 0; s2 < S; ++s2) M = fmaxf(M, part[s2 * (rv + 2)]);
+    float L = 0.f;
+#pragma unroll 4
+    for (int s2 = 0; s2 < S; ++s2) {
+      const float ms = part[s2 * (rv + 2)];
+      const float f = ms == -INFINITY ? 0.f : exp2f(ms - M);  // empty split: weight 0
+      fs[bl * S + s2] = f;
+      L = fmaf(part[s2 * (rv + 2) + 1], f, L);
     }
-    abar[t] = A / L;
+    ls[bl] = L;
+  }
+  __syncthreads();
+  // averages A / L; sequences past B get zeros
+  const int na = kBT * rv;
+  for (int e0 = tid; e0 < na; e0 += kLoadBatch * nt) {
+    float a[kLoadBatch];
+#pragma unroll
+    for (int u = 0; u < kLoadBatch; ++u) a[u] = 0.f;
+    for (int s2 = 0; s2 < S; ++s2) {
+      float v[kLoadBatch];
+#pragma unroll
+      for (int u = 0; u < kLoadBatch; ++u) {
+        const int e = min(e0 + u * nt, na - 1), b = min(b0 + e / rv, p.B - 1);
+        v[u] = p.ws[(int64_t)(b * p.H + h) * S * (rv + 2) + s2 * (rv + 2) + 2 + e % rv];
+      }
+#pragma unroll
+      for (int u = 0; u < kLoadBatch; ++u) {
+        const int e = min(e0 + u * nt, na - 1);
+        a[u] = fmaf(v[u], fs[(e / rv) * S + s2], a[u]);
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < kLoadBatch; ++u) {
+      const int e = e0 + u * nt;
+      if (e < na) abar[e] = b0 + e / rv < p.B ? a[u] / ls[e / rv] : 0.f;
+    }
   }
   __syncthreads();
   const bool vec = sizeof(E) == 2 && rv % 8 == 0 && ((uintptr_t)p.wv & 15u) == 0;
-  for (int i = tid; i < d; i += blockDim.x) {
+  for (int i = tid; i < d; i += nt) {
     float acc[kBT];
 #pragma unroll
     for (int bl = 0; bl < kBT; ++bl) acc[bl] = 0.f;
-    const E *w = reinterpret_cast<const E *>(p.wv) + ((int64_t)h * d + i) * rv;
-    if (vec) {
-      // 8 weights of the row per 16-byte load; the 8 matching averages of
-      // each sequence as two 16-byte LDS reads (the same address in every
-      // lane: a broadcast)
+    const E *w = wg + (int64_t)i * rv;
+    if (w_vec || vec) {
+      // 8 weights of the row at a time (LDS, else one 16-byte load); the 8
+      // matching averages of each sequence as two 16-byte LDS reads (the
+      // same address in every lane: a broadcast)
+      const uint32_t *wrow = wl + i * lay.w_pitch;
       const uint4 *w4 = reinterpret_cast<const uint4 *>(w);
       for (int r8 = 0; r8 < rv / 8; ++r8) {
-        const uint4 v = w4[r8];
-        const float wf[8] = {bf16_lo(v.x), bf16_hi(v.x), bf16_lo(v.y), bf16_hi(v.y),
-                             bf16_lo(v.z), bf16_hi(v.z), bf16_lo(v.w), bf16_hi(v.w)};
+        float wf[8];
+        if (w_vec) {
+#pragma unroll
+          for (int e = 0; e < 8; ++e) wf[e] = w_lds_elem<E>(wrow, 8 * r8 + e);
+        } else {
+          const uint4 v = w4[r8];
+          const uint32_t u[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            wf[2 * e] = bf16_lo(u[e]);
+            wf[2 * e + 1] = bf16_hi(u[e]);
+          }
+        }
 #pragma unroll
         for (int bl = 0; bl < kBT; ++bl) {
           const float4 a0 = *reinterpret_cast<const float4 *>(abar + bl * rv + 8 * r8);
@@ -276,7 +363,6 @@ __global__ __launch_bounds__(256) void decode_merge_batched(DecodeParams p) {
 // rows padded to an odd number of dwords so that consecutive rows start in
 // different banks.
 constexpr int kMaxQ = 32;       // in-flight queries per call
-constexpr int kLoadBatch = 8;   // loads a thread issues before it waits
 constexpr int kQGroup = 8;      // queries per W_up,v,t pass
 
 template <typename E>
@@ -302,24 +388,7 @@ __global__ __launch_bounds__(256) void decode_merge_inflight(DecodeParams p, con
   const int row_bytes = rv * (int)sizeof(E);
   const bool w_vec =
       p.w_lds != 0 && row_bytes % 16 == 0 && (reinterpret_cast<uintptr_t>(wg) & 15) == 0;
-  if (w_vec) {
-    const u32x4_t *src = reinterpret_cast<const u32x4_t *>(wg);
-    const int rc = row_bytes / 16, n = d * rc;  // 16-byte chunks per row, in all
-    for (int c0 = t; c0 < n; c0 += kLoadBatch * nt) {
-      u32x4_t v[kLoadBatch];
-#pragma unroll
-      for (int u = 0; u < kLoadBatch; ++u) v[u] = src[min(c0 + u * nt, n - 1)];
-#pragma unroll
-      for (int u = 0; u < kLoadBatch; ++u) {
-        const int c = c0 + u * nt;
-        if (c < n) {
-          uint32_t *dst = wl + (c / rc) * lay.w_pitch + 4 * (c % rc);
-#pragma unroll
-          for (int w = 0; w < 4; ++w) dst[w] = v[u][w];
-        }
-      }
-    }
-  }
+  if (w_vec) w_rows_to_lds(wg, d, rv, lay.w_pitch, wl, t, nt);
 
   // rotate-half RoPE of the in-flight keys and the queries at pos0 + m
   if (act) {
@@ -442,13 +511,7 @@ __global__ __launch_bounds__(256) void decode_merge_inflight(DecodeParams p, con
 #pragma unroll
     for (int j = 0; j < kQGroup; ++j) wa[j] = 0.f;
     for (int r = 0; r < rv; ++r) {
-      float w;
-      if (!w_vec)
-        w = load_elem(wgrow, r);
-      else if (sizeof(E) == 4)
-        w = __uint_as_float(wrow[r]);
-      else
-        w = (r & 1) ? bf16_hi(wrow[r >> 1]) : bf16_lo(wrow[r >> 1]);
+      const float w = w_vec ? w_lds_elem<E>(wrow, r) : load_elem(wgrow, r);
       const float *ar = abar + r * nqp + i0;
 #pragma unroll
       for (int j = 0; j < kQGroup; ++j) wa[j] = fmaf(w, ar[j], wa[j]);
@@ -499,11 +562,19 @@ hipError_t launch_decode_valu(const DecodeParams &p, int dtype, hipStream_t st) 
 hipError_t launch_decode_merge_batched(const DecodeParams &p, int dtype, hipStream_t st) {
   dim3 grid(p.H, (p.B + kBT - 1) / kBT);
   const int threads = p.d >= 256 ? 256 : (p.d + 63) / 64 * 64;
-  const size_t sm = sizeof(float) * p.rv * kBT;
+  const BatchedMergeLds lay = batched_merge_lds(p.d, p.rv, p.S, dtype == LLA_DT_F32 ? 4 : 2);
+  DecodeParams q = p;
+  q.w_lds = lay.with_w <= kBatchedMergeWLdsMax ? 1 : 0;  // else W_up,v,t is read from HBM
+  const size_t sm = q.w_lds ? lay.with_w : lay.base;
+  if (sm > 160 * 1024) return hipErrorInvalidValue;
+  const void *fn = dtype == LLA_DT_F32 ? reinterpret_cast<const void *>(decode_merge_batched<float>)
+                                       : reinterpret_cast<const void *>(decode_merge_batched<bf16_t>);
+  const hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)sm);
+  if (e != hipSuccess) return e;
   if (dtype == LLA_DT_F32)
-    hipLaunchKernelGGL(decode_merge_batched<float>, grid, dim3(threads), sm, st, p);
+    hipLaunchKernelGGL(decode_merge_batched<float>, grid, dim3(threads), sm, st, q);
   else
-    hipLaunchKernelGGL(decode_merge_batched<bf16_t>, grid, dim3(threads), sm, st, p);
+    hipLaunchKernelGGL(decode_merge_batched<bf16_t>, grid, dim3(threads), sm, st, q);
   return hipGetLastError();
 }
 

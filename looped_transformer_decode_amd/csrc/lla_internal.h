@@ -53,7 +53,7 @@ struct DecodeParams {
   int32_t qps;
   int32_t inflight;
   int32_t write_out;       // the split kernel applies W_up,v,t itself (one split)
-  int32_t w_lds;           // in-flight merge: W_up,v,t of the head staged in LDS
+  int32_t w_lds;           // merge kernels: W_up,v,t of the head staged in LDS
 };
 
 // Which store sequence a (virtual) query reads, its rotary position, and the
@@ -91,6 +91,27 @@ __host__ __device__ inline InflightMergeLds inflight_merge_lds(int32_t nq, int32
   l.nq_pad = (nq + 7) / 8 * 8;
   const size_t f = (size_t)2 * nq * d + (size_t)nq * nq + (size_t)l.nq_pad * rv +
                    2 * (size_t)nq + (size_t)nq * S;
+  l.base = 4 * f;
+  l.w_off = (int32_t)((f + 3) / 4 * 4);
+  l.w_pitch = ((rv * esize + 3) / 4) | 1;
+  l.with_w = 4 * ((size_t)l.w_off + (size_t)d * l.w_pitch);
+  return l;
+}
+
+// LDS of the LLA-2D merge (floats unless noted): merged averages [8][rv],
+// split weights [8][S], merged sums [8]; then, 16-byte aligned, W_up,v,t of
+// the head as [d] rows of w_pitch dwords (odd).  base: bytes without the W
+// rows; with_w: bytes with them (used up to kBatchedMergeWLdsMax).
+struct BatchedMergeLds {
+  int32_t w_off;    // floats before the W rows
+  int32_t w_pitch;  // dwords per W row
+  size_t base, with_w;
+};
+constexpr size_t kBatchedMergeWLdsMax = 64 * 1024;
+__host__ __device__ inline BatchedMergeLds batched_merge_lds(int32_t d, int32_t rv, int32_t S,
+                                                             int32_t esize) {
+  BatchedMergeLds l;
+  const size_t f = (size_t)8 * rv + (size_t)8 * S + 8;
   l.base = 4 * f;
   l.w_off = (int32_t)((f + 3) / 4 * 4);
   l.w_pitch = ((rv * esize + 3) / 4) | 1;
