@@ -32,6 +32,7 @@ import argparse
 import hashlib
 import json
 import os
+import re
 import sys
 import time
 
@@ -42,6 +43,10 @@ sys.path.insert(0, ROOT)
 
 METRIC = "LLA decode-attn tokens/s at B=768, 4k ctx, ρ=21.3 + % of HBM roofline"
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
+# Names of the decode split kernels whose counters the traffic summary reads
+# (the same expression goes to rocprofv3 --kernel-include-regex); the split-K
+# encode kernel is not one of them.
+SPLIT_KERNELS = r"decode\w*_split|kv_split"
 # (r_k, r_v) pairs of the multi-query store pass (d = 128, at most 16 queries)
 MQ_RANKS = {(16, 32), (32, 64), (48, 80)}
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 matrix cores
@@ -151,7 +156,7 @@ def summarize_counters(w, fetch_dir: str, write_dir: str, path: str = "lla") -> 
         vals = []
         for f in glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True):
             for r in csv.DictReader(open(f)):
-                if r["Counter_Name"] == counter and "split" in r["Kernel_Name"]:
+                if r["Counter_Name"] == counter and re.search(SPLIT_KERNELS, r["Kernel_Name"]):
                     vals.append(float(r["Counter_Value"]))
         if not vals:
             raise SystemExit(f"no {counter} rows for a split kernel under {d}")

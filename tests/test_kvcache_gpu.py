@@ -57,6 +57,7 @@ FILL_CASES = [
     ("bf16_b32_ctx4k", dict(B=1, D=2, N=70, H=2, d=256, r_k=16, r_v=32), 0, 70),  # d = 256
     ("bf16_b32_ctx4k", dict(B=2, D=1, N=90, H=2, r_k=8, r_v=24), 20, 50),  # ranks off 16
     ("extreme_batch_b768_ctx4k", dict(B=2, D=1, N=1), 0, 1),            # a single slot
+    ("bf16_b32_ctx4k", dict(B=2, D=1, N=90, H=2, r_k=32, r_v=160), 7, 80),  # 10 k-steps (widest instance)
 ]
 
 
