@@ -33,7 +33,8 @@
 // records of the head group are contiguous in HBM; tiles of 32 slots are
 // streamed with nontemporal buffer loads that write LDS directly (no VGPR
 // staging), three or two tiles deep, plus the matching 8 KB tile of bf16 phi
-// rows.
+// rows; where LDS allows, the first tiles are already streaming while G is
+// built.
 // 16-byte chunks are XOR-swizzled by (slot & 7) inside each slot record so
 // that the per-lane record reads (lanes = consecutive slots) hit distinct
 // LDS banks.  Buffer loads past the slab return zeros, so partial tiles
@@ -55,6 +56,11 @@ constexpr int kTile = 32;           // slots per tile (MFMA column count)
 constexpr int kPhiTileBytes = kTile * kD * 2;
 constexpr int kLdsMax = 160 * 1024;
 constexpr float kRescaleGap = 8.0f; // log2-domain headroom before rescaling
+// G^T rows in LDS: kD + 8 bf16 (272 bytes, so that consecutive rows start 16
+// bytes apart in bank space) and 32 more between heads, so that the two heads
+// a wave's 16-byte operand reads touch at once fall in different banks.
+constexpr int kGPitch = kD + 8;
+constexpr int kGHeadPad = 32;
 // Cache policy of the store loads: nontemporal (nt).  Every store byte is
 // read once per call; the hint keeps the stream from displacing the phi
 // rows and codec matrices that all workgroups share in L2 (measured: 5.96
@@ -87,11 +93,29 @@ struct Cfg {
   static_assert((kTile * CPT) % NT == 0 && (kPhiTileBytes / 16) % NT == 0, "load split");
   static_assert(NS >= 2, "two store stages must fit");
   static_assert(2 * LS + LP <= 63, "vmcnt range");
-  // LDS used before the pipeline starts: rotated queries + W_up,k,t of the group
-  static_assert(HG * kD * 4 + HG * kD * RK * 2 <= LDS_BYTES, "setup staging");
-  // LDS used by the final cross-lane reduction and the combined partials
-  static_assert((NW * PAIRS * 64 + HG) * (RV + 2) * 4 <= LDS_BYTES, "reduction staging");
+  // Setup staging: G^T of the group as bf16 rows of kGPitch elements, heads
+  // G_HEAD elements apart, then the g0 rows, then the rotated queries (fp32).
+  // When it fits between the first store stage and the phi buffers, the
+  // first store and phi tiles stream in while G is built (EARLY); otherwise
+  // it starts at 0 and the tiles are issued after it.
+  static constexpr int G_HEAD = RK * kGPitch + kGHeadPad;
+  static constexpr int SETUP_BYTES = (HG * G_HEAD + HG * kGPitch) * 2 + HG * kD * 4;
+  static constexpr bool EARLY = TILE_BYTES + SETUP_BYTES <= PHI_OFF;
+  static constexpr int SETUP_OFF = EARLY ? TILE_BYTES : 0;
+  static_assert(SETUP_OFF + SETUP_BYTES <= (EARLY ? PHI_OFF : LDS_BYTES), "setup staging");
+  // G blocks: (head, 8 k's, 8 i's of the first half) per item
+  static constexpr int ITEMS = HG * (RK / 8) * (kD / 16);
+  static constexpr int P1_PER_THREAD = (HG * (kD / 2) + NT - 1) / NT;  // (head, i < 64) pairs
+  static_assert(!EARLY || ITEMS <= NT, "EARLY: one G item per thread, loaded before the first tile");
+  // Final reduction: the 32 lanes' rescaled (l, acc) of every head, [HG][RV+1][32],
+  // the head maxima [HG], then the combined partials [HG][RV+2].
+  static constexpr int RED_FLOATS = HG * (RV + 1) * 32;
+  static_assert((RED_FLOATS + HG + HG * (RV + 2)) * 4 <= LDS_BYTES, "reduction staging");
   static_assert(RV % 8 == 0, "W_up,v,t rows are read as 16-byte vectors");
+  static constexpr int OUT_PER_THREAD = HG * kD / NT;  // W_up,v,t outputs per thread
+  static_assert(OUT_PER_THREAD * NT == HG * kD, "output split");
+  // W_up,v,t rows fetched before the final reduction when they fit in 64 VGPRs
+  static constexpr bool WV_AHEAD = OUT_PER_THREAD * (RV / 8) * 4 <= 64;
 };
 
 // Wait until at most n vector-memory operations are outstanding (0 <= n
@@ -142,81 +166,6 @@ __global__ __launch_bounds__(NW * 64, 1) void decode_mfma_split(DecodeParams p) 
   }
   const int ntiles = (t1 - t0 + kTile - 1) / kTile;
 
-  // ---- setup: rotated + scaled queries and W_up,k,t of the group in LDS ----
-  float *qr = reinterpret_cast<float *>(lds);                          // [HG][kD]
-  uint16_t *wl = reinterpret_cast<uint16_t *>(lds + C::HG * kD * 4);   // [HG][kD][RK]
-  {
-    const float *rq = p.rope_f32 + (int64_t)pos * kD;  // [kD/2][2] at pos
-    for (int i = tid; i < C::HG * (kD / 2); i += C::NT) {
-      const int hl = i / (kD / 2), ii = i % (kD / 2);
-      const float *qb = p.q + ((int64_t)vb * p.H + h0 + hl) * kD;
-      const float c = rq[2 * ii], sn = rq[2 * ii + 1];
-      const float a = qb[ii], bb = qb[ii + kD / 2];
-      qr[hl * kD + ii] = (a * c - bb * sn) * p.scale_log2;
-      qr[hl * kD + ii + kD / 2] = (a * sn + bb * c) * p.scale_log2;
-    }
-    const u32x4_t *wsrc =
-        reinterpret_cast<const u32x4_t *>(reinterpret_cast<const uint16_t *>(p.wk) +
-                                          (int64_t)h0 * kD * RK);
-    u32x4_t *wdst = reinterpret_cast<u32x4_t *>(wl);
-    for (int i = tid; i < C::HG * kD * RK / 8; i += C::NT) wdst[i] = wsrc[i];
-  }
-  __syncthreads();
-
-  // ---- A operands: G^T rows (per head pair) and the mu row block ----
-  const int row = lane & 31, khalf = lane >> 5;
-  bf16x8_t Ak[C::PAIRS][C::KT][kKSteps];
-  bf16x8_t Amu[kKSteps];
-#pragma unroll
-  for (int pp = 0; pp < C::PAIRS; ++pp) {
-#pragma unroll
-    for (int ti = 0; ti < C::KT; ++ti) {
-      const int hip = (row >> 2) & 1;
-      const int k = ti * 16 + ((row >> 3) << 2) + (row & 3);
-      const int hl = wave * HPW + 2 * pp + hip;
-      const float *qh = qr + hl * kD;
-      const uint16_t *wh = wl + hl * kD * RK;
-#pragma unroll
-      for (int st = 0; st < kKSteps; ++st) {
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const int i = 16 * st + 8 * khalf + e;
-          float gv;
-          if (i < kD / 2) {
-            gv = qh[i] * bf16_bits_to_f32(wh[i * RK + k]) +
-                 qh[i + kD / 2] * bf16_bits_to_f32(wh[(i + kD / 2) * RK + k]);
-          } else {
-            gv = qh[i] * bf16_bits_to_f32(wh[(i - kD / 2) * RK + k]) -
-                 qh[i - kD / 2] * bf16_bits_to_f32(wh[i * RK + k]);
-          }
-          Ak[pp][ti][st][e] = (short)f32_to_bf16_bits(gv);
-        }
-      }
-    }
-  }
-  {
-    // mu rows: row 8*pp + 4*hip (pp < PAIRS) carries head wave*HPW + 2*pp + hip;
-    // an output lane l then finds its head's mu term in accumulator 4*pp.
-    const bool used = ((row & 3) == 0) && ((row >> 3) < C::PAIRS);
-    const int hl = wave * HPW + 2 * (row >> 3) + ((row >> 2) & 1);
-    const float *qh = qr + (used ? hl : 0) * kD;
-    const float *mu = p.muk + (int64_t)(h0 + (used ? hl : 0)) * kD;
-#pragma unroll
-    for (int st = 0; st < kKSteps; ++st) {
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const int i = 16 * st + 8 * khalf + e;
-        float gv = 0.f;
-        if (used) {
-          gv = (i < kD / 2) ? qh[i] * mu[i] + qh[i + kD / 2] * mu[i + kD / 2]
-                            : qh[i] * mu[i - kD / 2] - qh[i - kD / 2] * mu[i];
-        }
-        Amu[st][e] = (short)f32_to_bf16_bits(gv);
-      }
-    }
-  }
-  __syncthreads();  // the setup LDS area is reused by the pipeline stages
-
   // ---- tile streaming setup ----
   const int64_t slab_elems = (int64_t)p.N * p.Hs * p.R;
   const uint16_t *slab = reinterpret_cast<const uint16_t *>(p.store) +
@@ -260,6 +209,141 @@ __global__ __launch_bounds__(NW * 64, 1) void decode_mfma_split(DecodeParams p) 
           phi_off + (uint32_t)(n * C::NT + tid) * 16, 0, 0, 0);
   };
 
+
+  // ---- setup: G^T and g0 of the group, bf16, in LDS ----
+  // Pass 1, one thread per (head hl, i < 64): q' = RoPE(q, pos) * scale at i
+  // and i + 64 into qr, g0 at i and i + 64 into g0t.  Pass 2, one item per
+  // (head hl, k block k0..k0+7, i block i0..i0+7 < 64): the 16 rows W[i0 + ii]
+  // and W[i0 + 64 + ii] (8 k's each, one 16-byte load per row) give the 8 x 8
+  // blocks of G^T at columns i0 and i0 + 64, written as 16-byte rows.  All
+  // global loads of both passes are issued first; with EARLY the first store
+  // and phi tiles are issued right after them and stream in during the rest.
+  uint16_t *gt = reinterpret_cast<uint16_t *>(lds + C::SETUP_OFF);  // [HG][RK][kGPitch] (+pad)
+  uint16_t *g0t = gt + C::HG * C::G_HEAD;                             // [HG][kGPitch]
+  float *qr = reinterpret_cast<float *>(g0t + C::HG * kGPitch);       // [HG][kD]
+  {
+    // Indexes past the last (head, i) pair or G item are clamped to it: every
+    // load is valid and such threads write the same values to the same LDS
+    // words as the thread that owns them, so no step is conditional.
+    float qin[C::P1_PER_THREAD][2], mkin[C::P1_PER_THREAD][2];
+    float2 csin[C::P1_PER_THREAD];
+#pragma unroll
+    for (int n = 0; n < C::P1_PER_THREAD; ++n) {
+      const int o = min(n * C::NT + tid, C::HG * (kD / 2) - 1);
+      const int hl = o / (kD / 2), i = o % (kD / 2);
+      const float *qb = p.q + ((int64_t)vb * p.H + h0 + hl) * kD;
+      const float *mu = p.muk + (int64_t)(h0 + hl) * kD;
+      qin[n][0] = qb[i];
+      qin[n][1] = qb[i + kD / 2];
+      mkin[n][0] = mu[i];
+      mkin[n][1] = mu[i + kD / 2];
+      csin[n] = reinterpret_cast<const float2 *>(p.rope_f32 + (int64_t)pos * kD)[i];
+    }
+    auto item_w = [&](int j, u32x4_t (&wlo)[8], u32x4_t (&whi)[8]) {
+      const int ib = j % 8, kb = (j / 8) % (RK / 8), hl = j / RK;
+      const uint16_t *wb = reinterpret_cast<const uint16_t *>(p.wk) +
+                           ((int64_t)(h0 + hl) * kD + 8 * ib) * RK + 8 * kb;
+#pragma unroll
+      for (int ii = 0; ii < 8; ++ii) {
+        wlo[ii] = *reinterpret_cast<const u32x4_t *>(wb + ii * RK);
+        whi[ii] = *reinterpret_cast<const u32x4_t *>(wb + (ii + kD / 2) * RK);
+      }
+    };
+    u32x4_t wlo[8], whi[8];
+    item_w(min(tid, C::ITEMS - 1), wlo, whi);
+    if constexpr (C::EARLY) {
+      __builtin_amdgcn_sched_barrier(0);  // the setup loads go out before the tiles
+      issue_store(0);                     // ntiles >= 1 here
+      issue_phi(0);
+    }
+#pragma unroll
+    for (int n = 0; n < C::P1_PER_THREAD; ++n) {
+      const int o = min(n * C::NT + tid, C::HG * (kD / 2) - 1);
+      const int hl = o / (kD / 2), i = o % (kD / 2);
+      const float cn = csin[n].x, sn = csin[n].y, a = qin[n][0], bb = qin[n][1];
+      const float qa = (a * cn - bb * sn) * p.scale_log2;  // q' at i
+      const float qc = (a * sn + bb * cn) * p.scale_log2;  // q' at i + 64
+      qr[hl * kD + i] = qa;
+      qr[hl * kD + i + kD / 2] = qc;
+      // g0 = G with mu_k,t in place of W[:, k]
+      g0t[hl * kGPitch + i] = f32_to_bf16_bits(qa * mkin[n][0] + qc * mkin[n][1]);
+      g0t[hl * kGPitch + i + kD / 2] = f32_to_bf16_bits(qc * mkin[n][0] - qa * mkin[n][1]);
+    }
+    lds_barrier();  // the first tiles may still be in flight
+    auto item_build = [&](int j, const u32x4_t (&wlo)[8], const u32x4_t (&whi)[8]) {
+      const int ib = j % 8, kb = (j / 8) % (RK / 8), hl = j / RK;
+      const int i0 = 8 * ib, k0 = 8 * kb;
+      float qa[8], qc[8];  // q' at i0 + ii and i0 + 64 + ii
+#pragma unroll
+      for (int ii = 0; ii < 8; ++ii) {
+        qa[ii] = qr[hl * kD + i0 + ii];
+        qc[ii] = qr[hl * kD + i0 + ii + kD / 2];
+      }
+      uint16_t *gh = gt + hl * C::G_HEAD;
+#pragma unroll
+      for (int kk = 0; kk < 8; ++kk) {
+        u32x4_t vlo, vhi;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          float glo[2], ghi[2];
+#pragma unroll
+          for (int h = 0; h < 2; ++h) {
+            const int ii = 2 * e + h;
+            const uint32_t pa = wlo[ii][kk / 2], pb = whi[ii][kk / 2];
+            const float wa = (kk & 1) ? bf16_hi(pa) : bf16_lo(pa);
+            const float wc = (kk & 1) ? bf16_hi(pb) : bf16_lo(pb);
+            glo[h] = qa[ii] * wa + qc[ii] * wc;  // G[i0 + ii, k]
+            ghi[h] = qc[ii] * wa - qa[ii] * wc;  // G[i0 + 64 + ii, k]
+          }
+          vlo[e] = pack_bf16x2(glo[0], glo[1]);
+          vhi[e] = pack_bf16x2(ghi[0], ghi[1]);
+        }
+        *reinterpret_cast<u32x4_t *>(gh + (k0 + kk) * kGPitch + i0) = vlo;
+        *reinterpret_cast<u32x4_t *>(gh + (k0 + kk) * kGPitch + i0 + kD / 2) = vhi;
+      }
+    };
+    if constexpr (C::EARLY) {
+      item_build(min(tid, C::ITEMS - 1), wlo, whi);
+    } else {
+      for (int j = tid; j < C::ITEMS; j += C::NT) {
+        if (j != tid) item_w(j, wlo, whi);
+        item_build(j, wlo, whi);
+      }
+    }
+  }
+  lds_barrier();
+
+  // ---- A operands: G^T rows (per head pair) and the mu row block ----
+  const int row = lane & 31, khalf = lane >> 5;
+  bf16x8_t Ak[C::PAIRS][C::KT][kKSteps];
+  bf16x8_t Amu[kKSteps];
+#pragma unroll
+  for (int pp = 0; pp < C::PAIRS; ++pp) {
+#pragma unroll
+    for (int ti = 0; ti < C::KT; ++ti) {
+      const int hip = (row >> 2) & 1;
+      const int k = ti * 16 + ((row >> 3) << 2) + (row & 3);
+      const int hl = wave * HPW + 2 * pp + hip;
+      const uint16_t *src = gt + hl * C::G_HEAD + k * kGPitch + 8 * khalf;
+#pragma unroll
+      for (int st = 0; st < kKSteps; ++st)
+        Ak[pp][ti][st] = *reinterpret_cast<const bf16x8_t *>(src + 16 * st);
+    }
+  }
+  {
+    // mu rows: row 8*pp + 4*hip (pp < PAIRS) carries head wave*HPW + 2*pp + hip;
+    // an output lane l then finds its head's mu term in accumulator 4*pp.
+    const bool used = ((row & 3) == 0) && ((row >> 3) < C::PAIRS);
+    const int hl = used ? wave * HPW + 2 * (row >> 3) + ((row >> 2) & 1) : 0;
+    const uint16_t *src = g0t + hl * kGPitch + 8 * khalf;
+#pragma unroll
+    for (int st = 0; st < kKSteps; ++st) {
+      const bf16x8_t v = *reinterpret_cast<const bf16x8_t *>(src + 16 * st);
+      Amu[st] = used ? v : bf16x8_t{};
+    }
+  }
+  lds_barrier();  // the setup LDS area is reused by the pipeline stages
+
   // ---- online-softmax state: per lane (slot residue l%32, head of the pair) ----
   float m[C::PAIRS], l[C::PAIRS], acc[C::PAIRS][RV];
 #pragma unroll
@@ -273,11 +357,17 @@ __global__ __launch_bounds__(NW * 64, 1) void decode_mfma_split(DecodeParams p) 
   // Issue order: iteration it issues phi(it+1), then store(it+NS-1), right
   // after the barrier that shows every wave is done with tile it-1 (whose
   // buffers they reuse).  The prologue issues the stores before tile NS-1
-  // and phi(0), in the order the iterations would have.
-  for (int k = 0; k + 2 < C::NS; ++k)
-    if (k < ntiles) issue_store(k);
-  issue_phi(0);
-  if (C::NS - 2 < ntiles) issue_store(C::NS - 2);
+  // and phi(0), in the order the iterations would have (with EARLY, store(0)
+  // and phi(0) were issued before the setup).
+  if constexpr (C::EARLY) {
+    for (int k = 1; k + 2 < C::NS; ++k)
+      if (k < ntiles) issue_store(k);
+  } else {
+    for (int k = 0; k + 2 < C::NS; ++k)
+      if (k < ntiles) issue_store(k);
+    issue_phi(0);
+  }
+  if (C::NS - 2 < ntiles && (C::NS > 2 || !C::EARLY)) issue_store(C::NS - 2);
 
   const int tj = lane & 31;
   const int swz = tj & 7;
@@ -359,34 +449,60 @@ __global__ __launch_bounds__(NW * 64, 1) void decode_mfma_split(DecodeParams p) 
   }
 
   // ---- combine the 32 lane states of every head and write the partial ----
+  // The head's maximum M over its 32 lanes (xor butterfly inside the half
+  // wave); every lane rescales its (l, acc) to M, and the 32 lanes are summed
+  // through LDS by one thread per partial value.
+  u32x4_t wpre[C::WV_AHEAD ? C::OUT_PER_THREAD : 1][RV / 8];
+  float mupre[C::WV_AHEAD ? C::OUT_PER_THREAD : 1];
+  if constexpr (C::WV_AHEAD) {
+    if (p.write_out) {  // W_up,v,t rows and mu_v,t of this thread's outputs, ahead of use
+#pragma unroll
+      for (int n = 0; n < C::OUT_PER_THREAD; ++n) {
+        const int o = n * C::NT + tid, hl = o / kD, i = o % kD;
+        const u32x4_t *wrow = reinterpret_cast<const u32x4_t *>(
+            reinterpret_cast<const uint16_t *>(p.wv) + ((int64_t)(h0 + hl) * kD + i) * RV);
+#pragma unroll
+        for (int r8 = 0; r8 < RV / 8; ++r8) wpre[n][r8] = wrow[r8];
+        mupre[n] = p.muv[(int64_t)(h0 + hl) * kD + i];
+      }
+    }
+  }
   __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
   __syncthreads();  // every wave is done reading the last tile's buffers
-  float *red = reinterpret_cast<float *>(lds);  // [NW][PAIRS][64][RV + 2]
+  float *red = reinterpret_cast<float *>(lds);  // [HG][RV + 1][32]: rescaled l, acc
+  float *hmax = red + C::RED_FLOATS;            // [HG]
+  float *comb = hmax + C::HG;                   // [HG][RV + 2], one context split
 #pragma unroll
   for (int pp = 0; pp < C::PAIRS; ++pp) {
-    float *dst = red + ((wave * C::PAIRS + pp) * 64 + lane) * (RV + 2);
-    dst[0] = m[pp];
-    dst[1] = l[pp];
+    float M = m[pp];
 #pragma unroll
-    for (int r = 0; r < RV; ++r) dst[2 + r] = acc[pp][r];
+    for (int o = 16; o > 0; o >>= 1) M = fmaxf(M, __shfl_xor(M, o, 64));
+    const float f = m[pp] == -INFINITY ? 0.f : exp2f(m[pp] - M);
+    const int hl = wave * HPW + 2 * pp + (lane >> 5);
+    float *dst = red + hl * (RV + 1) * 32 + (lane & 31);
+    dst[0] = l[pp] * f;
+#pragma unroll
+    for (int r = 0; r < RV; ++r) dst[(r + 1) * 32] = acc[pp][r] * f;
+    if ((lane & 31) == 0) hmax[hl] = M;
   }
   __syncthreads();
-  float *comb = red + NW * C::PAIRS * 64 * (RV + 2);  // [HG][RV + 2], one context split
   for (int o = tid; o < C::HG * (RV + 2); o += C::NT) {
     const int hl = o / (RV + 2), r = o % (RV + 2);
-    const int w = hl / HPW, pp = (hl % HPW) / 2, half = hl & 1;
-    const float *src = red + ((w * C::PAIRS + pp) * 64 + half * 32) * (RV + 2);
-    float M = -INFINITY;
-    for (int i = 0; i < 32; ++i) M = fmaxf(M, src[i * (RV + 2)]);
     float v;
     if (r == 0) {
-      v = M;
+      v = hmax[hl];
     } else {
-      v = 0.f;
-      for (int i = 0; i < 32; ++i) {
-        const float mi = src[i * (RV + 2)];
-        if (mi != -INFINITY) v = fmaf(src[i * (RV + 2) + r], exp2f(mi - M), v);
+      const float4 *src = reinterpret_cast<const float4 *>(red + (hl * (RV + 1) + r - 1) * 32);
+      float4 t = src[0];
+#pragma unroll
+      for (int c = 1; c < 8; ++c) {
+        const float4 u = src[c];
+        t.x += u.x;
+        t.y += u.y;
+        t.z += u.z;
+        t.w += u.w;
       }
+      v = (t.x + t.y) + (t.z + t.w);
     }
     if (p.write_out)
       comb[o] = v;
@@ -398,23 +514,25 @@ __global__ __launch_bounds__(NW * 64, 1) void decode_mfma_split(DecodeParams p) 
     // (no merge launch).  out = W_up,v,t (acc / l) + mu_v,t, one thread per
     // output element, the bf16 row of W_up,v,t read as 16-byte vectors.
     __syncthreads();
-    for (int o = tid; o < C::HG * kD; o += C::NT) {
-      const int hl = o / kD, i = o % kD;
+#pragma unroll
+    for (int n = 0; n < C::OUT_PER_THREAD; ++n) {
+      const int o = n * C::NT + tid, hl = o / kD, i = o % kD;
       const float *c = comb + hl * (RV + 2);
       const u32x4_t *wrow = reinterpret_cast<const u32x4_t *>(
           reinterpret_cast<const uint16_t *>(p.wv) + ((int64_t)(h0 + hl) * kD + i) * RV);
       float a = 0.f;
 #pragma unroll
       for (int r8 = 0; r8 < RV / 8; ++r8) {
-        const u32x4_t wv = wrow[r8];
+        const u32x4_t wv = C::WV_AHEAD ? wpre[C::WV_AHEAD ? n : 0][r8] : wrow[r8];
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           a = fmaf(bf16_lo(wv[e]), c[2 + 8 * r8 + 2 * e], a);
           a = fmaf(bf16_hi(wv[e]), c[3 + 8 * r8 + 2 * e], a);
         }
       }
+      const float mu = C::WV_AHEAD ? mupre[C::WV_AHEAD ? n : 0] : p.muv[(int64_t)(h0 + hl) * kD + i];
       const int64_t oi = ((int64_t)vb * p.H + h0 + hl) * kD + i;
-      p.out[oi] = fmaf(a, 1.0f / c[1], p.muv[(int64_t)(h0 + hl) * kD + i]);
+      p.out[oi] = fmaf(a, 1.0f / c[1], mu);
     }
   }
 #endif

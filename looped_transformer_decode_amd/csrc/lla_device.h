@@ -54,6 +54,19 @@ __device__ __forceinline__ float wave_sum(float v) {
   return v;
 }
 
+// Workgroup barrier for LDS data: a wave waits for its own LDS operations
+// (lgkmcnt) before the barrier, but not for outstanding global loads or
+// global-to-LDS transfers, which a __syncthreads() fence would also wait
+// for; the signal fences keep the compiler from moving memory accesses
+// across the barrier.
+constexpr int kWaitLgkmOnly = 15 | (7 << 4) | (0 << 8) | (3 << 14);  // lgkmcnt(0)
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_s_waitcnt(kWaitLgkmOnly);
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  __builtin_amdgcn_s_barrier();
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+}
+
 // s_waitcnt immediate that waits until at most n vector-memory operations
 // are outstanding and does not wait on the other counters (gfx9 encoding:
 // vmcnt[3:0] | expcnt[6:4] | lgkmcnt[11:8] | vmcnt[5:4] << 14).
