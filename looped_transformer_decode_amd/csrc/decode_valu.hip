@@ -123,10 +123,14 @@ __global__ __launch_bounds__(kThreads) void decode_valu_split(DecodeParams p) {
   if (tid < rv) part[2 + tid] = acc;
 }
 
+constexpr int kLoadBatch = 8;   // loads a thread issues before it waits
+
 // Merge the context splits of every (sequence, head) by log-sum-exp and
 // apply the loop-t value up-projection once: out = W_up,v,t (A / L) + mu_v,t.
 // A block covers merge_heads_per_block() heads of one sequence, one thread
-// per output element.
+// per output element.  The block's time is its chain of memory round trips,
+// so loads go out in batches of kLoadBatch independent ones (indexes past
+// the end clamped to the last element, whose duplicates are then skipped).
 template <typename E>
 __global__ __launch_bounds__(256) void decode_merge(DecodeParams p) {
   const int tid = threadIdx.x, b = blockIdx.y;
@@ -138,15 +142,34 @@ __global__ __launch_bounds__(256) void decode_merge(DecodeParams p) {
     const int hl = t / rv, r = t % rv;
     if (h0 + hl >= p.H) continue;
     const float *part = p.ws + (int64_t)(b * p.H + h0 + hl) * S * (rv + 2);
-    float M = -INFINITY;
-    for (int s = 0; s < S; ++s) M = fmaxf(M, part[s * (rv + 2)]);
-    float L = 0.f, A = 0.f;
-    for (int s = 0; s < S; ++s) {
-      const float *ps = part + s * (rv + 2);
-      if (ps[0] == -INFINITY) continue;  // empty split
-      const float f = exp2f(ps[0] - M);
-      L = fmaf(ps[1], f, L);
-      A = fmaf(ps[2 + r], f, A);
+    // Online over batches of splits (one batch when S <= kLoadBatch).
+    float M = -INFINITY, L = 0.f, A = 0.f;
+    for (int s0 = 0; s0 < S; s0 += kLoadBatch) {
+      float mv[kLoadBatch], lv[kLoadBatch], av[kLoadBatch];
+#pragma unroll
+      for (int u = 0; u < kLoadBatch; ++u) {
+        const float *ps = part + min(s0 + u, S - 1) * (rv + 2);
+        mv[u] = ps[0];
+        lv[u] = ps[1];
+        av[u] = ps[2 + r];
+      }
+      float Mb = M;
+#pragma unroll
+      for (int u = 0; u < kLoadBatch; ++u)
+        if (s0 + u < S) Mb = fmaxf(Mb, mv[u]);
+      if (Mb == -INFINITY) continue;  // every split so far empty
+      const float g = exp2f(M - Mb);  // 0 while M is -inf
+      L *= g;
+      A *= g;
+#pragma unroll
+      for (int u = 0; u < kLoadBatch; ++u) {
+        if (s0 + u < S && mv[u] != -INFINITY) {  // skip empty splits
+          const float f = exp2f(mv[u] - Mb);
+          L = fmaf(lv[u], f, L);
+          A = fmaf(av[u], f, A);
+        }
+      }
+      M = Mb;
     }
     abar[t] = A / L;
   }
@@ -155,24 +178,34 @@ __global__ __launch_bounds__(256) void decode_merge(DecodeParams p) {
   for (int o = tid; o < hpb * d; o += blockDim.x) {
     const int hl = o / d, i = o % d, h = h0 + hl;
     if (h >= p.H) continue;
+    const float mu = p.muv[(int64_t)h * d + i];
     const float *ab = abar + hl * rv;
     const E *w = reinterpret_cast<const E *>(p.wv) + ((int64_t)h * d + i) * rv;
     float acc = 0.f;
     if (vec) {
       const uint4 *w4 = reinterpret_cast<const uint4 *>(w);
-      for (int r8 = 0; r8 < rv / 8; ++r8) {
-        const uint4 v = w4[r8];
-        const uint32_t u[4] = {v.x, v.y, v.z, v.w};
+      const int n8 = rv / 8;
+      for (int c0 = 0; c0 < n8; c0 += kLoadBatch) {
+        uint4 v[kLoadBatch];
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          acc = fmaf(bf16_lo(u[e]), ab[8 * r8 + 2 * e], acc);
-          acc = fmaf(bf16_hi(u[e]), ab[8 * r8 + 2 * e + 1], acc);
+        for (int u = 0; u < kLoadBatch; ++u) v[u] = w4[min(c0 + u, n8 - 1)];
+#pragma unroll
+        for (int u = 0; u < kLoadBatch; ++u) {
+          if (c0 + u < n8) {
+            const uint32_t uu[4] = {v[u].x, v[u].y, v[u].z, v[u].w};
+            const float *a8 = ab + 8 * (c0 + u);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              acc = fmaf(bf16_lo(uu[e]), a8[2 * e], acc);
+              acc = fmaf(bf16_hi(uu[e]), a8[2 * e + 1], acc);
+            }
+          }
         }
       }
     } else {
       for (int r = 0; r < rv; ++r) acc = fmaf(load_elem(w, r), ab[r], acc);
     }
-    p.out[((int64_t)b * p.H + h) * d + i] = acc + p.muv[(int64_t)h * d + i];
+    p.out[((int64_t)b * p.H + h) * d + i] = acc + mu;
   }
 }
 
@@ -187,7 +220,6 @@ __global__ __launch_bounds__(256) void decode_merge(DecodeParams p) {
 // read in batches of kLoadBatch independent loads.
 constexpr int kBT = 8;
 static_assert(kBT == 8, "batched_merge_lds() sizes the LDS for tiles of 8 sequences");
-constexpr int kLoadBatch = 8;   // loads a thread issues before it waits
 
 // Copies the d x rv block of W_up,v,t at wg (16-byte aligned, rows of a
 // whole number of 16-byte chunks) into LDS rows of `pitch` dwords.
