@@ -363,7 +363,7 @@ __global__ __launch_bounds__(512, 1) void decode2d_split(DecodeParams p) {
     issue_store(1);
   }
   wait_vm_small(ntiles > 1 ? C::PHI_LOADS + LW : 0);  // store(0), phi(0) have landed
-  __syncthreads();
+  lds_barrier();  // (a __syncthreads() would also wait for store(1), phi(1))
 
   const int j = lane & 31;
   const int fj = swz(j);
@@ -462,7 +462,10 @@ __global__ __launch_bounds__(512, 1) void decode2d_split(DecodeParams p) {
 #pragma unroll
     for (int pp = 0; pp < C::PAIRS; ++pp) scp[pp] = scc[pp];
     wait_vm_small(it + 2 < ntiles ? C::PHI_LOADS + LW : 0);  // store(it+1), phi(it+1)
-    __syncthreads();
+    // LDS-only barrier: a __syncthreads() would also wait for store(it+2)
+    // and phi(it+2), issued at the top of this iteration, and so cut the
+    // prefetch to one iteration.
+    lds_barrier();
   }
 
   // ---- partials (m, l, sum p c_v) of every head ----
