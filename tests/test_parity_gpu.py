@@ -145,6 +145,10 @@ BF16_SHAPES = [
     ("long_recurrence_t16_ctx8k", dict(B=2, D=2, N=260, H=8)),
     ("extreme_batch_b768_ctx4k", dict(B=2, D=1, N=160, d=64)),   # generic (VALU) bf16 path
     ("lla2d_b256_ctx4k", dict(B=2, D=2, N=170)),
+    # two head groups per sequence on the fast path (16, 8 and 8 heads per workgroup)
+    ("extreme_batch_b768_ctx4k", dict(B=2, D=1, N=130, H=32)),
+    ("bf16_b32_ctx4k", dict(B=2, D=1, N=100, H=16)),
+    ("long_recurrence_t16_ctx8k", dict(B=2, D=1, N=90, H=16)),
 ]
 
 
