@@ -409,8 +409,8 @@ __global__ __launch_bounds__(256) void decode_merge_inflight(DecodeParams p, con
   float *qr = kr + nq * d;        // [nq][d]  rotated, scaled queries
   float *sc = qr + nq * d;        // [nq][nq] in-flight scores (m <= i)
   float *abar = sc + nq * nq;     // [rv][nqp] store latent numerators, query-minor
-  float *st = abar + rv * nqp;    // [nq][2]  store M, L
-  float *wsp = st + 2 * nq;       // [nq][S]  split weights
+  float *st = abar + rv * nqp;    // [nq][4]  store M, L; then fs, fs L, denominator
+  float *wsp = st + 4 * nq;       // [nq][S]  split weights
   uint32_t *wl = reinterpret_cast<uint32_t *>(sm + lay.w_off);  // [d][lay.w_pitch] dwords
   const int first = min(max(p.pos[b], 0), p.N);
   const bool act = t < d;
@@ -474,8 +474,8 @@ __global__ __launch_bounds__(256) void decode_merge_inflight(DecodeParams p, con
       wsp[i * S + s2] = w;
       L = fmaf(part[s2 * (rv + 2) + 1], w, L);
     }
-    st[2 * i] = M;
-    st[2 * i + 1] = L;
+    st[4 * i] = M;
+    st[4 * i + 1] = L;
   }
   __syncthreads();
   const int na = nqp * rv;  // padded queries get zero numerators
@@ -503,19 +503,59 @@ __global__ __launch_bounds__(256) void decode_merge_inflight(DecodeParams p, con
     }
   }
   __syncthreads();
-  // scores s[i][m], m <= i: one thread per pair, the element order rotated
-  // per thread so that threads of a wave read different banks
+  // scores s[i][m], m <= i: one thread per pair, four partial sums over
+  // 16-byte LDS reads (loads batched by the unrolled loop), the chunk order
+  // rotated per thread so that threads of a wave read different banks
+  const bool vec4 = d % 4 == 0;
   for (int pr = t; pr < nq * nq; pr += nt) {
     const int i = pr / nq, m = pr % nq;
     if (m > i) continue;
-    float v = 0.f;
-    const int e0 = pr % d;
     const float *qi = qr + i * d, *km = kr + m * d;
-    for (int e = e0; e < d; ++e) v = fmaf(qi[e], km[e], v);
-    for (int e = 0; e < e0; ++e) v = fmaf(qi[e], km[e], v);
+    float v;
+    if (vec4) {
+      const int nc = d / 4, c0 = pr % nc;
+      const float4 *q4 = reinterpret_cast<const float4 *>(qi);
+      const float4 *k4 = reinterpret_cast<const float4 *>(km);
+      float a0 = 0.f, a1 = 0.f, a2 = 0.f, a3 = 0.f;
+#pragma unroll 8
+      for (int c = 0; c < nc; ++c) {
+        const int cc = c + c0 < nc ? c + c0 : c + c0 - nc;
+        const float4 x = q4[cc], y = k4[cc];
+        a0 = fmaf(x.x, y.x, a0);
+        a1 = fmaf(x.y, y.y, a1);
+        a2 = fmaf(x.z, y.z, a2);
+        a3 = fmaf(x.w, y.w, a3);
+      }
+      v = (a0 + a1) + (a2 + a3);
+    } else {
+      v = 0.f;
+      const int e0 = pr % d;
+      for (int e = e0; e < d; ++e) v = fmaf(qi[e], km[e], v);
+      for (int e = 0; e < e0; ++e) v = fmaf(qi[e], km[e], v);
+    }
     sc[i * nq + m] = v;
   }
   __syncthreads();
+  // per query, once: the maximum M over the store part and its in-flight
+  // scores, the store factor fs = 2^(M_s - M), the in-flight weights
+  // 2^(s_m - M) in place of the scores (0 for m > i) and the denominator
+  for (int i = t; i < nq; i += nt) {
+    const float Ms = st[4 * i], Ls = st[4 * i + 1];
+    float M = Ms;
+#pragma unroll 8
+    for (int m = 0; m < nq; ++m) M = m <= i ? fmaxf(M, sc[i * nq + m]) : M;
+    const float fs = (Ms == -INFINITY) ? 0.f : exp2f(Ms - M);
+    float den = fs * Ls;
+#pragma unroll 8
+    for (int m = 0; m < nq; ++m) {
+      const float e = m <= i ? exp2f(sc[i * nq + m] - M) : 0.f;
+      sc[i * nq + m] = e;
+      den += e;
+    }
+    st[4 * i] = fs;
+    st[4 * i + 1] = fs * Ls;
+    st[4 * i + 2] = den;
+  }
   // the keys are done with: stage the in-flight values instead
   if (act) {
     for (int m0 = 0; m0 < nq; m0 += kLoadBatch) {
@@ -542,6 +582,7 @@ __global__ __launch_bounds__(256) void decode_merge_inflight(DecodeParams p, con
     float wa[kQGroup];
 #pragma unroll
     for (int j = 0; j < kQGroup; ++j) wa[j] = 0.f;
+#pragma unroll 8
     for (int r = 0; r < rv; ++r) {
       const float w = w_vec ? w_lds_elem<E>(wrow, r) : load_elem(wgrow, r);
       const float *ar = abar + r * nqp + i0;
@@ -552,17 +593,12 @@ __global__ __launch_bounds__(256) void decode_merge_inflight(DecodeParams p, con
     for (int j = 0; j < kQGroup; ++j) {
       const int i = i0 + j;
       if (i >= nq) break;
-      const float Ms = st[2 * i], Ls = st[2 * i + 1];
-      float M = Ms;
-      for (int m = 0; m <= i; ++m) M = fmaxf(M, sc[i * nq + m]);
-      const float fs = (Ms == -INFINITY) ? 0.f : exp2f(Ms - M);
-      float num = fs * fmaf(mu, Ls, wa[j]), den = fs * Ls;
-      for (int m = 0; m <= i; ++m) {
-        const float e = exp2f(sc[i * nq + m] - M);
-        den += e;
-        num = fmaf(e, kr[m * d + el], num);
-      }
-      p.out[((int64_t)(b * nq + i) * H + h) * d + el] = num / den;
+      // [fs (W_up,v,t A + mu_v,t L_s) + sum_m w_m v_m] / den, w_m = 0 for m > i
+      float num = fmaf(st[4 * i], wa[j], st[4 * i + 1] * mu);
+      const float *wi = sc + i * nq;
+#pragma unroll 8
+      for (int m = 0; m < nq; ++m) num = fmaf(wi[m], kr[m * d + el], num);
+      p.out[((int64_t)(b * nq + i) * H + h) * d + el] = num / st[4 * i + 2];
     }
   }
 }

@@ -74,7 +74,8 @@ __device__ __forceinline__ QuerySlot query_slot(const DecodeParams &p, int32_t v
 
 // LDS of the in-flight merge (floats unless noted): rotated keys and queries
 // [2][nq][d], in-flight scores [nq][nq], store numerators [rv][nq_pad] (query
-// count padded to whole groups of 8), M and L [nq][2], split weights [nq][S];
+// count padded to whole groups of 8), per-query store M, L and softmax
+// factors [nq][4], split weights [nq][S];
 // then, 16-byte aligned, W_up,v,t of the head as [d] rows of w_pitch dwords
 // (an odd count, so that consecutive rows start in different banks).
 // base: bytes without the W rows; with_w: bytes with them.
@@ -90,7 +91,7 @@ __host__ __device__ inline InflightMergeLds inflight_merge_lds(int32_t nq, int32
   InflightMergeLds l;
   l.nq_pad = (nq + 7) / 8 * 8;
   const size_t f = (size_t)2 * nq * d + (size_t)nq * nq + (size_t)l.nq_pad * rv +
-                   2 * (size_t)nq + (size_t)nq * S;
+                   4 * (size_t)nq + (size_t)nq * S;
   l.base = 4 * f;
   l.w_off = (int32_t)((f + 3) / 4 * 4);
   l.w_pitch = ((rv * esize + 3) / 4) | 1;
