@@ -235,6 +235,7 @@ INFLIGHT_SHAPES = [
     ("lla2d_b256_ctx4k", dict(B=2, D=1, N=170), 4),                  # LLA-2D fast path
     ("tiny_fp32", dict(B=2, N=128, d=96), 5),                        # d not dividing the block
     ("bf16_b32_ctx4k", dict(B=2, D=1, N=200, H=2), 32),              # most queries: 4 groups of 8
+    ("extreme_batch_b768_ctx4k", dict(B=2, D=1, N=150), 20),         # single-query fast path per query
 ]
 
 
