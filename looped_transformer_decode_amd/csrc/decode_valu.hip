@@ -18,6 +18,8 @@ namespace detail {
 constexpr int kThreads = 256;
 constexpr int kWaves = kThreads / 64;
 typedef __attribute__((__vector_size__(4 * sizeof(uint32_t)))) uint32_t u32x4_t;
+typedef __attribute__((__vector_size__(8 * sizeof(short)))) short bf16x8_t;
+typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4_t;
 
 template <typename E, int RKM>
 __global__ __launch_bounds__(kThreads) void decode_valu_split(DecodeParams p) {
@@ -570,6 +572,77 @@ __global__ __launch_bounds__(256) void decode_merge_inflight(DecodeParams p, con
   }
   __syncthreads();
 
+  if constexpr (sizeof(E) == 2) {
+    if (w_vec && d % 16 == 0 && d <= 256 && rv <= 128 && nt == 256) {
+      // bf16 W_up,v,t in LDS: (queries x r_v) x (r_v x d) on the matrix
+      // cores, v_mfma_f32_16x16x32_bf16 tiles of 16 queries x 16 output
+      // elements over 32 value components (components past r_v are zero);
+      // wave w takes the element tiles w, w + 4, ...  The latent averages
+      // are rounded to bf16 for the products (sums in fp32).  Lane l holds
+      // A = averages of query l % 16 at components 8 (l / 16) + 0..7, B = the
+      // W_up,v,t row of element l % 16 at the same components, and D =
+      // queries 4 (l / 16) + 0..3 of element l % 16.
+      constexpr int kMaxKs = 4;  // r_v <= 128
+      const int l16 = t & 15, g = (t & 63) >> 4, wave = t >> 6;
+      const int nqt = (nq + 15) / 16, nks = (rv + 31) / 32;
+      float mus[4];  // mu_v,t of this lane's element in each of its tiles, fetched ahead
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        mus[j] = p.muv[(int64_t)h * d + min(16 * (wave + 4 * j) + l16, d - 1)];
+      for (int qt = 0; qt < nqt; ++qt) {
+        bf16x8_t a[kMaxKs];
+#pragma unroll
+        for (int ks = 0; ks < kMaxKs; ++ks) {
+          const int q = 16 * qt + l16, r0 = 32 * ks + 8 * g;
+          float f[8];
+#pragma unroll
+          for (int e = 0; e < 8; ++e)
+            f[e] = (r0 < rv && q < nqp) ? abar[(r0 + e) * nqp + q] : 0.f;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const uint32_t pk = pack_bf16x2(f[2 * e], f[2 * e + 1]);
+            a[ks][2 * e] = (short)(pk & 0xFFFFu);
+            a[ks][2 * e + 1] = (short)(pk >> 16);
+          }
+        }
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {  // element tiles wave + 4 j (d <= 256)
+          const int et = wave + 4 * j;
+          if (et >= d / 16) break;
+          const int el = 16 * et + l16;
+          const uint32_t *wr = wl + el * lay.w_pitch;
+          f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int ks = 0; ks < kMaxKs; ++ks) {
+            if (ks >= nks) break;
+            const int r0 = 32 * ks + 8 * g;
+            bf16x8_t bw;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              const uint32_t pk = r0 < rv ? wr[r0 / 2 + e] : 0u;
+              bw[2 * e] = (short)(pk & 0xFFFFu);
+              bw[2 * e + 1] = (short)(pk >> 16);
+            }
+            acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[ks], bw, acc, 0, 0, 0);
+          }
+          // [fs (W_up,v,t A + mu_v,t L_s) + sum_m w_m v_m] / den, w_m = 0 for m > i
+          const float mu = mus[j];
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int q = 16 * qt + 4 * g + i;
+            if (q < nq) {
+              float num = fmaf(st[4 * q], acc[i], st[4 * q + 1] * mu);
+              const float *wq = sc + q * nq;
+#pragma unroll 8
+              for (int m = 0; m < nq; ++m) num = fmaf(wq[m], kr[m * d + el], num);
+              p.out[((int64_t)(b * nq + q) * H + h) * d + el] = num / st[4 * q + 2];
+            }
+          }
+        }
+      }
+      return;
+    }
+  }
   // W_up,v,t row `el` against the latent averages of a group of queries,
   // then the in-flight term of each query of the group
   const int rows = nt / d;  // whole rows of d threads; the rest sit this out
