@@ -424,6 +424,14 @@ __global__ __launch_bounds__(256) void decode_merge_inflight(DecodeParams p, con
       p.w_lds != 0 && row_bytes % 16 == 0 && (reinterpret_cast<uintptr_t>(wg) & 15) == 0;
   if (w_vec) w_rows_to_lds(wg, d, rv, lay.w_pitch, wl, t, nt);
 
+  // The in-flight values of the first kVAhead tokens, fetched now (they
+  // replace the keys in LDS once the scores are done) so that their memory
+  // latency overlaps the phases in between.
+  constexpr int kVAhead = 16;
+  float vah[kVAhead];
+#pragma unroll
+  for (int j = 0; j < kVAhead; ++j)
+    vah[j] = v_new[((int64_t)(b * nq + min(j, nq - 1)) * H + h) * d + (act ? t : 0)];
   // rotate-half RoPE of the in-flight keys and the queries at pos0 + m
   if (act) {
     const int u = t < half ? t : t - half;   // pair index
@@ -560,7 +568,10 @@ __global__ __launch_bounds__(256) void decode_merge_inflight(DecodeParams p, con
   }
   // the keys are done with: stage the in-flight values instead
   if (act) {
-    for (int m0 = 0; m0 < nq; m0 += kLoadBatch) {
+#pragma unroll
+    for (int j = 0; j < kVAhead; ++j)
+      if (j < nq) kr[j * d + t] = vah[j];
+    for (int m0 = kVAhead; m0 < nq; m0 += kLoadBatch) {
       float v[kLoadBatch];
 #pragma unroll
       for (int j = 0; j < kLoadBatch; ++j)
