@@ -382,10 +382,12 @@ __global__ __launch_bounds__(256) void decode_merge_batched(DecodeParams p) {
 //         / [e^(M_s - M) L_s + sum_m e^(s_m - M)],
 //   s_m = scale * RoPE(q_i, pos0 + i) . RoPE(k_m, pos0 + m)   (log2 domain).
 // One block per (head, sequence).  Every query's store partials are merged
-// at once, and W_up,v,t is applied to the latent averages of kQGroup queries
-// per pass over its row: with R = blockDim / d whole rows of d threads,
-// thread t < R d owns output element t % d of query groups t / d, t / d + R,
-// ...
+// at once; each query's maximum, store factor, in-flight weights and
+// denominator are formed once.  W_up,v,t is applied to the latent averages
+// of all queries on the matrix cores for bf16 stores (W_up,v,t in LDS, d a
+// multiple of 16), else by kQGroup queries per pass over its row: with
+// R = blockDim / d whole rows of d threads, thread t < R d owns output
+// element t % d of query groups t / d, t / d + R, ...
 //
 // The block's work is a chain of short phases, so its time is set by the
 // round trips to memory in that chain.  Every phase issues its global loads
