@@ -329,17 +329,25 @@ __global__ __launch_bounds__(512, 1) void decode2d_split(DecodeParams p) {
     const char *sb = lds + (t % C::NS) * C::TILE_BYTES;
     const f32x4_t al = *reinterpret_cast<const f32x4_t *>(
         reinterpret_cast<const float *>(lds + C::OFF_ALPHA + (t & 1) * H * 4) + 4 * g4);
+    // slots past the attended ones (only in the last tile) may hold
+    // anything, NaN included, so their C_v is zeroed there
+    const bool full = t0 + (t + 1) * kTile <= t1;  // workgroup-uniform
 #pragma unroll
     for (int v = 0; v < C::VB; ++v) {
       const int comp = RK + 16 * (C::VB * wave + v) + l16;
       // slots 8 g4 + e share swz_v = 2 g4: one base address, stride REC
       const char *gb = sb + 8 * g4 * C::REC + (((comp >> 3) ^ (2 * g4)) * 16) + (comp & 7) * 2;
       bf16x8_t bv;
+      if (full) {
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const int sl = 8 * g4 + e;
-        const uint16_t x = *reinterpret_cast<const uint16_t *>(gb + e * C::REC);
-        bv[e] = (t0 + t * kTile + sl < t1) ? (short)x : (short)0;
+        for (int e = 0; e < 8; ++e) bv[e] = *reinterpret_cast<const short *>(gb + e * C::REC);
+      } else {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const int sl = 8 * g4 + e;
+          const uint16_t x = *reinterpret_cast<const uint16_t *>(gb + e * C::REC);
+          bv[e] = (t0 + t * kTile + sl < t1) ? (short)x : (short)0;
+        }
       }
 #pragma unroll
       for (int i = 0; i < 4; ++i) pv[v][i] *= al[i];
