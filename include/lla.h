@@ -15,7 +15,9 @@
  * Conventions shared by every entry point
  *  - Every pointer argument named "device" is device memory owned by the
  *    caller; the library allocates no device memory, keeps no global
- *    mutable state and may be called from several host threads.
+ *    mutable state and may be called from several host threads.  The one
+ *    exception is lla_decode_attn_noalloc, which uses a static per-device
+ *    scratch array instead of a workspace argument.
  *  - Launching calls are asynchronous on the given stream (0 = the null
  *    stream).  Nothing on the decode / encode path synchronises the host.
  *  - All arguments are validated on the host before any launch; an invalid
@@ -52,8 +54,10 @@ typedef enum {
   LLA_E_UNSUPPORTED = 6, /* valid request that no kernel here implements    */
   LLA_E_VARIANT = 7,     /* per-head call on an LLA-2D store or vice versa   */
   LLA_E_HIP = 8,         /* a HIP runtime call or kernel launch failed       */
-  LLA_E_OVERFLOW = 9     /* a size does not fit (bytes in size_t / int64, or  */
+  LLA_E_OVERFLOW = 9,    /* a size does not fit (bytes in size_t / int64, or  */
                          /* batch x queries x heads in int32)                */
+  LLA_E_SCRATCH = 10     /* lla_decode_attn_noalloc: the call needs more than */
+                         /* LLA_NOALLOC_SCRATCH_BYTES of split partials      */
 } lla_status_t;
 
 typedef enum { LLA_DT_F32 = 0, LLA_DT_BF16 = 1 } lla_dtype_t;
@@ -217,6 +221,33 @@ lla_status_t lla_decode_attn_inflight(const lla_store_t *store, int32_t layer, i
                                       const void *rope_table, float softmax_scale, float *out,
                                       void *workspace, size_t ws_bytes, int32_t n_splits,
                                       hipStream_t stream);
+
+/* ---------------------------------------------------------------------------
+ * lla_decode_attn without a workspace argument, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc).  Same arguments, results and errors as
+ * lla_decode_attn, minus workspace / ws_bytes: the split partials go to a
+ * static device array of LLA_NOALLOC_SCRATCH_BYTES that the library holds on
+ * every GPU it runs on until the process ends.  The call allocates nothing
+ * and calls no allocating routine.
+ *  - The scratch belongs to the current device (hipGetDevice), which must be
+ *    the device of `stream`; its address is looked up once per device, on
+ *    that device's first call.
+ *  - A call whose partials need more than LLA_NOALLOC_SCRATCH_BYTES
+ *    (lla_decode_workspace_bytes(store, n_splits) with this call's split
+ *    count) returns LLA_E_SCRATCH and launches nothing.
+ *  - Every call on one GPU shares that GPU's scratch: calls that may overlap
+ *    on one GPU (different streams, different host threads without ordering)
+ *    race and must be serialised by the caller.  The kernels write every
+ *    partial they read, so nothing in the scratch has to start at zero.
+ * ------------------------------------------------------------------------- */
+#define LLA_NOALLOC_SCRATCH_BYTES ((size_t)8 << 20)
+lla_status_t lla_decode_attn_noalloc(const lla_store_t *store, int32_t layer, int32_t loop,
+                                     const float *q, const void *w_up_k_t, const void *w_up_v_t,
+                                     const float *mu_k_t, const float *mu_v_t,
+                                     const int32_t *pos, const void *rope_table,
+                                     float softmax_scale, float *out, int32_t n_splits,
+                                     hipStream_t stream);
 
 /* Name of the kernel family lla_decode_attn / lla2d_decode_attn would
  * launch for this store ("mfma" fast path or "valu" generic path), or NULL

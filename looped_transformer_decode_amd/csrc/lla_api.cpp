@@ -348,6 +348,9 @@ const char *lla_status_string(lla_status_t s) {
     case LLA_E_VARIANT: return "LLA_E_VARIANT: store variant does not match the call";
     case LLA_E_HIP: return "LLA_E_HIP: HIP launch or runtime error";
     case LLA_E_OVERFLOW: return "LLA_E_OVERFLOW: size does not fit";
+    case LLA_E_SCRATCH:
+      return "LLA_E_SCRATCH: the call needs more than the static scratch "
+             "(LLA_NOALLOC_SCRATCH_BYTES) of lla_decode_attn_noalloc";
   }
   return "LLA_E_UNKNOWN";
 }

@@ -19,7 +19,7 @@ LLA_PER_HEAD, LLA_2D = 0, 1
 LLA_DT_F32, LLA_DT_BF16 = 0, 1
 STATUS = ["LLA_OK", "LLA_E_NULL", "LLA_E_SHAPE", "LLA_E_DTYPE", "LLA_E_RANGE",
           "LLA_E_WORKSPACE", "LLA_E_UNSUPPORTED", "LLA_E_VARIANT", "LLA_E_HIP",
-          "LLA_E_OVERFLOW"]
+          "LLA_E_OVERFLOW", "LLA_E_SCRATCH"]
 _TORCH_DT = {LLA_DT_F32: torch.float32, LLA_DT_BF16: torch.bfloat16}
 _DT_NAME = {"f32": LLA_DT_F32, "bf16": LLA_DT_BF16}
 _VARIANT_NAME = {"per_head": LLA_PER_HEAD, "2d": LLA_2D}
@@ -59,6 +59,8 @@ _SIGS = {
                         _I32),
     "lla2d_decode_attn": ([_P, _I32, _I32, _P, _P, _P, _P, _P, _P, _P, _F, _P, _P, _SZ, _I32,
                            _P], _I32),
+    "lla_decode_attn_noalloc": ([_P, _I32, _I32, _P, _P, _P, _P, _P, _P, _P, _F, _P, _I32, _P],
+                                _I32),
     "lla_decode_path": ([_P], ctypes.c_char_p),
     "lla_decode_inflight_workspace_bytes": ([_P, _I32, _I32], _SZ),
     "lla_decode_attn_inflight": ([_P, _I32, _I32, _I32, _P, _P, _P, _P, _P, _P, _P, _P, _P, _F,
@@ -311,6 +313,31 @@ def lla_decode_attn(store, layer, loop, q, w_up_k_t, w_up_v_t, mu_k_t, mu_v_t, p
     """Decode-time attention at (layer, loop) over a per-head latent store."""
     return _decode(lib().lla_decode_attn, store, layer, loop, q, w_up_k_t, w_up_v_t, mu_k_t,
                    mu_v_t, pos, rope_table, out, workspace, softmax_scale, n_splits, stream)
+
+
+def lla_decode_attn_noalloc(store, layer, loop, q, w_up_k_t, w_up_v_t, mu_k_t, mu_v_t, pos,
+                            rope_table, out, softmax_scale=0.0, n_splits=0, stream=None):
+    """lla_decode_attn without a workspace: the split partials go to the
+    library's static per-device scratch (LLA_NOALLOC_SCRATCH_BYTES); calls
+    that overlap on one GPU race."""
+    s = store
+    H, d = s.heads, s.d_head
+    _need(q, torch.float32, (s.batch, H, d), "q")
+    _need(w_up_k_t, s.torch_dtype, (H, d, s.r_k), "w_up_k_t")
+    _need(w_up_v_t, s.torch_dtype, (H, d, s.r_v), "w_up_v_t")
+    _need(mu_k_t, torch.float32, (H, d), "mu_k_t")
+    _need(mu_v_t, torch.float32, (H, d), "mu_v_t")
+    _need(pos, torch.int32, (s.batch,), "pos")
+    _need(out, torch.float32, (s.batch, H, d), "out")
+    dsc = s.desc()
+    _check(lib().lla_decode_attn_noalloc(ctypes.byref(dsc), layer, loop, _ptr(q), _ptr(w_up_k_t),
+                                         _ptr(w_up_v_t), _ptr(mu_k_t), _ptr(mu_v_t), _ptr(pos),
+                                         _ptr(rope_table), float(softmax_scale), _ptr(out),
+                                         n_splits, _stream(stream)), "lla_decode_attn_noalloc")
+    return out
+
+
+NOALLOC_SCRATCH_BYTES = 8 << 20  # LLA_NOALLOC_SCRATCH_BYTES of include/lla.h
 
 
 def lla2d_decode_attn(store, layer, loop, q, w_up_k_t, w_up_v_t, mu_k_t, mu_v_t, pos,
