@@ -78,6 +78,9 @@ def parse():
     ap.add_argument("--copy-calibration", type=float, default=0.0, metavar="GB",
                     help="instead of the benchmark, copy a buffer of this size a few times "
                          "(reference for HBM byte counters)")
+    ap.add_argument("--read-ceiling", type=float, default=0.0, metavar="GB",
+                    help="instead of the benchmark, time a plain streaming-read kernel over a "
+                         "buffer of this size (the practical HBM read ceiling)")
     ap.add_argument("--no-encode", action="store_true", help=argparse.SUPPRESS)
     ap.add_argument("--inflight", action="store_true",
                     help="decode with the step's n_new tokens in flight (multi-query causal "
@@ -111,9 +114,29 @@ def kv_algorithmic_bytes(w, pos_plus_one: int) -> int:
 
 
 def kernel_source(w, path="lla") -> str:
-    if path != "lla":
+    """Source of the split kernel whose counters a traffic summary holds;
+    path: lla, inflight (multi-query store pass), fast or final_loop."""
+    if path in ("fast", "final_loop"):
         return os.path.join(CSRC, "kvcache.hip")
+    if path == "inflight":
+        return os.path.join(CSRC, "decode_mq.hip")
     return os.path.join(CSRC, "decode2d_mfma.hip" if w.variant == "2d" else "decode_mfma.hip")
+
+
+def inflight_bytes(w, nq: int) -> int:
+    """Bytes of one in-flight call: the store slots before pos0 once, plus
+    q, k_new, v_new and out of every query, W_up,t and mu_t."""
+    return (algorithmic_bytes(w, w.N - w.n_new) - 2 * w.B * w.H * w.d * 4
+            + 4 * w.B * nq * w.H * w.d * 4)
+
+
+def encode_bytes(w) -> int:
+    """Bytes one encode-append call must move: x of both axes, W_down and mu
+    of both axes, the latents written and the start positions."""
+    K = w.T * w.width
+    rows = w.B * w.n_new * w.store_heads
+    return (2 * rows * K * w.elt_bytes + w.store_heads * K * w.R * w.elt_bytes
+            + 2 * w.store_heads * K * 4 + rows * w.R * w.elt_bytes + 4 * w.B)
 
 
 def traffic_file(w, path="lla") -> str:
@@ -165,7 +188,8 @@ def summarize_counters(w, fetch_dir: str, write_dir: str, path: str = "lla") -> 
     fetch, nf = per_dispatch(fetch_dir, "FETCH_SIZE")
     write, nw = per_dispatch(write_dir, "WRITE_SIZE")
     hbm = fetch * 1024 * FETCH_SCALE + write * 1024 * WRITE_SCALE
-    algo = algorithmic_bytes(w, w.N) if path == "lla" else kv_algorithmic_bytes(w, w.N)
+    algo = (algorithmic_bytes(w, w.N) if path == "lla" else
+            inflight_bytes(w, w.n_new) if path == "inflight" else kv_algorithmic_bytes(w, w.N))
     res = {"workload": w.name, "path": path, "batch": w.B,
            "kernel_source": os.path.relpath(kernel_source(w, path), ROOT),
            "kernel_sha256": kernel_sha(w, path), "fetch_kib_per_dispatch": round(fetch, 1),
@@ -177,11 +201,28 @@ def summarize_counters(w, fetch_dir: str, write_dir: str, path: str = "lla") -> 
     return res
 
 
+def host_cpu() -> dict:
+    """The host cores this process may run on and the CPU model."""
+    model = None
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    return {"affinity_cores": len(os.sched_getaffinity(0)), "cpu_model": model}
+
+
+def blas_threads() -> int:
+    from threadpoolctl import threadpool_info
+    return max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
+
+
 def cpu_baseline(w, codec, budget_s: float):
     """Oracle decode of the (layer 0, loop 0) call, one sequence at a time
     until the time budget is spent; scaled to tokens/s of the whole step."""
-    from threadpoolctl import threadpool_info
-
     from oracle import lla_oracle as O
     from synth.workloads import store_slab
     layer, t = 0, 0
@@ -203,8 +244,8 @@ def cpu_baseline(w, codec, budget_s: float):
         done += 1
     per_seq = spent / done
     t_step = per_seq * w.B * w.D * w.T
-    threads = max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
-    return {"value": w.B / t_step, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+    return {"value": w.B / t_step, "unit": "tokens/s", "cores": blas_threads(), "kind": "oracle",
+            "t_call_s": per_seq * w.B, **host_cpu(),
             "sample": f"{done} sequence(s) x {w.H} heads of the (layer 0, loop 0) call at pos "
                       f"{w.N - 1}, {spent:.1f} s; scaled x{w.B}/{done} sequences x "
                       f"{w.D * w.T} calls per step"}
@@ -222,8 +263,6 @@ def cpu_baseline_kv(w, budget_s: float):
     """Oracle flash-decode (decode_cache) of one (layer, loop) call, one
     sequence at a time on seeded slabs of the cache's shape, until the time
     budget is spent; scaled to tokens/s of the whole step."""
-    from threadpoolctl import threadpool_info
-
     from oracle import lla_oracle as O
     from synth import gen
     calls = w.D * w.T
@@ -237,8 +276,8 @@ def cpu_baseline_kv(w, budget_s: float):
         spent += time.perf_counter() - t0
         done += 1
     t_step = spent / done * w.B * calls
-    threads = max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
-    return {"value": w.B / t_step, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+    return {"value": w.B / t_step, "unit": "tokens/s", "cores": blas_threads(), "kind": "oracle",
+            "t_call_s": spent / done * w.B, **host_cpu(),
             "sample": f"{done} sequence(s) x {w.H} heads of one flash-decode call at pos "
                       f"{w.N - 1}, {spent:.1f} s; scaled x{w.B}/{done} sequences x {calls} "
                       f"calls per step"}
@@ -483,13 +522,14 @@ class CallTimer:
         return np.array([a.elapsed_time(b) for a, b in self.ev[:self.i]])
 
 
-def time_step(args, step, stream, torch, calls_per_step: int):
+def time_step(args, step, stream, torch, calls_per_step: int, enc_per_step: int = 0):
     """Warm-up; a plain eager pass (ms/step as launched from the host); a
     pass with events around every decode call, queued behind a spin kernel
     so that the GPU never waits for the host inside it (the events then
     bracket the kernels alone); then, unless --eager, the step captured as a
     HIP graph and replayed.  Returns (eager ms/step, reported ms/step,
-    per-call ms array)."""
+    per-call ms array), plus the per-call ms of the encode appends when
+    enc_per_step > 0 (step then takes a second timer for them)."""
     for i in range(args.warmup):
         step()
         torch.cuda.synchronize()
@@ -508,13 +548,17 @@ def time_step(args, step, stream, torch, calls_per_step: int):
 
     ms_eager = timed(step)
     timer = CallTimer(torch, calls_per_step * args.steps)
+    etimer = CallTimer(torch, enc_per_step * args.steps) if enc_per_step else None
     torch.cuda.synchronize()
     try:  # hold the queue for longer than the host needs to enqueue the pass
         torch.cuda._sleep(int(3e6 * (2.0 * ms_eager * args.steps + 20.0)))
     except (AttributeError, RuntimeError):
         pass
     for _ in range(args.steps):
-        step(timer)
+        if etimer is None:
+            step(timer)
+        else:
+            step(timer, etimer)
     torch.cuda.synchronize()
     call_ms = timer.ms()
     log(f"[bench] {args.steps} eager steps: {ms_eager:.3f} ms/step; decode call mean "
@@ -529,7 +573,47 @@ def time_step(args, step, stream, torch, calls_per_step: int):
         torch.cuda.synchronize()
         ms_step = timed(graph.replay)
         log(f"[bench] {args.steps} graph replays: {ms_step:.3f} ms/step")
+    if etimer is not None:
+        return ms_eager, ms_step, call_ms, etimer.ms()
     return ms_eager, ms_step, call_ms
+
+
+def run_read_ceiling(args, torch):
+    """A plain streaming read of a buffer larger than the caches (the
+    practical HBM read ceiling the decode kernels are compared with):
+    workgroups of 256 threads, each walking one contiguous range with eight
+    16-byte nontemporal loads per thread in flight."""
+    from synth.device import read_stream
+    dev = torch.device("cuda:0")
+    n = int(args.read_ceiling * 1e9) // (16 * 2048) * (16 * 2048)
+    src = torch.zeros(n // 4, dtype=torch.int32, device=dev)
+    results = {}
+    for blocks in (2048, 4096, 8192):
+        sink = torch.empty(blocks * 256 * 4, dtype=torch.int32, device=dev)
+        for _ in range(3):
+            read_stream(src, sink, blocks)
+        torch.cuda.synchronize()
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+        reps = max(args.steps, 5)
+        ev[0].record()
+        for _ in range(reps):
+            read_stream(src, sink, blocks)
+        ev[1].record()
+        torch.cuda.synchronize()
+        ms = ev[0].elapsed_time(ev[1]) / reps
+        results[blocks] = (ms, n / (ms / 1e3) / 1e9)
+        log(f"[bench] read ceiling: {blocks} workgroups, {n / 1e9:.2f} GB in {ms * 1e3:.1f} us: "
+            f"{results[blocks][1]:.1f} GB/s")
+    best = max(results, key=lambda b: results[b][1])
+    print(json.dumps({"metric": "streaming-read GB/s (plain read kernel, context for the decode "
+                                "kernels' HBM fraction)",
+                      "value": round(results[best][1], 1), "unit": "GB/s",
+                      "peak": HBM_PEAK_GBS, "frac": round(results[best][1] / HBM_PEAK_GBS, 4),
+                      "bytes": n, "kernel": "read_stream (synth/fill.hip)",
+                      "workgroups": best,
+                      "sweep": {str(b): {"launch_us": round(v[0] * 1e3, 2),
+                                         "GBps": round(v[1], 1)} for b, v in results.items()}}),
+          flush=True)
 
 
 def main():
@@ -544,7 +628,8 @@ def main():
         w = WORKLOADS[args.workload]
         if args.batch:
             w = w.scaled(B=args.batch)
-        print(json.dumps(summarize_counters(w, *args.summarize_counters, args.path)))
+        tag = "inflight" if args.inflight else args.path
+        print(json.dumps(summarize_counters(w, *args.summarize_counters, tag)))
         return
 
     import torch
@@ -564,6 +649,10 @@ def main():
         ms = e0.elapsed_time(e1)
         print(json.dumps({"copy_bytes_read": n * 4, "copy_bytes_written": n * 4, "ms": ms,
                           "GBps_read_plus_write": 2 * n * 4 / ms / 1e6}), flush=True)
+        return
+
+    if args.read_ceiling > 0:
+        run_read_ceiling(args, torch)
         return
 
     import looped_transformer_decode_amd as L
@@ -648,7 +737,7 @@ def main():
     log(f"[bench] path={L.lla_decode_path(store)} "
         f"splits={args.splits or L.lla_decode_auto_splits(store)}")
 
-    def step(timer=None):
+    def step(timer=None, etimer=None):
         for t in range(w.T):
             for l in range(w.D):
                 if timer is not None:
@@ -664,16 +753,23 @@ def main():
                     timer.stop(stream)
         if not args.no_encode:
             for l in range(w.D):
+                if etimer is not None:
+                    etimer.start(stream)
                 encode(store, l, xk[l], xv[l], muk[l], muv[l], wdk[l], wdv[l], start)
+                if etimer is not None:
+                    etimer.stop(stream)
 
-    ms_eager, ms_step, call_ms = time_step(args, step, stream, torch, w.D * w.T)
+    if args.no_encode:
+        ms_eager, ms_step, call_ms = time_step(args, step, stream, torch, w.D * w.T)
+        enc_ms = None
+    else:
+        ms_eager, ms_step, call_ms, enc_ms = time_step(args, step, stream, torch, w.D * w.T, w.D)
     value = w.B * nq / (ms_step / 1e3)   # generated tokens per second, all sequences
     bytes_call = algorithmic_bytes(w, w.N)
     if args.inflight:
-        # store slots before pos0 once, plus q, k_new, v_new and out of every query
-        bytes_call = (algorithmic_bytes(w, w.N - w.n_new) - 2 * w.B * w.H * w.d * 4
-                      + 4 * w.B * nq * w.H * w.d * 4)
+        bytes_call = inflight_bytes(w, nq)
     path = L.lla_decode_path(store)
+    tag = "inflight" if args.inflight else "lla"
     if w.variant == "2d":
         flops_call = algorithmic_flops(w, w.N)
         achieved = flops_call / (call_ms.mean() / 1e3) / 1e12
@@ -690,13 +786,14 @@ def main():
         splits = args.splits or L.lla_decode_auto_splits(store)
         roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
-                    "traffic": traffic_for_current_kernel(w),
+                    "traffic": traffic_for_current_kernel(w, tag),
                     "kernel": (("decode_mq_split" if path == "mfma" and 1 < nq <= 16 and w.d == 128
                                 and w.variant == "per_head" and (w.r_k, w.r_v) in MQ_RANKS
                                 else "decode split kernel")
                                + " + decode_merge_inflight (one lla_decode_attn_inflight call)")
                               if args.inflight else
-                              ("decode_mfma_split (one lla_decode_attn call"
+                              (("decode_mfma_split" if path == "mfma" else "decode_valu_split")
+                               + " (one lla_decode_attn call"
                                + (")" if splits == 1 and path == "mfma" else " + decode_merge)")),
                     "bytes_per_launch": bytes_call, "launch_us": round(call_ms.mean() * 1e3, 2)}
     res = {
@@ -718,6 +815,16 @@ def main():
         "memory": memory_summary(L.lla_store_bytes(store), w.B,
                                  torch.cuda.mem_get_info(dev)[1]),
     }
+    if enc_ms is not None and len(enc_ms):
+        eb = encode_bytes(w)
+        ea = eb / (enc_ms.mean() / 1e3) / 1e9
+        res["encode"] = {"bound": "hbm", "achieved": round(ea, 1), "peak": HBM_PEAK_GBS,
+                         "unit": "GB/s", "frac": round(ea / HBM_PEAK_GBS, 4),
+                         "kernel": f"{'lla2d' if is2d else 'lla'}_encode_append: "
+                                   f"{w.B * w.n_new} tokens x {w.store_heads} codecs, "
+                                   f"K = {w.T * w.width}",
+                         "bytes_per_launch": eb, "launch_us": round(enc_ms.mean() * 1e3, 2),
+                         "calls_per_step": w.D}
     if args.cpu_seconds > 0:
         del store, q, xk, xv
         torch.cuda.empty_cache()

@@ -86,6 +86,50 @@ def build(verbose: bool = False) -> list[str]:
     return [LIB, SYNTH_LIB]
 
 
+# Host-side sanitizer build of the C ABI: the two files that hold host
+# arithmetic (argument validation, sizes, offsets, splits, the RoPE table,
+# the scratch lookup) are compiled with AddressSanitizer and
+# UndefinedBehaviorSanitizer on their host pass only (-Xarch_host; the device
+# code is built as usual) and linked with the regular build's other objects
+# into _build/liblla_san.so.  The sanitizer runtime is not linked in: load it
+# first with LD_PRELOAD=sanitizer_runtime() and point the binding at the
+# library with LLA_LIBRARY (tests/test_sanitized_abi.py does both).
+SAN_SOURCES = ["lla_api.cpp", "decode_noalloc.hip"]
+SAN_LIB = os.path.join(BUILD, "liblla_san.so")
+SAN_FLAGS = ["-g", "-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
+             "-Xarch_host", "-fno-sanitize-recover=all", "-Xarch_host", "-fno-omit-frame-pointer"]
+
+
+def sanitizer_runtime() -> str:
+    """The clang AddressSanitizer runtime (it carries the UBSan handlers)."""
+    res = _run([HIPCC, "-print-resource-dir"]).strip().splitlines()[-1]
+    path = os.path.join(res, "lib", "linux", "libclang_rt.asan-x86_64.so")
+    if not os.path.exists(path):
+        raise RuntimeError(f"sanitizer runtime not found at {path}")
+    return path
+
+
+def build_sanitized() -> str:
+    build()
+    objs = []
+    for s in SOURCES:
+        if s in SAN_SOURCES:
+            o = os.path.join(BUILD, os.path.splitext(s)[0] + "_san.o")
+            _run([HIPCC, *COMMON, *SAN_FLAGS, "-x", "hip", "-c", os.path.join(CSRC, s), "-o", o])
+        else:
+            o = os.path.join(BUILD, os.path.splitext(s)[0] + ".o")
+        objs.append(o)
+    tmp = SAN_LIB + ".tmp"
+    _run([HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs])
+    os.replace(tmp, SAN_LIB)
+    return SAN_LIB
+
+
 if __name__ == "__main__":
-    for p in build(verbose=True):
-        print("built", p)
+    import sys
+    if sys.argv[1:] == ["--sanitize"]:
+        print("built", build_sanitized())
+        print("runtime", sanitizer_runtime())
+    else:
+        for p in build(verbose=True):
+            print("built", p)

@@ -336,7 +336,12 @@ int32_t svd_block(int32_t K, int32_t r) {
 
 extern "C" {
 
-const char *lla_status_string(lla_status_t s) {
+const char *lla_status_string(lla_status_t status) {
+  // A C caller may pass any int: read the argument's bytes as an integer
+  // rather than reading an enumerator that may be out of the type's range.
+  int32_t s;
+  static_assert(sizeof(s) == sizeof(status), "lla_status_t is 32-bit");
+  std::memcpy(&s, &status, sizeof(s));
   switch (s) {
     case LLA_OK: return "LLA_OK";
     case LLA_E_NULL: return "LLA_E_NULL: a required pointer is NULL";

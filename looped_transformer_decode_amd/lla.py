@@ -13,7 +13,10 @@ from fractions import Fraction
 
 import torch
 
-LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "liblla.so")
+# LLA_LIBRARY selects another build of the same library (the host-side
+# sanitizer build, _build/liblla_san.so); the default is the in-tree build.
+LIB_PATH = os.environ.get("LLA_LIBRARY") or os.path.join(
+    os.path.dirname(os.path.abspath(__file__)), "liblla.so")
 
 LLA_PER_HEAD, LLA_2D = 0, 1
 LLA_DT_F32, LLA_DT_BF16 = 0, 1

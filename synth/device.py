@@ -20,6 +20,9 @@ def _load():
         L.synth_fill.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_uint64,
                                  ctypes.c_int64, ctypes.c_float, ctypes.c_void_p]
         L.synth_fill.restype = ctypes.c_int
+        L.synth_read_stream.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32,
+                                        ctypes.c_void_p, ctypes.c_void_p]
+        L.synth_read_stream.restype = ctypes.c_int
         _lib = L
     return _lib
 
@@ -34,3 +37,15 @@ def fill_hash_normal(t: torch.Tensor, key: int, first: int = 0, scale: float = 1
     if err != 0:
         raise RuntimeError(f"synth_fill failed: hipError {err}")
     return t
+
+
+def read_stream(src: torch.Tensor, sink: torch.Tensor, blocks: int) -> None:
+    """Launch the streaming-read kernel over all of src (bytes a multiple of
+    16) with `blocks` workgroups; sink must hold blocks * 256 * 16 bytes."""
+    nbytes = src.numel() * src.element_size()
+    if sink.numel() * sink.element_size() < blocks * 256 * 16:
+        raise ValueError("sink too small")
+    err = _load().synth_read_stream(src.data_ptr(), nbytes, blocks, sink.data_ptr(),
+                                    torch.cuda.current_stream(src.device).cuda_stream)
+    if err != 0:
+        raise RuntimeError(f"synth_read_stream failed: hipError {err}")

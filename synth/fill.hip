@@ -4,6 +4,10 @@
 // 5-bit fields, (sum - 186) / 32, then multiplied by `scale` in float32 and
 // stored as float32 or bfloat16 (nearest, ties to even).  Holds no LLA
 // arithmetic; it only fills multi-GB input buffers on the device.
+//
+// Also here, for the benchmark's context figure: a plain streaming-read
+// kernel (synth_read_stream), the practical HBM read ceiling the decode
+// kernels are compared with.
 #include <cstdint>
 
 #include <hip/hip_runtime.h>
@@ -42,7 +46,58 @@ __global__ void fill_f32(float *dst, int64_t n, uint64_t key, int64_t first, flo
     dst[i] = hash_value(key, (uint64_t)(first + i)) * scale;
 }
 
+// Streaming read of n16 16-byte words.  Workgroup g walks the contiguous
+// range [g * per, (g + 1) * per); each thread keeps 8 nontemporal 16-byte
+// loads in flight and folds what it read with XOR.  A thread writes its fold
+// only if it equals a fixed pattern (practically never, but the compiler
+// cannot drop the loads), so the kernel's traffic is the read alone.
+constexpr int kReadUnroll = 8;
+typedef uint32_t u32x4_v __attribute__((ext_vector_type(4)));
+__global__ __launch_bounds__(256) void read_stream(const u32x4_v *src, int64_t n16, int64_t per,
+                                                    u32x4_v *sink) {
+  const int64_t b0 = (int64_t)blockIdx.x * per;
+  const int64_t b1 = b0 + per < n16 ? b0 + per : n16;
+  uint32_t a0 = 0, a1 = 0, a2 = 0, a3 = 0;
+  int64_t i = b0 + threadIdx.x;
+  for (; i + (kReadUnroll - 1) * 256 < b1; i += 256 * kReadUnroll) {
+    u32x4_v v[kReadUnroll];
+#pragma unroll
+    for (int u = 0; u < kReadUnroll; ++u) v[u] = __builtin_nontemporal_load(src + i + u * 256);
+#pragma unroll
+    for (int u = 0; u < kReadUnroll; ++u) {
+      a0 ^= v[u].x;
+      a1 ^= v[u].y;
+      a2 ^= v[u].z;
+      a3 ^= v[u].w;
+    }
+  }
+  for (; i < b1; i += 256) {  // the tail of the last workgroup's range
+    const u32x4_v v = __builtin_nontemporal_load(src + i);
+    a0 ^= v.x;
+    a1 ^= v.y;
+    a2 ^= v.z;
+    a3 ^= v.w;
+  }
+  if ((a0 ^ a1 ^ a2 ^ a3) == 0x9E3779B9u)
+    sink[(int64_t)blockIdx.x * 256 + threadIdx.x] = u32x4_v{a0, a1, a2, a3};
+}
+
 }  // namespace
+
+// Reads `bytes` (a multiple of 16) from src with `blocks` workgroups of 256
+// threads; sink holds blocks * 256 16-byte words.  Returns a hipError_t value.
+extern "C" int synth_read_stream(const void *src, int64_t bytes, int32_t blocks, void *sink,
+                                 hipStream_t stream) {
+  if (bytes <= 0 || bytes % 16 != 0 || blocks <= 0) return (int)hipErrorInvalidValue;
+  const int64_t n16 = bytes / 16;
+  // whole unrolled rounds per workgroup (2048 words), so that only the last
+  // range has a tail
+  const int64_t round = 256 * kReadUnroll;
+  const int64_t per = ((n16 + blocks - 1) / blocks + round - 1) / round * round;
+  hipLaunchKernelGGL(read_stream, dim3((unsigned)blocks), dim3(256), 0, stream,
+                     (const u32x4_v *)src, n16, per, (u32x4_v *)sink);
+  return (int)hipGetLastError();
+}
 
 // dtype 0: float32, 1: bfloat16.  Returns a hipError_t value.
 extern "C" int synth_fill(void *dst, int64_t n, int32_t dtype, uint64_t key, int64_t first,

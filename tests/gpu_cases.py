@@ -37,6 +37,35 @@ def row_rel_l2(gpu: np.ndarray, ref: np.ndarray) -> np.ndarray:
     return num / den
 
 
+def attn_rel_l2(gpu: np.ndarray, ref: np.ndarray, mu_v: np.ndarray) -> np.ndarray:
+    """Per-row error relative to the softmax-dependent part of the output:
+    ||out - out_ref|| / ||out_ref - mu_v,t||, i.e. the relative L2 of
+    (out - mu_v,t).  Over long contexts ||mu_v,t|| can exceed the attention
+    part several times, and the plain row metric then understates the error
+    of the part the kernels compute.  mu_v: broadcastable to the rows [.., H, d]."""
+    num = np.linalg.norm(gpu - ref, axis=-1)
+    den = np.maximum(np.linalg.norm(ref - mu_v, axis=-1), 1e-300)
+    return num / den
+
+
+def mu_rows(inp, w) -> np.ndarray:
+    """mu_v,t of a DecodeInputs as [H, d] (LLA-2D's [H*d] split by head)."""
+    return np.asarray(inp.mv).reshape(w.H, w.d)
+
+
+def full_precision_slab(w: Workload, b: int, layer: int) -> np.ndarray:
+    """Host N(0, 1) latents of one (sequence, layer) slab rounded to the
+    store type: full mantissas and tails, unlike the device filler's
+    multiples of 1/32.  [N, H', R] float64 exact values."""
+    v = gen.normal(w.seed, 50_000 + b * 1000 + layer, (w.N, w.store_heads, w.R))
+    return gen.as_storage(v, w.dtype)[1]
+
+
+def put_slab(store: L.LatentStore, w: Workload, b: int, layer: int, vals: np.ndarray):
+    """Overwrite store[b, layer] on the device with exact values vals."""
+    store.tensor[b, layer].copy_(to_device(vals, w.dtype, store.tensor.device))
+
+
 def new_store(w: Workload, device, tensor=None) -> L.LatentStore:
     return L.LatentStore(w.variant, w.dtype, batch=w.B, layers=w.D, max_ctx=w.N, heads=w.H,
                          d_head=w.d, loops=w.T, r_k=w.r_k, r_v=w.r_v, tensor=tensor,

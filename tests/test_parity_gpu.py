@@ -16,8 +16,9 @@ import looped_transformer_decode_amd as L
 from oracle import lla_oracle as O
 from synth import gen
 from synth.workloads import WORKLOADS, Codec
-from tests.gpu_cases import (TOL, DecodeInputs, device_slab, fill_store_on_device, from_device,
-                             host_store, new_store, row_rel_l2, to_device)
+from tests.gpu_cases import (TOL, DecodeInputs, attn_rel_l2, device_slab, fill_store_on_device,
+                             from_device, full_precision_slab, host_store, mu_rows, new_store,
+                             put_slab, row_rel_l2, to_device)
 
 pytestmark = pytest.mark.gpu
 
@@ -32,7 +33,9 @@ def small(name, **kw):
 
 
 def decode_case(w, layer, t, pos, device, n_splits=0, tid=1, scale=0.0):
-    """Host-generated store; returns (gpu [B,H,d], oracle [B,H,d], store path)."""
+    """Host-generated store; returns (gpu [B,H,d], oracle [B,H,d], store path).
+    Also checks the error of the softmax-dependent part, (out - mu_v,t),
+    against the same bound."""
     say(f"[decode] {w.name} {w.variant} {w.dtype} B={w.B} N={w.N} H={w.H} rk={w.r_k} "
         f"rv={w.r_v} layer={layer} t={t} splits={n_splits}")
     vals = host_store(w, tid)
@@ -43,7 +46,15 @@ def decode_case(w, layer, t, pos, device, n_splits=0, tid=1, scale=0.0):
     ref = np.stack([inp.oracle(vals[b, layer, :, :, :w.r_k], vals[b, layer, :, :, w.r_k:], b,
                                pos[b], None if scale == 0.0 else scale)
                     for b in range(w.B)])
+    check_attn_part(got, ref, mu_rows(inp, w), w.dtype)
     return got, ref, L.lla_decode_path(store)
+
+
+def check_attn_part(got, ref, mu_v, dtype):
+    """Print and bound the relative L2 of (out - mu_v,t) per row."""
+    a = attn_rel_l2(got, ref, mu_v).max()
+    say(f"  (out - mu_v,t) max row rel L2 {a:.3e}")
+    assert a <= TOL[dtype], a
 
 
 # ----------------------------------------------------------------- float32
@@ -270,6 +281,7 @@ def inflight_case(w, n_q, pos0, device, n_splits=0, layer=None):
                                       inp.mk.reshape(-1) if is2d else inp.mk,
                                       inp.mv.reshape(-1) if is2d else inp.mv, int(pos0[b]),
                                       variant=w.variant) for b in range(w.B)])
+    check_attn_part(got, ref, mu_rows(inp, w), w.dtype)
     return got, ref
 
 
@@ -325,6 +337,11 @@ def test_inflight_full_size_sampled(device):
     fill_store_on_device(w, store)
     rope = L.rope_table(store, device)
     layer, t = w.D - 1, w.T - 1
+    # the sampled sequences get full-precision N(0, 1) latents from the host
+    samples = sorted({0, 1, w.B - 1})
+    slabs = {b: full_precision_slab(w, b, layer) for b in samples}
+    for b in samples:
+        put_slab(store, w, b, layer, slabs[b])
     inp = DecodeInputs(w, Codec(w), layer, t, device)
     rng = np.random.default_rng(w.seed + 78)
     f32 = lambda a: a.astype(np.float32).astype(np.float64)
@@ -341,15 +358,16 @@ def test_inflight_full_size_sampled(device):
                                L.workspace(store, n_q=n_q))
     torch.cuda.synchronize()
     got = out.cpu().numpy().astype(np.float64)
-    worst = 0.0
-    for b in sorted({0, 1, w.B - 1}):
-        ck, cv = device_slab(w, b, layer)
+    worst = worst_attn = 0.0
+    for b in samples:
+        ck, cv = slabs[b][..., :w.r_k], slabs[b][..., w.r_k:]
         ref = O.decode_inflight(ck, cv, q[b], kn[b], vn[b], inp.wk, inp.wv, inp.mk, inp.mv,
                                 int(pos0[b]))
         err = row_rel_l2(got[b], ref).max()
-        worst = max(worst, err)
-        say(f"  b={b} pos0={pos0[b]} max row rel L2 {err:.3e}")
-    assert worst <= TOL["bf16"]
+        ea = attn_rel_l2(got[b], ref, mu_rows(inp, w)).max()
+        worst, worst_attn = max(worst, err), max(worst_attn, ea)
+        say(f"  b={b} pos0={pos0[b]} max row rel L2 {err:.3e}; (out - mu_v,t) {ea:.3e}")
+    assert worst <= TOL["bf16"] and worst_attn <= TOL["bf16"]
     del store
     torch.cuda.empty_cache()
 
@@ -513,16 +531,26 @@ def test_full_size_sampled(device, name):
     rng = np.random.default_rng(w.seed)
     pos = np.full(w.B, w.N - 1)
     pos[1::3] = rng.integers(0, w.N, size=len(pos[1::3]))
-    got = inp.run(store, pos, rope)
     samples = sorted({0, 1, w.B - 1, int(rng.integers(0, w.B))})
-    worst = 0.0
+    # half of the sampled sequences hold full-precision N(0, 1) latents from
+    # the host (full mantissas and tails), the rest the device filler's values
+    host = {b: full_precision_slab(w, b, layer) for b in samples[::2]}
+    for b, v in host.items():
+        put_slab(store, w, b, layer, v)
+    got = inp.run(store, pos, rope)
+    worst = worst_attn = 0.0
     for b in samples:
-        ck, cv = device_slab(w, b, layer)
+        if b in host:
+            ck, cv = host[b][..., :w.r_k], host[b][..., w.r_k:]
+        else:
+            ck, cv = device_slab(w, b, layer)
         ref = inp.oracle(ck, cv, b, pos[b])
         err = row_rel_l2(got[b], ref).max()
-        worst = max(worst, err)
-        say(f"  b={b} pos={pos[b]} max row rel L2 {err:.3e}")
-    assert worst <= TOL["bf16"]
+        ea = attn_rel_l2(got[b], ref, mu_rows(inp, w)).max()
+        worst, worst_attn = max(worst, err), max(worst_attn, ea)
+        say(f"  b={b} pos={pos[b]} ({'host N(0,1)' if b in host else 'device filler'}) "
+            f"max row rel L2 {err:.3e}; (out - mu_v,t) {ea:.3e}")
+    assert worst <= TOL["bf16"] and worst_attn <= TOL["bf16"]
     assert np.isfinite(got).all()
     del store
     torch.cuda.empty_cache()
