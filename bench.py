@@ -81,6 +81,9 @@ def parse():
     ap.add_argument("--read-ceiling", type=float, default=0.0, metavar="GB",
                     help="instead of the benchmark, time a plain streaming-read kernel over a "
                          "buffer of this size (the practical HBM read ceiling)")
+    ap.add_argument("--mfma-ceiling", action="store_true",
+                    help="instead of the benchmark, time a register-only bf16 MFMA kernel "
+                         "(the practical matrix-core ceiling)")
     ap.add_argument("--no-encode", action="store_true", help=argparse.SUPPRESS)
     ap.add_argument("--inflight", action="store_true",
                     help="decode with the step's n_new tokens in flight (multi-query causal "
@@ -616,6 +619,41 @@ def run_read_ceiling(args, torch):
           flush=True)
 
 
+def run_mfma_ceiling(args, torch):
+    """Register-only v_mfma_f32_32x32x16_bf16 chains (four independent
+    accumulators per wave) at one to four waves per SIMD: the bf16
+    matrix-core throughput this box sustains, against the 2.5 PFLOP/s
+    nominal peak."""
+    from synth.device import mfma_spin
+    dev = torch.device("cuda:0")
+    iters = 4096
+    results = {}
+    for waves_per_simd in (1, 2, 4):
+        blocks = 256 * waves_per_simd            # 4 waves per workgroup: one per SIMD
+        sink = torch.empty(blocks * 256, dtype=torch.float32, device=dev)
+        mfma_spin(blocks, 64, sink)
+        torch.cuda.synchronize()
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+        ev[0].record()
+        mfma_spin(blocks, iters, sink)
+        ev[1].record()
+        torch.cuda.synchronize()
+        ms = ev[0].elapsed_time(ev[1])
+        flops = blocks * 4 * 4 * iters * 32768
+        results[waves_per_simd] = (ms, flops / (ms / 1e3) / 1e12)
+        log(f"[bench] mfma ceiling: {waves_per_simd} wave(s)/SIMD, {ms * 1e3:.1f} us: "
+            f"{results[waves_per_simd][1]:.1f} TFLOP/s")
+    best = max(results, key=lambda k: results[k][1])
+    print(json.dumps({"metric": "bf16 MFMA TFLOP/s (register-only 32x32x16 chains, context for "
+                                "the LLA-2D roofline fraction)",
+                      "value": round(results[best][1], 1), "unit": "TFLOP/s",
+                      "peak": MFMA_BF16_PEAK_TFLOPS,
+                      "frac": round(results[best][1] / MFMA_BF16_PEAK_TFLOPS, 4),
+                      "kernel": "mfma_spin (synth/fill.hip)", "waves_per_simd": best,
+                      "sweep": {str(k): {"us": round(v[0] * 1e3, 1), "TFLOPs": round(v[1], 1)}
+                                for k, v in results.items()}}), flush=True)
+
+
 def main():
     args = parse()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
@@ -653,6 +691,9 @@ def main():
 
     if args.read_ceiling > 0:
         run_read_ceiling(args, torch)
+        return
+    if args.mfma_ceiling:
+        run_mfma_ceiling(args, torch)
         return
 
     import looped_transformer_decode_amd as L

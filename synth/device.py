@@ -23,6 +23,9 @@ def _load():
         L.synth_read_stream.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32,
                                         ctypes.c_void_p, ctypes.c_void_p]
         L.synth_read_stream.restype = ctypes.c_int
+        L.synth_mfma_spin.argtypes = [ctypes.c_int32, ctypes.c_int32, ctypes.c_void_p,
+                                      ctypes.c_void_p]
+        L.synth_mfma_spin.restype = ctypes.c_int
         _lib = L
     return _lib
 
@@ -49,3 +52,14 @@ def read_stream(src: torch.Tensor, sink: torch.Tensor, blocks: int) -> None:
                                     torch.cuda.current_stream(src.device).cuda_stream)
     if err != 0:
         raise RuntimeError(f"synth_read_stream failed: hipError {err}")
+
+
+def mfma_spin(blocks: int, iters: int, sink: torch.Tensor) -> None:
+    """Launch the register-only MFMA kernel: blocks x 4 waves, each 4 * iters
+    v_mfma_f32_32x32x16_bf16; sink: float32, at least blocks * 256 values."""
+    if sink.numel() < blocks * 256 or sink.dtype != torch.float32:
+        raise ValueError("sink too small")
+    err = _load().synth_mfma_spin(blocks, iters, sink.data_ptr(),
+                                  torch.cuda.current_stream(sink.device).cuda_stream)
+    if err != 0:
+        raise RuntimeError(f"synth_mfma_spin failed: hipError {err}")

@@ -5,8 +5,9 @@
 // stored as float32 or bfloat16 (nearest, ties to even).  Holds no LLA
 // arithmetic; it only fills multi-GB input buffers on the device.
 //
-// Also here, for the benchmark's context figure: a plain streaming-read
-// kernel (synth_read_stream), the practical HBM read ceiling the decode
+// Also here, for the benchmark's context figures: a plain streaming-read
+// kernel (synth_read_stream) and a register-only matrix-core kernel
+// (synth_mfma_spin), the practical HBM and bf16 MFMA ceilings the decode
 // kernels are compared with.
 #include <cstdint>
 
@@ -82,7 +83,43 @@ __global__ __launch_bounds__(256) void read_stream(const u32x4_v *src, int64_t n
     sink[(int64_t)blockIdx.x * 256 + threadIdx.x] = u32x4_v{a0, a1, a2, a3};
 }
 
+// Matrix-core ceiling: every wave runs `iters` rounds of four independent
+// v_mfma_f32_32x32x16_bf16 accumulations on operands held in registers (no
+// memory traffic), then writes its sum only if it equals a fixed pattern.
+typedef short bf16x8_v __attribute__((ext_vector_type(8)));
+typedef float f32x16_v __attribute__((ext_vector_type(16)));
+__global__ __launch_bounds__(256) void mfma_spin(int iters, float *sink) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  const int lane = threadIdx.x & 63;
+  bf16x8_v a, b;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    a[e] = (short)(0x3F80 + ((lane + e) & 7));  // bf16 values near 1
+    b[e] = (short)(0x3C00 + ((lane * 3 + e) & 7));
+  }
+  f32x16_v c0 = {}, c1 = {}, c2 = {}, c3 = {};
+  for (int i = 0; i < iters; ++i) {
+    c0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c0, 0, 0, 0);
+    c1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(b, a, c1, 0, 0, 0);
+    c2 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, a, c2, 0, 0, 0);
+    c3 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(b, b, c3, 0, 0, 0);
+  }
+  float t = 0.f;
+#pragma unroll
+  for (int k = 0; k < 16; ++k) t += c0[k] + c1[k] + c2[k] + c3[k];
+  if (t == 1234.5f) sink[blockIdx.x * 256 + threadIdx.x] = t;
+#endif
+}
+
 }  // namespace
+
+// Launches the matrix-core ceiling kernel: `blocks` workgroups of four waves,
+// each wave 4 * iters MFMAs of 32x32x16 (32768 flop each).
+extern "C" int synth_mfma_spin(int32_t blocks, int32_t iters, float *sink, hipStream_t stream) {
+  if (blocks <= 0 || iters <= 0) return (int)hipErrorInvalidValue;
+  hipLaunchKernelGGL(mfma_spin, dim3((unsigned)blocks), dim3(256), 0, stream, iters, sink);
+  return (int)hipGetLastError();
+}
 
 // Reads `bytes` (a multiple of 16) from src with `blocks` workgroups of 256
 // threads; sink holds blocks * 256 16-byte words.  Returns a hipError_t value.
