@@ -80,54 +80,244 @@ struct Centred {
 };
 
 // C[g][i][j] = sum_k A(g, i, k) B(g, k, j), i < M, j < Nn.  64 x 64 output
-// tile per block, 16 x 16 threads with a 4 x 4 micro-tile each.
+// tile per block.  The operands are staged in LDS in chunks of 16 k (through
+// the loaders, which centre or bound-check element by element); the four
+// waves each multiply one 32 x 32 quarter of the tile on the fp32 matrix
+// cores (v_mfma_f32_32x32x2_f32: exact fp32 products, fp32 sums), with the
+// next chunk's elements loaded into registers while the current one is
+// multiplied.
+typedef __attribute__((__vector_size__(16 * sizeof(float)))) float f32x16_t;
 template <class LA, class LB>
 __global__ __launch_bounds__(kThreads) void gemm(LA A, LB B, float *C, int64_t c_sg, int ldc, int M,
                                                  int Nn, int Kd) {
-  __shared__ __align__(16) float As[kBK][kT + 4];
-  __shared__ __align__(16) float Bs[kBK][kT + 4];
+  __shared__ __align__(16) float As[2][kBK][kT + 4];
+  __shared__ __align__(16) float Bs[2][kBK][kT + 4];
   const int g = blockIdx.z, i0 = blockIdx.y * kT, j0 = blockIdx.x * kT;
-  const int tid = threadIdx.x, tx = tid % 16, ty = tid / 16;
-  float acc[4][4] = {};
-  for (int k0 = 0; k0 < Kd; k0 += kBK) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wi = wave >> 1, wj = wave & 1;  // this wave's 32 x 32 quarter
+  constexpr int PER = kBK * kT / kThreads;   // elements per thread per operand and chunk
+  float ra[PER], rb[PER];
+  auto fetch = [&](int k0) {
 #pragma unroll
-    for (int q = 0; q < kBK * kT / kThreads; ++q) {
+    for (int q = 0; q < PER; ++q) {
       const int e = tid + kThreads * q, kk = e / kT, ii = e % kT;
-      As[kk][ii] = A(g, i0 + ii, k0 + kk);
-      Bs[kk][ii] = B(g, k0 + kk, j0 + ii);
+      ra[q] = A(g, i0 + ii, k0 + kk);
+      rb[q] = B(g, k0 + kk, j0 + ii);
     }
-    __syncthreads();
+  };
+  auto stage = [&](int buf) {
 #pragma unroll
-    for (int kk = 0; kk < kBK; ++kk) {
-      const float4 a = *reinterpret_cast<const float4 *>(&As[kk][4 * ty]);
-      const float4 b = *reinterpret_cast<const float4 *>(&Bs[kk][4 * tx]);
-      const float av[4] = {a.x, a.y, a.z, a.w}, bv[4] = {b.x, b.y, b.z, b.w};
-#pragma unroll
-      for (int r = 0; r < 4; ++r)
-#pragma unroll
-        for (int c = 0; c < 4; ++c) acc[r][c] = fmaf(av[r], bv[c], acc[r][c]);
+    for (int q = 0; q < PER; ++q) {
+      const int e = tid + kThreads * q, kk = e / kT, ii = e % kT;
+      As[buf][kk][ii] = ra[q];
+      Bs[buf][kk][ii] = rb[q];
     }
+  };
+  f32x16_t acc = {};
+  fetch(0);
+  stage(0);
+  __syncthreads();
+  int buf = 0;
+  for (int k0 = 0; k0 < Kd; k0 += kBK) {
+    const bool more = k0 + kBK < Kd;
+    if (more) fetch(k0 + kBK);
+#pragma unroll
+    for (int kk = 0; kk < kBK; kk += 2) {
+      // A: row wi*32 + lane%32, k = kk + lane/32;  B: column wj*32 + lane%32
+      const float a = As[buf][kk + (lane >> 5)][wi * 32 + (lane & 31)];
+      const float b = Bs[buf][kk + (lane >> 5)][wj * 32 + (lane & 31)];
+      acc = __builtin_amdgcn_mfma_f32_32x32x2f32(a, b, acc, 0, 0, 0);
+    }
+    if (more) stage(buf ^ 1);
     __syncthreads();
+    buf ^= 1;
   }
+  // accumulator r: row 8 (r / 4) + 4 (lane / 32) + r % 4, column lane % 32
+  const int j = j0 + wj * 32 + (lane & 31);
+  if (j < Nn) {
 #pragma unroll
-  for (int r = 0; r < 4; ++r) {
-    const int i = i0 + 4 * ty + r;
-    if (i >= M) continue;
-#pragma unroll
-    for (int c = 0; c < 4; ++c) {
-      const int j = j0 + 4 * tx + c;
-      if (j < Nn) C[g * c_sg + (int64_t)i * ldc + j] = acc[r][c];
+    for (int r = 0; r < 16; ++r) {
+      const int i = i0 + wi * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+      if (i < M) C[g * c_sg + (int64_t)i * ldc + j] = acc[r];
     }
   }
 }
 
+// Gram matrix of the centred calibration rows, C[g] = Xc^T Xc with
+// Xc[n][f] = x[n][g][f] - mu[g][f], on the fp32 matrix cores.  C is
+// symmetric: only the 128 x 128 tiles (ti, tj) with ti <= tj are computed,
+// and those off the diagonal are also written transposed (through LDS, so
+// that both stores are coalesced).  Four waves, each a 64 x 64 quarter of
+// the tile as 2 x 2 blocks of v_mfma_f32_32x32x2_f32.  Samples are staged in
+// LDS in chunks of 32, centred and in fp32, feature-contiguous; the next
+// chunk is loaded into registers while the current one is multiplied.
+constexpr int kGT = 128;  // output tile
+constexpr int kGN = 32;   // samples per chunk
+typedef uint32_t u32x4_v __attribute__((ext_vector_type(4)));
+constexpr int kGP = kGT + 4;
+constexpr int kGramLds = 2 * 2 * kGN * kGP * 4;  // [buf][operand][n][feature] fp32
+static_assert(kGT * (kGT + 1) * 4 <= kGramLds, "the transposed store reuses the staging LDS");
+
+template <typename E>
+__global__ __launch_bounds__(kThreads) void gram(const E *x, const float *mu, int G, int N, int K,
+                                                  float *C) {
+  extern __shared__ __align__(16) float gs[];
+  const int T = (K + kGT - 1) / kGT;
+  int t = blockIdx.x, ti = 0;
+  while (t >= T - ti) {  // upper-triangle tile (ti, tj), ti <= tj
+    t -= T - ti;
+    ++ti;
+  }
+  const int tj = ti + t, g = blockIdx.y;
+  const int i0 = ti * kGT, j0 = tj * kGT;
+  const bool diag = ti == tj;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wi = wave >> 1, wj = wave & 1;
+  // This thread loads features f8 .. f8 + 7 of the tile (one 16-byte vector
+  // of bf16, or two of fp32) of chunk rows nr and nr + 16.  Loads are never
+  // conditional (indices are clamped, values past N or K zeroed afterwards),
+  // so that they all go out before the first is waited for.
+  const int f8 = (tid % (kGT / 8)) * 8, nr = tid / (kGT / 8);
+  const int fa = i0 + f8, fb = j0 + f8;
+  float mua[8], mub[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    mua[e] = fa + e < K ? mu[(int64_t)g * K + fa + e] : 0.f;
+    mub[e] = fb + e < K ? mu[(int64_t)g * K + fb + e] : 0.f;
+  }
+  const bool fa_ok = fa < K, fb_ok = fb < K;  // K % 8 == 0: whole vectors in or out
+  const int fa_c = fa_ok ? fa : 0, fb_c = fb_ok ? fb : 0;
+  // raw 16-byte vectors of the two rows (bf16: one per row, fp32: two),
+  // converted and centred only when staged, after the chunk's products
+  constexpr int NV = sizeof(E) == 2 ? 1 : 2;
+  u32x4_v ra[2][NV], rb[2][NV];
+  auto fetch = [&](int n0) {
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+      const int n = min(n0 + nr + 16 * q, N - 1);
+      const int64_t row = ((int64_t)n * G + g) * K;
+      const u32x4_v *pa = reinterpret_cast<const u32x4_v *>(x + row + fa_c);
+      const u32x4_v *pb = reinterpret_cast<const u32x4_v *>(x + row + (diag ? fa_c : fb_c));
+#pragma unroll
+      for (int v = 0; v < NV; ++v) {
+        ra[q][v] = pa[v];
+        rb[q][v] = pb[v];  // on the diagonal a second copy of the same features (unused)
+      }
+    }
+  };
+  auto unpack = [&](const u32x4_v (&raw)[NV], float (&dst)[8]) {
+    if constexpr (sizeof(E) == 2) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        dst[2 * e] = bf16_lo(raw[0][e]);
+        dst[2 * e + 1] = bf16_hi(raw[0][e]);
+      }
+    } else {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) dst[e] = __uint_as_float(raw[e / 4][e % 4]);
+    }
+  };
+  auto stage = [&](int buf, int n0) {
+    float *sa = gs + (buf * 2) * kGN * kGP, *sb = sa + kGN * kGP;
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+      const bool nok = n0 + nr + 16 * q < N;
+      float va[8], vb[8];
+      unpack(ra[q], va);
+      unpack(rb[q], vb);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        va[e] = nok && fa_ok ? va[e] - mua[e] : 0.f;
+        vb[e] = nok && fb_ok ? vb[e] - mub[e] : 0.f;
+      }
+      float *da = sa + (nr + 16 * q) * kGP + f8;
+      *reinterpret_cast<float4 *>(da) = make_float4(va[0], va[1], va[2], va[3]);
+      *reinterpret_cast<float4 *>(da + 4) = make_float4(va[4], va[5], va[6], va[7]);
+      if (!diag) {
+        float *db = sb + (nr + 16 * q) * kGP + f8;
+        *reinterpret_cast<float4 *>(db) = make_float4(vb[0], vb[1], vb[2], vb[3]);
+        *reinterpret_cast<float4 *>(db + 4) = make_float4(vb[4], vb[5], vb[6], vb[7]);
+      }
+    }
+  };
+  f32x16_t acc[2][2];
+#pragma unroll
+  for (int a = 0; a < 2; ++a)
+#pragma unroll
+    for (int b = 0; b < 2; ++b) acc[a][b] = f32x16_t{};
+  fetch(0);
+  stage(0, 0);
+  __syncthreads();
+  int buf = 0;
+  for (int n0 = 0; n0 < N; n0 += kGN) {
+    const bool more = n0 + kGN < N;
+    if (more) fetch(n0 + kGN);
+    __builtin_amdgcn_sched_barrier(0);  // the loads go out before the products
+    const float *sa = gs + (buf * 2) * kGN * kGP;
+    const float *sb = diag ? sa : sa + kGN * kGP;
+#pragma unroll
+    for (int kk = 0; kk < kGN; kk += 2) {
+      const int r = (kk + (lane >> 5)) * kGP + (lane & 31);
+      float av[2], bv[2];
+#pragma unroll
+      for (int a = 0; a < 2; ++a) av[a] = sa[r + wi * 64 + 32 * a];
+#pragma unroll
+      for (int b = 0; b < 2; ++b) bv[b] = sb[r + wj * 64 + 32 * b];
+#pragma unroll
+      for (int a = 0; a < 2; ++a)
+#pragma unroll
+        for (int b = 0; b < 2; ++b)
+          acc[a][b] = __builtin_amdgcn_mfma_f32_32x32x2f32(av[a], bv[b], acc[a][b], 0, 0, 0);
+    }
+    __builtin_amdgcn_sched_barrier(0);  // and are waited for only after them
+    if (more) stage(buf ^ 1, n0 + kGN);
+    __syncthreads();
+    buf ^= 1;
+  }
+  // tile rows i (features of the first operand), columns j: accumulator r of
+  // block (a, b) is row 64 wi + 32 a + 8 (r / 4) + 4 (lane / 32) + r % 4,
+  // column 64 wj + 32 b + lane % 32
+  float *Cg = C + (int64_t)g * K * K;
+  float *tr = gs;  // [kGT][kGT + 1]: the tile, for the transposed store
+#pragma unroll
+  for (int a = 0; a < 2; ++a)
+#pragma unroll
+    for (int b = 0; b < 2; ++b)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int il = 64 * wi + 32 * a + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+        const int jl = 64 * wj + 32 * b + (lane & 31);
+        if (i0 + il < K && j0 + jl < K) Cg[(int64_t)(i0 + il) * K + j0 + jl] = acc[a][b][r];
+        if (!diag) tr[il * (kGT + 1) + jl] = acc[a][b][r];
+      }
+  if (diag) return;  // workgroup-uniform
+  __syncthreads();
+  for (int e = tid; e < kGT * kGT; e += kThreads) {
+    const int jl = e / kGT, il = e % kGT;  // C[j][i] = tile[i][j], consecutive i per lane
+    if (j0 + jl < K && i0 + il < K) Cg[(int64_t)(j0 + jl) * K + i0 + il] = tr[il * (kGT + 1) + jl];
+  }
+}
+
+// mu[g][f] = (1/N) sum_n x[n][g][f] in fp64: a block covers 32 features;
+// its 8 row groups (n = r, r + 8, ...) sum in parallel and are added in a
+// fixed order at the end.
+constexpr int kMeanF = 32, kMeanR = kThreads / kMeanF;
 template <typename E>
 __global__ __launch_bounds__(kThreads) void column_mean(const E *x, int G, int N, int K, float *mu) {
-  const int g = blockIdx.y, f = blockIdx.x * kThreads + threadIdx.x;
-  if (f >= K) return;
+  __shared__ double part[kMeanR][kMeanF];
+  const int g = blockIdx.y, fx = threadIdx.x % kMeanF, ry = threadIdx.x / kMeanF;
+  const int f = blockIdx.x * kMeanF + fx;
   double s = 0.0;
-  for (int n = 0; n < N; ++n) s += load_elem(x, ((int64_t)n * G + g) * K + f);
-  mu[(int64_t)g * K + f] = (float)(s / N);
+  if (f < K)
+    for (int n = ry; n < N; n += kMeanR) s += load_elem(x, ((int64_t)n * G + g) * K + f);
+  part[ry][fx] = s;
+  __syncthreads();
+  if (ry == 0 && f < K) {
+    double t = 0.0;
+#pragma unroll
+    for (int r = 0; r < kMeanR; ++r) t += part[r][fx];
+    mu[(int64_t)g * K + f] = (float)(t / N);
+  }
 }
 
 // SplitMix64 (Steele, Lea and Flood, OOPSLA 2014) at counter i: the
@@ -172,29 +362,30 @@ __global__ __launch_bounds__(kThreads) void small_gram64(const float *P, const f
 // Cholesky A = L L^T of one codec's m x m matrix (fp64, in LDS, with a tiny
 // diagonal shift so that a rank-deficient block cannot break it), then
 // Rinv = (L^T)^-1, the factor that makes Y Rinv orthonormal.
+// Factorisation step j: every thread forms the pivot itself and updates its
+// (row, column) share of the trailing lower triangle, scaling column j on the
+// fly; after the step's one barrier the column is stored scaled (the next
+// step reads none of it).
 __global__ __launch_bounds__(kThreads) void chol_inv(const double *A, int m, float *Rinv) {
   extern __shared__ double L[];  // [m][m]
-  const int g = blockIdx.x, tid = threadIdx.x;
+  const int g = blockIdx.x, tid = threadIdx.x, ty = tid / 16, tx = tid % 16;
   const double *Ag = A + (int64_t)g * m * m;
   for (int e = tid; e < m * m; e += kThreads) L[e] = Ag[e];
   __syncthreads();
   double dmax = 0.0;
   for (int i = 0; i < m; ++i) dmax = fmax(dmax, L[i * m + i]);
   const double shift = 1e-13 * dmax + 1e-300;
-  __syncthreads();
   for (int j = 0; j < m; ++j) {
-    if (tid == 0) L[j * m + j] = sqrt(fmax(L[j * m + j] + shift, shift));
-    __syncthreads();
-    const double djj = L[j * m + j];
-    for (int i = j + 1 + tid; i < m; i += kThreads) L[i * m + j] /= djj;
-    __syncthreads();
-    const int rest = m - j - 1;
-    for (int e = tid; e < rest * rest; e += kThreads) {
-      const int i = j + 1 + e / rest, k = j + 1 + e % rest;
-      if (k <= i) L[i * m + k] -= L[i * m + j] * L[k * m + j];
+    const double djj = sqrt(fmax(L[j * m + j] + shift, shift));
+    const double inv = 1.0 / djj;
+    for (int i = j + 1 + ty; i < m; i += 16) {
+      const double lij = L[i * m + j] * inv;
+      for (int k = j + 1 + tx; k <= i; k += 16) L[i * m + k] -= lij * (L[k * m + j] * inv);
     }
     __syncthreads();
+    for (int i = j + tid; i < m; i += kThreads) L[i * m + j] = i == j ? djj : L[i * m + j] * inv;
   }
+  __syncthreads();
   // Linv (lower triangular) goes into the unused upper triangle, transposed:
   // Linv[i][c] (i > c) at [c][i]; thread c forms column c from the rows of L
   // and its own earlier entries, all in LDS.
@@ -202,10 +393,21 @@ __global__ __launch_bounds__(kThreads) void chol_inv(const double *A, int m, flo
   for (int c = tid; c < m; c += kThreads) {
     const double inv_cc = 1.0 / L[c * m + c];
     Rg[(int64_t)c * m + c] = (float)inv_cc;
+    const double *Lc = L + c * m;  // this column's Linv entries, at [c][k]
     for (int i = c + 1; i < m; ++i) {
-      double s = L[i * m + c] * inv_cc;
-      for (int k = c + 1; k < i; ++k) s += L[i * m + k] * L[c * m + k];
-      const double v = -s / L[i * m + i];
+      const double *Li = L + i * m;
+      // four independent partial sums: the LDS reads of one step need not
+      // wait for the previous step's sum
+      double s0 = Li[c] * inv_cc, s1 = 0.0, s2 = 0.0, s3 = 0.0;
+      int k = c + 1;
+      for (; k + 3 < i; k += 4) {
+        s0 += Li[k] * Lc[k];
+        s1 += Li[k + 1] * Lc[k + 1];
+        s2 += Li[k + 2] * Lc[k + 2];
+        s3 += Li[k + 3] * Lc[k + 3];
+      }
+      for (; k < i; ++k) s0 += Li[k] * Lc[k];
+      const double v = -((s0 + s1) + (s2 + s3)) / Li[i];
       L[c * m + i] = v;
       Rg[(int64_t)c * m + i] = (float)v;  // Rinv[c][i] = Linv[i][c]
     }
@@ -406,12 +608,21 @@ static hipError_t run(const SvdParams &p, hipStream_t st) {
 #define LLA_TRY(call)                   \
   if ((e = (call)) != hipSuccess) return e;
 
-  hipLaunchKernelGGL(column_mean<E>, dim3((K + kThreads - 1) / kThreads, G), dim3(kThreads), 0, st,
+  hipLaunchKernelGGL(column_mean<E>, dim3((K + kMeanF - 1) / kMeanF, G), dim3(kThreads), 0, st,
                      x, G, N, K, p.mu);
   LLA_TRY(hipGetLastError());
   // Gram matrix of the centred rows: C = Xc^T Xc  (K x K, contraction over N)
-  LLA_TRY(launch_gemm(Centred<E, true>{x, p.mu, G, N, K}, Centred<E, false>{x, p.mu, G, N, K}, C,
-                      (int64_t)K * K, K, G, K, K, N, st));
+  if (K % 8 == 0 && ((uintptr_t)x & 15u) == 0) {  // whole 16-byte feature vectors
+    const int T = (K + kGT - 1) / kGT;
+    LLA_TRY(hipFuncSetAttribute(reinterpret_cast<const void *>(gram<E>),
+                                hipFuncAttributeMaxDynamicSharedMemorySize, kGramLds));
+    hipLaunchKernelGGL(gram<E>, dim3((unsigned)(T * (T + 1) / 2), G), dim3(kThreads), kGramLds, st,
+                       x, p.mu, G, N, K, C);
+    LLA_TRY(hipGetLastError());
+  } else {
+    LLA_TRY(launch_gemm(Centred<E, true>{x, p.mu, G, N, K}, Centred<E, false>{x, p.mu, G, N, K},
+                        C, (int64_t)K * K, K, G, K, K, N, st));
+  }
   const int64_t qn = (int64_t)G * K * m;
   hipLaunchKernelGGL(start_block, dim3((unsigned)std::min<int64_t>((qn + kThreads - 1) / kThreads, 65536)),
                      dim3(kThreads), 0, st, Q, qn);
