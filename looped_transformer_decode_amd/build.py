@@ -48,10 +48,16 @@ def _run(cmd):
 NO_SPILL = {"decode_mfma.hip", "decode2d_mfma.hip"}
 
 
+# Per-source code-generation options.  The multi-query decode feeds every
+# MFMA result straight into vector arithmetic: with the VGPR form of the
+# MFMA instructions its results need no accumulator-register copies.
+SOURCE_FLAGS = {"decode_mq.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
+
+
 def _compile(src: str, obj: str):
-    extra = []
+    extra = list(SOURCE_FLAGS.get(os.path.basename(src), []))
     if os.path.basename(src) in NO_SPILL:
-        extra = ["-Rpass-analysis=kernel-resource-usage"]
+        extra += ["-Rpass-analysis=kernel-resource-usage"]
     out = _run([HIPCC, *COMMON, "-x", "hip", *extra, "-c", src, "-o", obj])
     if extra:
         spills = [l for l in out.splitlines()
@@ -61,6 +67,18 @@ def _compile(src: str, obj: str):
                                + "\n".join(spills))
         out = ""  # the resource remarks are not build output
     return out
+
+
+def _check_defined(lib: str):
+    """A kernel whose host pass could not instantiate it leaves its launch
+    stub undefined while the compile still succeeds; refuse such a library."""
+    r = subprocess.run(["nm", "-D", "--undefined-only", lib], stdout=subprocess.PIPE,
+                       stderr=subprocess.STDOUT, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"nm failed on {lib}:\n{r.stdout}")
+    missing = [l.split()[-1] for l in r.stdout.splitlines() if "_ZN3lla" in l]
+    if missing:
+        raise RuntimeError(f"{lib}: undefined library symbols:\n" + "\n".join(missing))
 
 
 def build(verbose: bool = False) -> list[str]:
@@ -79,6 +97,7 @@ def build(verbose: bool = False) -> list[str]:
     objs = [o for _, o in jobs[:-1]]
     tmp = LIB + ".tmp"
     _run([HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs])
+    _check_defined(tmp)
     os.replace(tmp, LIB)
     tmp = SYNTH_LIB + ".tmp"
     _run([HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, jobs[-1][1]])
