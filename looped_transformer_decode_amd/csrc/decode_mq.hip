@@ -10,25 +10,30 @@
 //
 // Reconstruct first.  With n_q queries sharing every tile, rebuilding the
 // keys once and multiplying them by all queries beats the single-query
-// bilinear form (whose matrix work grows with the number of queries).  Per
-// 32-slot tile and head (one wave per head, four heads per workgroup):
-//  * K^T = W_up,k,t [c | 1]^T on v_mfma_f32_32x32x16_bf16, the mean folded
-//    in as two extra latent components (mu split exactly into bf16 hi + lo)
-//    of value one.  Lane l holds slot l%32 and dims 32T + 8c + 4(l/32) + e,
-//    so the rotate-half partner (dim + 64) sits in the same lane; RoPE is
-//    applied in registers and four consecutive dims are stored to LDS with
-//    one 8-byte write (16-byte chunks XOR-swizzled by slot).
-//  * S = Q K^T on v_mfma_f32_16x16x32_bf16 (queries x slots, K = d); lane
-//    l owns query rows 4(l/16) + i, which are also the rows it owns in the
-//    value accumulator, so softmax state and rescaling stay in registers.
-//  * P C_v on v_mfma_f32_16x16x32_bf16 (queries x value columns, K = 32
-//    slots), P through LDS, C_v gathered from a staged tile whose row pitch
-//    spreads the four slot groups over distinct banks.
-// Latent rows are read with direct 16-byte global loads, the next tile's
-// issued as soon as the current one's have been consumed.  The rotation of
-// each (slot, dim) comes from the RoPE table's bf16 phi tile of the 32 slots,
-// copied HBM-to-LDS once per workgroup (a quarter by each wave, two buffers,
-// one barrier per tile); every other LDS region is private to a wave.
+// bilinear form (whose matrix work grows with the number of queries).  One
+// wave per head, four heads per workgroup; per 32-slot tile and wave, all on
+// v_mfma_f32_16x16x32_bf16 with every operand in registers:
+//  * K^T = W_up,k,t [c | 1]^T per 16-dim tile and 16-slot half, the mean
+//    folded in as two extra latent components (mu split exactly into bf16
+//    hi + lo) of value one.  Lane l holds slot l%16 and dims 16a + 4(l/16)
+//    + 0..3, so the rotate-half partner (dim + 64, tile a + 4) sits in the
+//    same lane and RoPE is applied in registers.
+//  * S^T = K Q^T (slots x queries): the rotated keys of tiles a and a + 4
+//    are exactly the A operand of one k-step, with the dims of a k-step
+//    taken in the order the lanes hold them (the queries' B operand uses
+//    the same order).  Lane l ends with query l%16 and slots 4(l/16) + 0..3
+//    of each half.
+//  * acc^T += C_v^T P^T (value columns x queries, K = the 32 slots): those
+//    eight softmax weights per lane are the B operand as they stand (slots
+//    again in lane order), C_v^T is gathered from the staged tile in the
+//    same order, and the output lane keeps query l%16, so the softmax state
+//    and the rescaling of its accumulator stay in the lane.
+// Latent tiles stream HBM -> LDS directly (buffer loads into LDS, no
+// register staging) into a ring of two to four tiles per wave; a tile's
+// 16-byte chunks are rotated within each slot record so that the 16 slots a
+// read touches fall in distinct banks.  The rotation of each (slot, dim)
+// comes from the RoPE table's bf16 phi tile of the 32 slots, copied into
+// LDS a quarter by each wave, two buffers, one barrier per tile.
 #include "lla_device.h"
 #include "lla_internal.h"
 
@@ -36,7 +41,6 @@ namespace lla {
 namespace mq {
 
 typedef __attribute__((__vector_size__(8 * sizeof(short)))) short bf16x8_t;
-typedef __attribute__((__vector_size__(16 * sizeof(float)))) float f32x16_t;
 typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4_t;
 typedef __attribute__((__vector_size__(4 * sizeof(uint32_t)))) uint32_t u32x4_t;
 typedef __attribute__((__vector_size__(2 * sizeof(uint32_t)))) uint32_t u32x2_t;
@@ -46,63 +50,69 @@ constexpr int kHalf = kD / 2;
 constexpr int kTile = 32;
 constexpr int kWaves = 4;
 constexpr int kThreads = 64 * kWaves;
-constexpr int kQ = 16;               // query rows of the MFMA tiles
+constexpr int kQ = 16;               // query columns of the MFMA tiles
 constexpr float kRescaleGap = 8.0f;  // log2 domain
 constexpr int kPhiTileBytes = kTile * kD * 2;  // bf16 phi rows of one 32-slot tile
+constexpr int kLdsPerGroup = 80 * 1024;        // two workgroups per CU
+// Cache policy of the latent loads: nontemporal (each latent is read once
+// per call); the phi tiles, shared by every workgroup, use the default.
+constexpr int kCachePolicyStream = 2;
 #define LDS_AS __attribute__((address_space(3)))
+
+constexpr int gcd16(int a) { return (a % 16 == 0) ? 16 : (a % 8 == 0) ? 8 : (a % 4 == 0) ? 4 : (a % 2 == 0) ? 2 : 1; }
 
 template <int RK, int RV>
 struct Cfg {
-  static constexpr int KS = RK / 16;                       // latent k-steps (+1 for mu)
-  static constexpr int VCH = RV / 8;                       // 16-byte chunks of a V row
-  static constexpr int VLOADS = (kTile * VCH + 63) / 64;   // V chunks per lane
-  static constexpr int VPITCH = RV + 4;                    // staged V row, elements
-  static constexpr int VB = RV / 16;                       // value column blocks
-  static constexpr int PPITCH = kTile + 8;                 // staged P row, elements
-  static constexpr int K_OFF = 0;
-  static constexpr int V_OFF = kTile * kD * 2;
-  static constexpr int P_OFF = V_OFF + (kTile * VPITCH * 2 + 15) / 16 * 16;
-  static constexpr int WAVE_BYTES = P_OFF + kQ * PPITCH * 2;
-  static constexpr int PHI_OFF = WAVE_BYTES * kWaves;     // two shared phi tiles
+  static constexpr int R = RK + RV;
+  static constexpr int CPR = R / 8;                  // 16-byte chunks per (slot, head) record
+  static constexpr int KCH = RK / 8;                 // of which K latent
+  static constexpr int STAGE = kTile * CPR * 16;     // one wave's tile in LDS
+  static constexpr int LS = kTile * CPR / 64;        // LDS-direct loads per lane per tile
+  static constexpr int NS_FIT = (kLdsPerGroup - 2 * kPhiTileBytes) / (kWaves * STAGE);
+  static constexpr int NS = NS_FIT > 4 ? 4 : NS_FIT;  // ring depth (tiles per wave)
+  static constexpr int PHI_OFF = kWaves * NS * STAGE;
   static constexpr int LDS = PHI_OFF + 2 * kPhiTileBytes;
+  static constexpr int KS = (RK + 2 + 31) / 32;      // k-steps of K^T: latent, mu hi, mu lo
+  static constexpr int VB = RV / 16;                 // value column blocks
+  // chunk c of slot j sits at position (c + j / PER) % CPR of its record:
+  // 16 consecutive slots then start in 16 distinct 16-byte bank groups
+  static constexpr int PER = 16 / gcd16(CPR);
+  static_assert(R % 16 == 0 && RK % 16 == 0 && RV % 16 == 0, "rank granularity");
+  static_assert((kTile * CPR) % 64 == 0, "whole loads per tile");
+  static_assert(NS >= 2, "two tiles per wave must fit");
+  static_assert(LDS <= kLdsPerGroup, "LDS budget");
+  static_assert(LS + 2 <= 63, "vmcnt range");
 };
 
-// DPP row operations within groups of 16 lanes (see kvcache.hip).
-template <int CTRL>
-__device__ __forceinline__ float dpp(float v) {
-  return __builtin_bit_cast(
-      float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), CTRL, 0xF, 0xF, true));
-}
-__device__ __forceinline__ float row16_max(float v) {
-  v = fmaxf(v, dpp<0xB1>(v));
-  v = fmaxf(v, dpp<0x4E>(v));
-  v = fmaxf(v, dpp<0x141>(v));
-  return fmaxf(v, dpp<0x140>(v));
-}
-__device__ __forceinline__ float row16_sum(float v) {
-  v += dpp<0xB1>(v);
-  v += dpp<0x4E>(v);
-  v += dpp<0x141>(v);
-  return v + dpp<0x140>(v);
+// Every ds read of a wave happens before it passes the next barrier; the
+// signal fences keep the compiler from moving LDS accesses across it.  The
+// wait leaves at most n vector-memory operations (the latest tile loads)
+// outstanding.
+template <int N>
+__device__ __forceinline__ void tile_barrier() {
+  __builtin_amdgcn_s_waitcnt(waitcnt_vm(N));
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  __builtin_amdgcn_s_barrier();
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
 }
 
-__device__ __forceinline__ int kswz(int slot, int chunk) { return chunk ^ (slot & 15); }
-
-// Every LDS region here is private to one wave, so lanes of the same wave
-// exchange data through it without a workgroup barrier: wait for this
-// wave's LDS writes, and keep the compiler from moving LDS accesses across.
-__device__ __forceinline__ void wave_lds_sync() {
-  __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0); vmcnt, expcnt not waited
-  __builtin_amdgcn_wave_barrier();
+__device__ __forceinline__ float xor_max(float v) {
+  v = fmaxf(v, __shfl_xor(v, 16, 64));
+  return fmaxf(v, __shfl_xor(v, 32, 64));
+}
+__device__ __forceinline__ float xor_sum(float v) {
+  v += __shfl_xor(v, 16, 64);
+  return v + __shfl_xor(v, 32, 64);
 }
 
 template <int RK, int RV>
 __global__ __launch_bounds__(kThreads) void decode_mq_split(DecodeParams p) {
+#if defined(__HIP_DEVICE_COMPILE__)  // the body uses device-only builtins
   using C = Cfg<RK, RV>;
-  constexpr int R = RK + RV;
   extern __shared__ __attribute__((aligned(16))) char lds[];
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int l32 = lane & 31, h2 = lane >> 5, l16 = lane & 15, g4 = lane >> 4;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int l16 = lane & 15, g4 = lane >> 4;
   const int groups = (p.H + kWaves - 1) / kWaves;
   int bid = blockIdx.x;
   const int s = bid % p.S;
@@ -117,11 +127,6 @@ __global__ __launch_bounds__(kThreads) void decode_mq_split(DecodeParams p) {
   const int t0 = s * p.split_len;
   const int t1 = min(t0 + p.split_len, first);
 
-  char *wl = lds + wave * C::WAVE_BYTES;
-  uint16_t *Kt = reinterpret_cast<uint16_t *>(wl + C::K_OFF);   // [32][128], swizzled
-  uint16_t *Vt = reinterpret_cast<uint16_t *>(wl + C::V_OFF);   // [32][VPITCH]
-  uint16_t *Pt = reinterpret_cast<uint16_t *>(wl + C::P_OFF);   // [16][PPITCH]
-
   auto part_at = [&](int qi) {
     return p.ws + ((int64_t)((b * nq + qi) * p.H + h) * p.S + s) * (RV + 2);
   };
@@ -133,90 +138,44 @@ __global__ __launch_bounds__(kThreads) void decode_mq_split(DecodeParams p) {
       }
     return;
   }
+  const int ntiles = (t1 - t0 + kTile - 1) / kTile;
 
-  // ---- setup: rotated, scaled queries (A operand of S = Q K^T) ----
-  bf16x8_t qa[kD / 32];
-  {
-    const int qi = l16;
-    const bool qok = qi < nq;
-    const int qpos = min(first + qi, p.N - 1);
-    const float *qrow = p.q + ((int64_t)(b * nq + (qok ? qi : 0)) * p.H + h) * kD;
-    const float *cs = p.rope_f32 + (int64_t)qpos * kD;
-#pragma unroll
-    for (int ks = 0; ks < kD / 32; ++ks) {
-      float v[8];
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const int i = 32 * ks + 8 * g4 + e;
-        float r;
-        if (i < kHalf)
-          r = qrow[i] * cs[2 * i] - qrow[i + kHalf] * cs[2 * i + 1];
-        else
-          r = qrow[i] * cs[2 * (i - kHalf)] + qrow[i - kHalf] * cs[2 * (i - kHalf) + 1];
-        v[e] = qok ? r * p.scale_log2 : 0.f;
-      }
-      u32x4_t w;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) w[e] = pack_bf16x2(v[2 * e], v[2 * e + 1]);
-      qa[ks] = __builtin_bit_cast(bf16x8_t, w);
-    }
-  }
-  // ---- W_up,k,t rows with mu folded in (A operand of K^T) ----
-  bf16x8_t wa[4][C::KS + 1];
-  {
-    const uint16_t *W = reinterpret_cast<const uint16_t *>(p.wk) + (int64_t)h * kD * RK;
-#pragma unroll
-    for (int T = 0; T < 4; ++T) {
-      const int dim = 32 * T + l32;
-#pragma unroll
-      for (int ks = 0; ks < C::KS; ++ks)
-        wa[T][ks] = *reinterpret_cast<const bf16x8_t *>(W + (int64_t)dim * RK + 16 * ks + 8 * h2);
-      const float mu = p.muk[(int64_t)h * kD + dim];
-      const uint16_t hi = f32_to_bf16_bits(mu);
-      const uint16_t lo = f32_to_bf16_bits(mu - bf16_bits_to_f32(hi));
-      u32x4_t w = {h2 == 0 ? (uint32_t)hi | ((uint32_t)lo << 16) : 0u, 0u, 0u, 0u};
-      wa[T][C::KS] = __builtin_bit_cast(bf16x8_t, w);
-    }
-  }
-  const u32x4_t ones_w = {h2 == 0 ? 0x3F803F80u : 0u, 0u, 0u, 0u};
-  const bf16x8_t ones = __builtin_bit_cast(bf16x8_t, ones_w);
-
-  // ---- latent streaming ----
-  const int64_t srow = (int64_t)p.Hs * R;  // elements per slot
-  const uint16_t *lat = reinterpret_cast<const uint16_t *>(p.store) +
-                        ((int64_t)b * p.D + p.layer) * p.N * srow + (int64_t)h * R;
-  u32x4_t kb[C::KS], vch[C::VLOADS];
-  auto load_k = [&](int tb) {
-    const int js = min(tb + l32, t1 - 1);
-#pragma unroll
-    for (int ks = 0; ks < C::KS; ++ks)
-      kb[ks] = __builtin_nontemporal_load(
-          reinterpret_cast<const u32x4_t *>(lat + js * srow + 16 * ks + 8 * h2));
-  };
-  auto load_v = [&](int tb) {
-#pragma unroll
-    for (int u = 0; u < C::VLOADS; ++u) {
-      const int c = lane + 64 * u;
-      const int sl = min(c / C::VCH, kTile - 1), q = c % C::VCH;
-      const int j = min(tb + sl, t1 - 1);
-      if (c < kTile * C::VCH)
-        vch[u] = __builtin_nontemporal_load(
-            reinterpret_cast<const u32x4_t *>(lat + j * srow + RK + 8 * q));
-    }
-  };
-  auto load_tile = [&](int tb) {
-    load_k(tb);
-    load_v(tb);
-  };
-
-  // bf16 phi rows of tile tb (the RoPE table's MFMA tiles): the workgroup's
-  // four waves each copy a quarter into LDS buffer `buf`, HBM to LDS directly
+  // ---- streaming: this wave's ring of latent tiles, the shared phi tiles ----
+  const int64_t slab_bytes = (int64_t)p.N * p.Hs * C::R * 2;
+  const char *slab = reinterpret_cast<const char *>(p.store) + ((int64_t)b * p.D + p.layer) * slab_bytes;
+  const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<char *>(slab), (short)0, (int)slab_bytes, 0x00020000);
   const __amdgpu_buffer_rsrc_t rphi = __builtin_amdgcn_make_buffer_rsrc(
       const_cast<uint16_t *>(p.rope_bf16), (short)0,
       ((p.N + kTile - 1) / kTile) * kPhiTileBytes, 0x00020000);
-  auto issue_phi = [&](int tb, int buf) {
-    char *pb = lds + C::PHI_OFF + buf * kPhiTileBytes;
-    const uint32_t off = (uint32_t)(tb / kTile) * kPhiTileBytes;
+  const uint32_t srow = (uint32_t)p.Hs * C::R * 2;  // bytes per slot
+  char *ring = lds + wave * C::NS * C::STAGE;
+  int jn[C::LS];          // slot (in the tile) of the chunk this lane loads
+  uint32_t cb[C::LS];     // its byte offset inside the slot
+#pragma unroll
+  for (int n = 0; n < C::LS; ++n) {
+    const int P = n * 64 + lane;  // LDS chunk position in the stage
+    const int j = P / C::CPR, r = P % C::CPR;
+    const int c = (r + C::CPR - (j / C::PER) % C::CPR) % C::CPR;
+    jn[n] = j;
+    cb[n] = (uint32_t)h * (C::R * 2) + (uint32_t)c * 16;
+  }
+  auto issue_lat = [&](int it) {
+    char *sb = ring + (it % C::NS) * C::STAGE;
+    const int tb = t0 + it * kTile;
+#pragma unroll
+    for (int n = 0; n < C::LS; ++n) {
+      // slots past the split's last repeat its last slot: every byte loaded
+      // is a finite latent, and the softmax gives those slots weight zero
+      const int j = min(tb + jn[n], t1 - 1);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (LDS_AS void *)(sb + n * 64 * 16), 16,
+                                               (uint32_t)j * srow + cb[n], 0, 0,
+                                               kCachePolicyStream);
+    }
+  };
+  auto issue_phi = [&](int it) {
+    char *pb = lds + C::PHI_OFF + (it & 1) * kPhiTileBytes;
+    const uint32_t off = (uint32_t)((t0 + it * kTile) / kTile) * kPhiTileBytes;
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
       const int blk = 2 * wave + u;  // 1 KB blocks 0..7
@@ -224,150 +183,198 @@ __global__ __launch_bounds__(kThreads) void decode_mq_split(DecodeParams p) {
                                                off + (uint32_t)(blk * 64 + lane) * 16, 0, 0, 0);
     }
   };
-
-  float m[4], lsum[4];
-  f32x4_t acc[C::VB];
+  // The first tiles stream in while the operands below are set up.
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    m[i] = -INFINITY;
-    lsum[i] = 0.f;
+  for (int k = 0; k + 2 < C::NS; ++k)
+    if (k < ntiles) issue_lat(k);
+  issue_phi(0);
+  if (C::NS - 2 < ntiles) issue_lat(C::NS - 2);
+
+  // ---- B operand of S^T: rotated, scaled queries in the lanes' dim order ----
+  // k-step a, lane (query l16, group g4), element e: dim 16a + 4 g4 + e
+  // (e < 4) and dim 64 + 16a + 4 g4 + e - 4 (e >= 4).
+  bf16x8_t qb[4];
+  {
+    const int qi = l16;
+    const bool qok = qi < nq;
+    const int qpos = min(first + qi, p.N - 1);
+    const float *qrow = p.q + ((int64_t)(b * nq + (qok ? qi : 0)) * p.H + h) * kD;
+    const float *cs = p.rope_f32 + (int64_t)qpos * kD;
+#pragma unroll
+    for (int a = 0; a < 4; ++a) {
+      float lo[4], hi[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int i = 16 * a + 4 * g4 + e;  // < 64
+        const float c = cs[2 * i], sn = cs[2 * i + 1];
+        const float x0 = qrow[i], x1 = qrow[i + kHalf];
+        lo[e] = qok ? (x0 * c - x1 * sn) * p.scale_log2 : 0.f;
+        hi[e] = qok ? (x0 * sn + x1 * c) * p.scale_log2 : 0.f;
+      }
+      const u32x4_t w = {pack_bf16x2(lo[0], lo[1]), pack_bf16x2(lo[2], lo[3]),
+                         pack_bf16x2(hi[0], hi[1]), pack_bf16x2(hi[2], hi[3])};
+      qb[a] = __builtin_bit_cast(bf16x8_t, w);
+    }
   }
+  // ---- A operand of K^T: W_up,k,t rows (dims 16 a' + l16), mu folded in ----
+  // k-step ks, lane group g4: latent components 32 ks + 8 g4 + 0..7; the
+  // group at component RK carries (mu_hi, mu_lo), later groups zeros.
+  bf16x8_t wa[8][C::KS];
+  {
+    const uint16_t *W = reinterpret_cast<const uint16_t *>(p.wk) + (int64_t)h * kD * RK;
+#pragma unroll
+    for (int a = 0; a < 8; ++a) {
+      const int dim = 16 * a + l16;
+      const float mu = p.muk[(int64_t)h * kD + dim];
+      const uint16_t mhi = f32_to_bf16_bits(mu);
+      const uint16_t mlo = f32_to_bf16_bits(mu - bf16_bits_to_f32(mhi));
+#pragma unroll
+      for (int ks = 0; ks < C::KS; ++ks) {
+        // unconditional (clamped) load, then the mu / zero groups selected
+        const int k0 = 32 * ks + 8 * g4;
+        u32x4_t w = *reinterpret_cast<const u32x4_t *>(W + (int64_t)dim * RK + min(k0, RK - 8));
+        const uint32_t keep = k0 < RK ? ~0u : 0u;
+        w[0] = (w[0] & keep) | (k0 == RK ? ((uint32_t)mhi | ((uint32_t)mlo << 16)) : 0u);
+        w[1] &= keep;
+        w[2] &= keep;
+        w[3] &= keep;
+        wa[a][ks] = __builtin_bit_cast(bf16x8_t, w);
+      }
+    }
+  }
+
+  float m = -INFINITY, lsum = 0.f;  // query l16
+  f32x4_t acc[C::VB];
 #pragma unroll
   for (int v = 0; v < C::VB; ++v) acc[v] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
-  load_tile(t0);
-  issue_phi(t0, 0);
-  for (int tb = t0, it = 0; tb < t1; tb += kTile, ++it) {
-    const bool more = tb + kTile < t1;
-    // this tile's latents (registers) and phi rows (LDS) have landed, and
-    // every wave is done with the phi buffer the next copy overwrites
-    __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
-    __syncthreads();
-    const char *phb = lds + C::PHI_OFF + (it & 1) * kPhiTileBytes;
-    // V chunks of this tile into the staged tile, then the next tile's V
-    // chunks and phi rows on their way
+  for (int it = 0; it < ntiles; ++it) {
+    const int tb = t0 + it * kTile;
+    // tile it's latents (this wave) and phi rows (all waves) have landed,
+    // and every wave is done with tile it - 1's buffers
+    if (C::NS >= 3 && it + C::NS - 2 < ntiles)
+      tile_barrier<C::LS>();
+    else
+      tile_barrier<0>();
+    if (it + 1 < ntiles) issue_phi(it + 1);
+    if (it + C::NS - 1 < ntiles) issue_lat(it + C::NS - 1);
+
+    const char *st = ring + (it % C::NS) * C::STAGE;
+    const uint16_t *ph = reinterpret_cast<const uint16_t *>(lds + C::PHI_OFF + (it & 1) * kPhiTileBytes);
+
+    // ---- S^T = K Q^T, one 16-slot half at a time ----
+    f32x4_t sc[2];
 #pragma unroll
-    for (int u = 0; u < C::VLOADS; ++u) {
-      const int c = lane + 64 * u;
-      if (c < kTile * C::VCH) {
-        const int sl = c / C::VCH, q = c % C::VCH;
-        u32x2_t *dst = reinterpret_cast<u32x2_t *>(Vt + sl * C::VPITCH + 8 * q);
-        dst[0] = u32x2_t{vch[u][0], vch[u][1]};
-        dst[1] = u32x2_t{vch[u][2], vch[u][3]};
-      }
-    }
-    if (more) issue_phi(tb + kTile, (it + 1) & 1);
-    // K^T of the tile, two dim-tile pairs (T, T + 2) at a time
-    bf16x8_t kbf[C::KS];
-#pragma unroll
-    for (int ks = 0; ks < C::KS; ++ks) kbf[ks] = __builtin_bit_cast(bf16x8_t, kb[ks]);
-#pragma unroll
-    for (int T = 0; T < 2; ++T) {
-      // one pair of accumulator tiles live at a time
-      __builtin_amdgcn_sched_barrier(0);
-      f32x16_t a0 = {}, a1 = {};
+    for (int sh = 0; sh < 2; ++sh) {
+      const int js = 16 * sh + l16;  // slot in the tile
+      const char *rec = st + js * C::CPR * 16;
+      const int rot = js / C::PER;
+      bf16x8_t kb[C::KS];
 #pragma unroll
       for (int ks = 0; ks < C::KS; ++ks) {
-        a0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wa[T][ks], kbf[ks], a0, 0, 0, 0);
-        a1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wa[T + 2][ks], kbf[ks], a1, 0, 0, 0);
+        // every lane reads (groups past the K latent an in-record chunk whose
+        // value is then replaced), so no read is conditional
+        const int c = 4 * ks + g4;
+        const int cr = c < C::CPR ? c : C::CPR - 1;
+        u32x4_t v = *reinterpret_cast<const u32x4_t *>(rec + ((cr + rot) % C::CPR) * 16);
+        if (ks == C::KS - 1) {
+          const uint32_t keep = c < C::KCH ? ~0u : 0u;
+          v[0] = (v[0] & keep) | (c == C::KCH ? 0x3F803F80u : 0u);
+          v[1] &= keep;
+          v[2] &= keep;
+          v[3] &= keep;
+        }
+        kb[ks] = __builtin_bit_cast(bf16x8_t, v);
       }
-      a0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wa[T][C::KS], ones, a0, 0, 0, 0);
-      a1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wa[T + 2][C::KS], ones, a1, 0, 0, 0);
+      f32x4_t so = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int c = 0; c < 4; ++c) {
-        const int i0 = 32 * T + 8 * c + 4 * h2;  // first of four consecutive dims (< 64)
-        // phi tile element (step 2T + c/2, lane l32 + 32 (c%2), 4 h2 + e): cos at dim
-        // i0 + e, and 4 steps further sin
-        const uint16_t *ph = reinterpret_cast<const uint16_t *>(phb) +
-                             ((2 * T + c / 2) * 64 + l32 + 32 * (c % 2)) * 8 + 4 * h2;
-        const u32x2_t cw = *reinterpret_cast<const u32x2_t *>(ph);
-        const u32x2_t sw = *reinterpret_cast<const u32x2_t *>(ph + 4 * 64 * 8);
+      for (int a = 0; a < 4; ++a) {
+        f32x4_t x0 = {0.f, 0.f, 0.f, 0.f}, x1 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int ks = 0; ks < C::KS; ++ks) {
+          x0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wa[a][ks], kb[ks], x0, 0, 0, 0);
+          x1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wa[a + 4][ks], kb[ks], x1, 0, 0, 0);
+        }
+        // phi element (k-step a, lane js + 32 (g4 / 2), 4 (g4 % 2) + e): cos of
+        // frequency 16a + 4 g4 + e; four k-steps further its sin
+        const uint16_t *pc = ph + ((a * 64 + js + 32 * (g4 >> 1)) * 8 + 4 * (g4 & 1));
+        const u32x2_t cw = *reinterpret_cast<const u32x2_t *>(pc);
+        const u32x2_t sw = *reinterpret_cast<const u32x2_t *>(pc + 4 * 64 * 8);
         const float co[4] = {bf16_lo(cw[0]), bf16_hi(cw[0]), bf16_lo(cw[1]), bf16_hi(cw[1])};
         const float sn[4] = {bf16_lo(sw[0]), bf16_hi(sw[0]), bf16_lo(sw[1]), bf16_hi(sw[1])};
         float r0[4], r1[4];
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          const float x0 = a0[4 * c + e], x1 = a1[4 * c + e];
-          r0[e] = x0 * co[e] - x1 * sn[e];
-          r1[e] = x0 * sn[e] + x1 * co[e];
+          r0[e] = x0[e] * co[e] - x1[e] * sn[e];
+          r1[e] = x0[e] * sn[e] + x1[e] * co[e];
         }
-        const int ch0 = (i0 >> 3), ch1 = ((i0 + kHalf) >> 3);
-        *reinterpret_cast<u32x2_t *>(Kt + l32 * kD + kswz(l32, ch0) * 8 + 4 * h2) =
-            u32x2_t{pack_bf16x2(r0[0], r0[1]), pack_bf16x2(r0[2], r0[3])};
-        *reinterpret_cast<u32x2_t *>(Kt + l32 * kD + kswz(l32, ch1) * 8 + 4 * h2) =
-            u32x2_t{pack_bf16x2(r1[0], r1[1]), pack_bf16x2(r1[2], r1[3])};
+        const u32x4_t kw = {pack_bf16x2(r0[0], r0[1]), pack_bf16x2(r0[2], r0[3]),
+                            pack_bf16x2(r1[0], r1[1]), pack_bf16x2(r1[2], r1[3])};
+        so = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, kw), qb[a],
+                                                     so, 0, 0, 0);
       }
+      sc[sh] = so;
     }
-    if (more) {  // the latents' registers are free again: the next tile's
-      load_k(tb + kTile);
-      load_v(tb + kTile);
-    }
-    wave_lds_sync();
 
-    // S = Q K^T: queries 4 g4 + i, slots 16 nt + l16
-    f32x4_t sc[2];
+    // ---- online softmax of query l16 over slots 16 sh + 4 g4 + i ----
+    float sv[8];
+    float mx = -INFINITY;
 #pragma unroll
-    for (int nt = 0; nt < 2; ++nt) {
-      const int sl = 16 * nt + l16;
-      f32x4_t o = {0.f, 0.f, 0.f, 0.f};
+    for (int sh = 0; sh < 2; ++sh)
 #pragma unroll
-      for (int ks = 0; ks < kD / 32; ++ks) {
-        const bf16x8_t kf = *reinterpret_cast<const bf16x8_t *>(
-            Kt + sl * kD + kswz(sl, 4 * ks + g4) * 8);
-        o = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[ks], kf, o, 0, 0, 0);
+      for (int i = 0; i < 4; ++i) {
+        const bool ok = tb + 16 * sh + 4 * g4 + i < t1;
+        sv[4 * sh + i] = ok ? sc[sh][i] : -INFINITY;
+        mx = fmaxf(mx, sv[4 * sh + i]);
       }
-      sc[nt] = o;
+    mx = xor_max(mx);  // every tile holds a slot before t1: finite
+    float alpha = 1.f;
+    if (mx > m + kRescaleGap) {
+      alpha = exp2f(m - mx);
+      m = mx;
     }
-    // online softmax per query row; P to LDS
-    const bool ok0 = tb + l16 < t1, ok1 = tb + 16 + l16 < t1;
-    float alpha[4];
+    uint32_t pw[4];
+    float psum = 0.f;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const float s0 = ok0 ? sc[0][i] : -INFINITY, s1 = ok1 ? sc[1][i] : -INFINITY;
-      const float mx = row16_max(fmaxf(s0, s1));
-      alpha[i] = 1.f;
-      if (mx > m[i] + kRescaleGap) {  // row-uniform
-        alpha[i] = exp2f(m[i] - mx);
-        m[i] = mx;
-      }
-      const uint16_t p0 = f32_to_bf16_bits(ok0 ? exp2f(s0 - m[i]) : 0.f);
-      const uint16_t p1 = f32_to_bf16_bits(ok1 ? exp2f(s1 - m[i]) : 0.f);
-      lsum[i] = fmaf(lsum[i], alpha[i], bf16_bits_to_f32(p0) + bf16_bits_to_f32(p1));
-      const int q = 4 * g4 + i;
-      Pt[q * C::PPITCH + l16] = p0;
-      Pt[q * C::PPITCH + 16 + l16] = p1;
+    for (int e = 0; e < 4; ++e) {
+      pw[e] = pack_bf16x2(exp2f(sv[2 * e] - m), exp2f(sv[2 * e + 1] - m));
+      psum += bf16_lo(pw[e]) + bf16_hi(pw[e]);
     }
-    wave_lds_sync();
+    lsum = fmaf(lsum, alpha, psum);
+    const bf16x8_t pb = __builtin_bit_cast(bf16x8_t, u32x4_t{pw[0], pw[1], pw[2], pw[3]});
 
-    // acc += P C_v (queries x value columns, K = 32 slots)
-    const bf16x8_t pa = *reinterpret_cast<const bf16x8_t *>(Pt + l16 * C::PPITCH + 8 * g4);
+    // ---- acc^T += C_v^T P^T: value columns 16 v + l16, slots in lane order ----
 #pragma unroll
     for (int v = 0; v < C::VB; ++v) {
-      const uint16_t *vb = Vt + (8 * g4) * C::VPITCH + 16 * v + l16;
-      bf16x8_t bv;
+      const int col = 16 * v + l16;
+      const int c = C::KCH + col / 8;
+      bf16x8_t av;
 #pragma unroll
-      for (int e = 0; e < 8; ++e) bv[e] = (short)vb[e * C::VPITCH];
+      for (int e = 0; e < 8; ++e) {
+        const int js = (e < 4) ? 4 * g4 + e : 16 + 4 * g4 + (e - 4);
+        const uint16_t *src = reinterpret_cast<const uint16_t *>(
+            st + (js * C::CPR + (c + js / C::PER) % C::CPR) * 16) + (col & 7);
+        av[e] = (short)*src;
+      }
 #pragma unroll
-      for (int i = 0; i < 4; ++i) acc[v][i] *= alpha[i];
-      acc[v] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pa, bv, acc[v], 0, 0, 0);
+      for (int i = 0; i < 4; ++i) acc[v][i] *= alpha;
+      acc[v] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, pb, acc[v], 0, 0, 0);
     }
   }
 
-  // ---- partials (m, l, sum p c_v) of every query ----
-  if (!head_ok) return;
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int q = 4 * g4 + i;
-    const float l = row16_sum(lsum[i]);
-    if (q >= nq) continue;
-    float *part = part_at(q);
-    if (l16 == 0) {
-      part[0] = m[i];
-      part[1] = l;
-    }
-#pragma unroll
-    for (int v = 0; v < C::VB; ++v) part[2 + 16 * v + l16] = acc[v][i];
+  // ---- partials (m, l, sum p c_v) of query l16 ----
+  const float l = xor_sum(lsum);
+  if (!head_ok || l16 >= nq) return;
+  float *part = part_at(l16);
+  if (g4 == 0) {
+    part[0] = m;
+    part[1] = l;
   }
+#pragma unroll
+  for (int v = 0; v < C::VB; ++v)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) part[2 + 16 * v + 4 * g4 + i] = acc[v][i];
+#endif
 }
 
 template <int RK, int RV>
