@@ -43,9 +43,10 @@ def _run(cmd):
 
 
 # Kernels that count their own outstanding vector-memory operations
-# (s_waitcnt vmcnt(n) after buffer loads into LDS): a register spill would
-# add scratch loads/stores to that count, so they must compile without any.
-NO_SPILL = {"decode_mfma.hip", "decode2d_mfma.hip"}
+# (s_waitcnt vmcnt(n) after buffer loads into LDS): a register spill or any
+# other scratch access would add loads/stores to that count, so they must
+# compile without any.
+NO_SPILL = {"decode_mfma.hip", "decode2d_mfma.hip", "decode_mq.hip"}
 
 
 # Per-source code-generation options.  The multi-query decode feeds every
@@ -61,7 +62,7 @@ def _compile(src: str, obj: str):
     out = _run([HIPCC, *COMMON, "-x", "hip", *extra, "-c", src, "-o", obj])
     if extra:
         spills = [l for l in out.splitlines()
-                  if re.search(r"(VGPRs|SGPRs) Spill: [1-9]", l)]
+                  if re.search(r"(VGPRs|SGPRs) Spill: [1-9]|ScratchSize \[bytes/lane\]: [1-9]", l)]
         if spills:
             raise RuntimeError(f"{src}: register spills in a kernel that counts vmcnt itself:\n"
                                + "\n".join(spills))

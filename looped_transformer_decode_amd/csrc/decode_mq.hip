@@ -337,7 +337,10 @@ __global__ __launch_bounds__(kThreads) void decode_mq_split(DecodeParams p) {
     float psum = 0.f;
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-      pw[e] = pack_bf16x2(exp2f(sv[2 * e] - m), exp2f(sv[2 * e + 1] - m));
+      // the hardware exp2 (arguments <= 8 or -inf; results below the normal
+      // range flush to zero)
+      pw[e] = pack_bf16x2(__builtin_amdgcn_exp2f(sv[2 * e] - m),
+                          __builtin_amdgcn_exp2f(sv[2 * e + 1] - m));
       psum += bf16_lo(pw[e]) + bf16_hi(pw[e]);
     }
     lsum = fmaf(lsum, alpha, psum);

@@ -591,10 +591,11 @@ __global__ __launch_bounds__(256) void decode_merge_inflight(DecodeParams p, con
       // cores, v_mfma_f32_16x16x32_bf16 tiles of 16 queries x 16 output
       // elements over 32 value components (components past r_v are zero);
       // wave w takes the element tiles w, w + 4, ...  The latent averages
-      // are rounded to bf16 for the products (sums in fp32).  Lane l holds
-      // A = averages of query l % 16 at components 8 (l / 16) + 0..7, B = the
-      // W_up,v,t row of element l % 16 at the same components, and D =
-      // queries 4 (l / 16) + 0..3 of element l % 16.
+      // enter as a bf16 pair hi + lo (lo the rounding remainder), so the
+      // products see them to about 16 mantissa bits (sums in fp32).  Lane l
+      // holds A = averages of query l % 16 at components 8 (l / 16) + 0..7,
+      // B = the W_up,v,t row of element l % 16 at the same components, and
+      // D = queries 4 (l / 16) + 0..3 of element l % 16.
       constexpr int kMaxKs = 4;  // r_v <= 128
       const int l16 = t & 15, g = (t & 63) >> 4, wave = t >> 6;
       const int nqt = (nq + 15) / 16, nks = (rv + 31) / 32;
@@ -603,7 +604,7 @@ __global__ __launch_bounds__(256) void decode_merge_inflight(DecodeParams p, con
       for (int j = 0; j < 4; ++j)
         mus[j] = p.muv[(int64_t)h * d + min(16 * (wave + 4 * j) + l16, d - 1)];
       for (int qt = 0; qt < nqt; ++qt) {
-        bf16x8_t a[kMaxKs];
+        bf16x8_t a[kMaxKs], alo[kMaxKs];
 #pragma unroll
         for (int ks = 0; ks < kMaxKs; ++ks) {
           const int q = 16 * qt + l16, r0 = 32 * ks + 8 * g;
@@ -616,6 +617,9 @@ __global__ __launch_bounds__(256) void decode_merge_inflight(DecodeParams p, con
             const uint32_t pk = pack_bf16x2(f[2 * e], f[2 * e + 1]);
             a[ks][2 * e] = (short)(pk & 0xFFFFu);
             a[ks][2 * e + 1] = (short)(pk >> 16);
+            const uint32_t pr = pack_bf16x2(f[2 * e] - bf16_lo(pk), f[2 * e + 1] - bf16_hi(pk));
+            alo[ks][2 * e] = (short)(pr & 0xFFFFu);
+            alo[ks][2 * e + 1] = (short)(pr >> 16);
           }
         }
 #pragma unroll
@@ -637,6 +641,7 @@ __global__ __launch_bounds__(256) void decode_merge_inflight(DecodeParams p, con
               bw[2 * e + 1] = (short)(pk >> 16);
             }
             acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[ks], bw, acc, 0, 0, 0);
+            acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(alo[ks], bw, acc, 0, 0, 0);
           }
           // [fs (W_up,v,t A + mu_v,t L_s) + sum_m w_m v_m] / den, w_m = 0 for m > i
           const float mu = mus[j];
