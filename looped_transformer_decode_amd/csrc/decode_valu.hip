@@ -401,8 +401,11 @@ __global__ __launch_bounds__(256) void decode_merge_batched(DecodeParams p) {
 constexpr int kMaxQ = 32;       // in-flight queries per call
 constexpr int kQGroup = 8;      // queries per W_up,v,t pass
 
+// Four blocks per CU (at most 128 VGPRs, about 38 KB of LDS at 16 queries,
+// d = 128, r_v = 80): the long-recurrence call's 1024 blocks then run as one
+// round over the 256 CUs.
 template <typename E>
-__global__ __launch_bounds__(256) void decode_merge_inflight(DecodeParams p, const float *k_new,
+__global__ __launch_bounds__(256, 4) void decode_merge_inflight(DecodeParams p, const float *k_new,
                                                             const float *v_new) {
   const int h = blockIdx.x, b = blockIdx.y, t = threadIdx.x, nt = blockDim.x;
   const int d = p.d, half = d / 2, rv = p.rv, S = p.S, nq = p.qps, H = p.H;
@@ -410,10 +413,10 @@ __global__ __launch_bounds__(256) void decode_merge_inflight(DecodeParams p, con
   const int nqp = lay.nq_pad;
   extern __shared__ float sm[];
   float *kr = sm;                 // [nq][d]  rotated in-flight keys, then their values
-  float *qr = kr + nq * d;        // [nq][d]  rotated, scaled queries
-  float *sc = qr + nq * d;        // [nq][nq] in-flight scores (m <= i)
-  float *abar = sc + nq * nq;     // [rv][nqp] store latent numerators, query-minor
-  float *st = abar + rv * nqp;    // [nq][4]  store M, L; then fs, fs L, denominator
+  float *qr = kr + nq * d;        // [nq][d]  rotated, scaled queries, until the scores
+  float *abar = qr;               // [rv][nqp] store latent numerators (query-minor), after
+  float *sc = qr + lay.qa_floats; // [nq][nq] in-flight scores (m <= i)
+  float *st = sc + nq * nq;       // [nq][4]  store M, L; then fs, fs L, denominator
   float *wsp = st + 4 * nq;       // [nq][S]  split weights
   uint32_t *wl = reinterpret_cast<uint32_t *>(sm + lay.w_off);  // [d][lay.w_pitch] dwords
   const int first = min(max(p.pos[b], 0), p.N);
@@ -471,8 +474,8 @@ __global__ __launch_bounds__(256) void decode_merge_inflight(DecodeParams p, con
       }
     }
   }
-  // store partials of every query, merged over the splits: split weights
-  // 2^(m_s - M) of every query, then the numerators
+  // store partials of every query, merged over the splits: the split
+  // weights 2^(m_s - M) of every query (the numerators follow the scores)
   for (int i = t; i < nq; i += nt) {
     const float *part = p.ws + (int64_t)((b * nq + i) * H + h) * S * (rv + 2);
     float M = -INFINITY;
@@ -488,31 +491,6 @@ __global__ __launch_bounds__(256) void decode_merge_inflight(DecodeParams p, con
     }
     st[4 * i] = M;
     st[4 * i + 1] = L;
-  }
-  __syncthreads();
-  const int na = nqp * rv;  // padded queries get zero numerators
-  for (int e0 = t; e0 < na; e0 += kLoadBatch * nt) {
-    float a[kLoadBatch];
-#pragma unroll
-    for (int u = 0; u < kLoadBatch; ++u) a[u] = 0.f;
-    for (int s2 = 0; s2 < S; ++s2) {
-      float v[kLoadBatch];
-#pragma unroll
-      for (int u = 0; u < kLoadBatch; ++u) {
-        const int e = min(e0 + u * nt, na - 1), i = min(e / rv, nq - 1), r = e % rv;
-        v[u] = p.ws[(int64_t)((b * nq + i) * H + h) * S * (rv + 2) + s2 * (rv + 2) + 2 + r];
-      }
-#pragma unroll
-      for (int u = 0; u < kLoadBatch; ++u) {
-        const int i = min(min(e0 + u * nt, na - 1) / rv, nq - 1);
-        a[u] = fmaf(v[u], wsp[i * S + s2], a[u]);
-      }
-    }
-#pragma unroll
-    for (int u = 0; u < kLoadBatch; ++u) {
-      const int e = e0 + u * nt, i = e / rv, r = e % rv;
-      if (e < na) abar[r * nqp + i] = i < nq ? a[u] : 0.f;
-    }
   }
   __syncthreads();
   // scores s[i][m], m <= i: one thread per pair, four partial sums over
@@ -548,6 +526,32 @@ __global__ __launch_bounds__(256) void decode_merge_inflight(DecodeParams p, con
     sc[i * nq + m] = v;
   }
   __syncthreads();
+  // the queries are done with: the store numerators of every query, merged
+  // over the splits, take their place
+  const int na = nqp * rv;  // padded queries get zero numerators
+  for (int e0 = t; e0 < na; e0 += kLoadBatch * nt) {
+    float a[kLoadBatch];
+#pragma unroll
+    for (int u = 0; u < kLoadBatch; ++u) a[u] = 0.f;
+    for (int s2 = 0; s2 < S; ++s2) {
+      float v[kLoadBatch];
+#pragma unroll
+      for (int u = 0; u < kLoadBatch; ++u) {
+        const int e = min(e0 + u * nt, na - 1), i = min(e / rv, nq - 1), r = e % rv;
+        v[u] = p.ws[(int64_t)((b * nq + i) * H + h) * S * (rv + 2) + s2 * (rv + 2) + 2 + r];
+      }
+#pragma unroll
+      for (int u = 0; u < kLoadBatch; ++u) {
+        const int i = min(min(e0 + u * nt, na - 1) / rv, nq - 1);
+        a[u] = fmaf(v[u], wsp[i * S + s2], a[u]);
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < kLoadBatch; ++u) {
+      const int e = e0 + u * nt, i = e / rv, r = e % rv;
+      if (e < na) abar[r * nqp + i] = i < nq ? a[u] : 0.f;
+    }
+  }
   // per query, once: the maximum M over the store part and its in-flight
   // scores, the store factor fs = 2^(M_s - M), the in-flight weights
   // 2^(s_m - M) in place of the scores (0 for m > i) and the denominator

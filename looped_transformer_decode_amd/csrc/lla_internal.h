@@ -72,14 +72,16 @@ __device__ __forceinline__ QuerySlot query_slot(const DecodeParams &p, int32_t v
   return {b, q, q};
 }
 
-// LDS of the in-flight merge (floats unless noted): rotated keys and queries
-// [2][nq][d], in-flight scores [nq][nq], store numerators [rv][nq_pad] (query
-// count padded to whole groups of 8), per-query store M, L and softmax
-// factors [nq][4], split weights [nq][S];
+// LDS of the in-flight merge (floats unless noted): rotated keys [nq][d];
+// rotated queries [nq][d], which the store numerators [rv][nq_pad] (query
+// count padded to whole groups of 8) replace once the scores are formed;
+// in-flight scores [nq][nq], per-query store M, L and softmax factors
+// [nq][4], split weights [nq][S];
 // then, 16-byte aligned, W_up,v,t of the head as [d] rows of w_pitch dwords
 // (an odd count, so that consecutive rows start in different banks).
 // base: bytes without the W rows; with_w: bytes with them.
 struct InflightMergeLds {
+  int32_t qa_floats;  // floats of the query / numerator region
   int32_t nq_pad;
   int32_t w_off;    // floats before the W rows
   int32_t w_pitch;  // dwords per W row
@@ -90,8 +92,9 @@ __host__ __device__ inline InflightMergeLds inflight_merge_lds(int32_t nq, int32
                                                                int32_t S, int32_t esize) {
   InflightMergeLds l;
   l.nq_pad = (nq + 7) / 8 * 8;
-  const size_t f = (size_t)2 * nq * d + (size_t)nq * nq + (size_t)l.nq_pad * rv +
-                   4 * (size_t)nq + (size_t)nq * S;
+  const size_t qa = (size_t)nq * d > (size_t)l.nq_pad * rv ? (size_t)nq * d : (size_t)l.nq_pad * rv;
+  const size_t f = (size_t)nq * d + qa + (size_t)nq * nq + 4 * (size_t)nq + (size_t)nq * S;
+  l.qa_floats = (int32_t)qa;
   l.base = 4 * f;
   l.w_off = (int32_t)((f + 3) / 4 * 4);
   l.w_pitch = ((rv * esize + 3) / 4) | 1;
