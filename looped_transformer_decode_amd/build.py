@@ -51,8 +51,12 @@ NO_SPILL = {"decode_mfma.hip", "decode2d_mfma.hip", "decode_mq.hip"}
 
 # Per-source code-generation options.  The multi-query decode feeds every
 # MFMA result straight into vector arithmetic: with the VGPR form of the
-# MFMA instructions its results need no accumulator-register copies.
-SOURCE_FLAGS = {"decode_mq.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
+# MFMA instructions its results need no accumulator-register copies.  The
+# same holds for the per-head decode at the larger ranks, whose waves use
+# more than 256 registers (measured: B = 32 call 78.0 -> 76.2 us, long
+# recurrence 342.5 -> 336.8 us).
+SOURCE_FLAGS = {"decode_mq.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
+                "decode_mfma.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
 
 
 def _compile(src: str, obj: str):
