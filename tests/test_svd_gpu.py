@@ -122,10 +122,12 @@ def test_lla2d_stack(device):
                 tol_sig=5e-3, tol_vec=1e-2)
 
 
-@pytest.mark.parametrize("n,K,r", [(10, 32, 12), (200, 16, 16), (64, 24, 1)],
-                         ids=["rank_deficient", "full_rank", "rank_one"])
+@pytest.mark.parametrize("n,K,r", [(10, 32, 12), (200, 16, 16), (64, 24, 1), (80, 12, 5)],
+                         ids=["rank_deficient", "full_rank", "rank_one", "k_not_multiple_of_8"])
 def test_edge_cases(device, n, K, r):
-    """Fewer rows than the rank (centred rank n - 1 < r), r = K, r = 1."""
+    """Fewer rows than the rank (centred rank n - 1 < r), r = K, r = 1, and a
+    stack length that is not a multiple of 8 (the Gram matrix then comes from
+    the generic tiled product with the centring in its loader)."""
     T, width = 2, K // 2
     rng = np.random.default_rng(n + K)
     x = gen.as_storage(rng.standard_normal((n, 1, K)) * 2 + 1, "f32")[1]
