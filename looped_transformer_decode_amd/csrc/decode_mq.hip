@@ -25,9 +25,10 @@
 //    of each half.
 //  * acc^T += C_v^T P^T (value columns x queries, K = the 32 slots): those
 //    eight softmax weights per lane are the B operand as they stand (slots
-//    again in lane order), C_v^T is gathered from the staged tile in the
-//    same order, and the output lane keeps query l%16, so the softmax state
-//    and the rescaling of its accumulator stay in the lane.
+//    again in lane order), C_v^T comes from the staged tile in the same
+//    order by two transposing LDS reads (ds_read_b64_tr_b16) per column
+//    block, and the output lane keeps query l%16, so the softmax state and
+//    the rescaling of its accumulator stay in the lane.
 // Latent tiles stream HBM -> LDS directly (buffer loads into LDS, no
 // register staging) into a ring of two to four tiles per wave; a tile's
 // 16-byte chunks are rotated within each slot record so that the 16 slots a
@@ -44,6 +45,7 @@ typedef __attribute__((__vector_size__(8 * sizeof(short)))) short bf16x8_t;
 typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4_t;
 typedef __attribute__((__vector_size__(4 * sizeof(uint32_t)))) uint32_t u32x4_t;
 typedef __attribute__((__vector_size__(2 * sizeof(uint32_t)))) uint32_t u32x2_t;
+typedef short short4_t __attribute__((ext_vector_type(4)));
 
 constexpr int kD = 128;
 constexpr int kHalf = kD / 2;
@@ -243,6 +245,22 @@ __global__ __launch_bounds__(kThreads) void decode_mq_split(DecodeParams p) {
     }
   }
 
+  // Byte offsets in a tile of this lane's 8-byte pieces for the transposing
+  // reads of C_v: for value block v and slot half hh, lane l16 of group g4
+  // reads slot 16 hh + 4 g4 + l16 / 4, columns 16 v + 4 (l16 % 4) + 0..3.
+  // ds_read_b64_tr_b16 gives lane i of a 16-lane group element i % 4 of
+  // the pieces of lanes i / 4 + 4 e (e = 0..3): column 16 v + i of the
+  // group's four slots.
+  uint32_t vofs[C::VB][2];
+#pragma unroll
+  for (int v = 0; v < C::VB; ++v)
+#pragma unroll
+    for (int hh = 0; hh < 2; ++hh) {
+      const int sl = 16 * hh + 4 * g4 + (l16 >> 2);
+      const int c = C::KCH + 2 * v + ((l16 & 3) >> 1);
+      vofs[v][hh] = (uint32_t)((sl * C::CPR + (c + sl / C::PER) % C::CPR) * 16 + 8 * (l16 & 1));
+    }
+
   float m = -INFINITY, lsum = 0.f;  // query l16
   f32x4_t acc[C::VB];
 #pragma unroll
@@ -349,16 +367,14 @@ __global__ __launch_bounds__(kThreads) void decode_mq_split(DecodeParams p) {
     // ---- acc^T += C_v^T P^T: value columns 16 v + l16, slots in lane order ----
 #pragma unroll
     for (int v = 0; v < C::VB; ++v) {
-      const int col = 16 * v + l16;
-      const int c = C::KCH + col / 8;
-      bf16x8_t av;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const int js = (e < 4) ? 4 * g4 + e : 16 + 4 * g4 + (e - 4);
-        const uint16_t *src = reinterpret_cast<const uint16_t *>(
-            st + (js * C::CPR + (c + js / C::PER) % C::CPR) * 16) + (col & 7);
-        av[e] = (short)*src;
-      }
+      // two transposing LDS reads: lane l16 receives column 16 v + l16 of
+      // the four slots 4 g4 + 0..3 (then 16 + 4 g4 + 0..3), read by the lanes
+      // of its 16-lane group as 8-byte pieces (vofs)
+      const short4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+          (LDS_AS short4_t *)(st + vofs[v][0]));
+      const short4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+          (LDS_AS short4_t *)(st + vofs[v][1]));
+      const bf16x8_t av = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
 #pragma unroll
       for (int i = 0; i < 4; ++i) acc[v][i] *= alpha;
       acc[v] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, pb, acc[v], 0, 0, 0);
