@@ -61,7 +61,10 @@ constexpr int kLdsPerGroup = 80 * 1024;        // two workgroups per CU
 constexpr int kCachePolicyStream = 2;
 #define LDS_AS __attribute__((address_space(3)))
 
-constexpr int gcd16(int a) { return (a % 16 == 0) ? 16 : (a % 8 == 0) ? 8 : (a % 4 == 0) ? 4 : (a % 2 == 0) ? 2 : 1; }
+// The largest power of two dividing both a and 16.
+constexpr int gcd16(int a) {
+  return (a % 16 == 0) ? 16 : (a % 8 == 0) ? 8 : (a % 4 == 0) ? 4 : (a % 2 == 0) ? 2 : 1;
+}
 
 template <int RK, int RV>
 struct Cfg {
