@@ -31,7 +31,7 @@ COMMON = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",
           "-I", INCLUDE, "-I", CSRC]
 SOURCES = ["lla_api.cpp", "decode_valu.hip", "decode_mfma.hip", "encode_valu.hip",
            "encode_mfma.hip", "decode2d_mfma.hip", "kvcache.hip",
-           "svd_init.hip", "decode_mq.hip", "decode_noalloc.hip"]
+           "svd_init.hip", "decode_mq.hip", "decode_noalloc.hip", "encode_stream.hip"]
 
 
 def _run(cmd):
@@ -46,7 +46,7 @@ def _run(cmd):
 # (s_waitcnt vmcnt(n) after buffer loads into LDS): a register spill or any
 # other scratch access would add loads/stores to that count, so they must
 # compile without any.
-NO_SPILL = {"decode_mfma.hip", "decode2d_mfma.hip", "decode_mq.hip"}
+NO_SPILL = {"decode_mfma.hip", "decode2d_mfma.hip", "decode_mq.hip", "encode_stream.hip"}
 
 
 # Per-source code-generation options.  The multi-query decode feeds every
@@ -56,7 +56,8 @@ NO_SPILL = {"decode_mfma.hip", "decode2d_mfma.hip", "decode_mq.hip"}
 # more than 256 registers (measured: B = 32 call 78.0 -> 76.2 us, long
 # recurrence 342.5 -> 336.8 us).
 SOURCE_FLAGS = {"decode_mq.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
-                "decode_mfma.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
+                "decode_mfma.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
+                "encode_stream.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
 
 
 def _compile(src: str, obj: str):

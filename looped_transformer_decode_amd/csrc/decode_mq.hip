@@ -45,7 +45,6 @@ typedef __attribute__((__vector_size__(8 * sizeof(short)))) short bf16x8_t;
 typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4_t;
 typedef __attribute__((__vector_size__(4 * sizeof(uint32_t)))) uint32_t u32x4_t;
 typedef __attribute__((__vector_size__(2 * sizeof(uint32_t)))) uint32_t u32x2_t;
-typedef short short4_t __attribute__((ext_vector_type(4)));
 
 constexpr int kD = 128;
 constexpr int kHalf = kD / 2;
@@ -281,6 +280,7 @@ __global__ __launch_bounds__(kThreads) void decode_mq_split(DecodeParams p) {
     if (it + C::NS - 1 < ntiles) issue_lat(it + C::NS - 1);
 
     const char *st = ring + (it % C::NS) * C::STAGE;
+    const uint32_t st_lds = (uint32_t)(uintptr_t)(LDS_AS const char *)st;
     const uint16_t *ph = reinterpret_cast<const uint16_t *>(lds + C::PHI_OFF + (it & 1) * kPhiTileBytes);
 
     // ---- S^T = K Q^T, one 16-slot half at a time ----
@@ -368,15 +368,20 @@ __global__ __launch_bounds__(kThreads) void decode_mq_split(DecodeParams p) {
     const bf16x8_t pb = __builtin_bit_cast(bf16x8_t, u32x4_t{pw[0], pw[1], pw[2], pw[3]});
 
     // ---- acc^T += C_v^T P^T: value columns 16 v + l16, slots in lane order ----
+    // two transposing LDS reads per value block: lane l16 receives column
+    // 16 v + l16 of the four slots 4 g4 + 0..3 (then 16 + 4 g4 + 0..3), read
+    // by the lanes of its 16-lane group as 8-byte pieces (vofs)
+    uint32_t ta[2 * C::VB];
 #pragma unroll
     for (int v = 0; v < C::VB; ++v) {
-      // two transposing LDS reads: lane l16 receives column 16 v + l16 of
-      // the four slots 4 g4 + 0..3 (then 16 + 4 g4 + 0..3), read by the lanes
-      // of its 16-lane group as 8-byte pieces (vofs)
-      const short4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-          (LDS_AS short4_t *)(st + vofs[v][0]));
-      const short4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-          (LDS_AS short4_t *)(st + vofs[v][1]));
+      ta[2 * v] = st_lds + vofs[v][0];
+      ta[2 * v + 1] = st_lds + vofs[v][1];
+    }
+    tr_short4_t tv[2 * C::VB];
+    lds_read_tr16_b64<2 * C::VB>(ta, tv);
+#pragma unroll
+    for (int v = 0; v < C::VB; ++v) {
+      const tr_short4_t lo = tv[2 * v], hi = tv[2 * v + 1];
       const bf16x8_t av = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
 #pragma unroll
       for (int i = 0; i < 4; ++i) acc[v][i] *= alpha;

@@ -436,6 +436,8 @@ hipError_t launch_encode_mfma(const EncodeParams &p, hipStream_t st) {
   // Few row blocks (small batch, LLA-2D): one 16-row, 16-column tile per
   // workgroup, the contraction split over its waves.
   if (blocks1 * 2 < 128) return launch_splitk(p, st);
+  // Many rows: the streamed form (x and W_down through an LDS ring).
+  if (encode_stream_supported(p)) return launch_encode_stream(p, st);
   // Two row tiles per wave when that still gives a full wave of workgroups
   // (only the smallest ranks: larger ones would spill at two waves per SIMD).
   const bool two = (int64_t)((M + 127) / 128) * p.Hs * 2 >= 256;

@@ -74,4 +74,70 @@ constexpr int waitcnt_vm(int n) {
   return (n & 15) | (7 << 4) | (15 << 8) | ((n >> 4) << 14);
 }
 
+
+// Transposing LDS reads (ds_read_b64_tr_b16) issued together, with the wait
+// for them in the same asm block.  Within each 16-lane group, lane i receives
+// element i % 4 of the 8-byte pieces addressed by lanes i / 4 + 4 e (e =
+// 0..3).  The builtin form of this read makes the compiler wait for every
+// outstanding LDS-direct load (buffer_load ... lds) before it, because it
+// cannot tell which LDS bytes those loads write; in a kernel that keeps a
+// ring of such loads in flight, that wait would drain the ring at every
+// read.  The caller's own vmcnt waits and barriers guarantee that the bytes
+// read here have landed.  out[i] = the read at LDS byte address a[i].
+typedef short tr_short4_t __attribute__((ext_vector_type(4)));
+template <int K>
+__device__ __forceinline__ void lds_read_tr16_b64(const uint32_t (&a)[K], tr_short4_t (&out)[K]) {
+  static_assert(K >= 1 && K <= 10, "1 to 10 reads per block");
+  if constexpr (K == 1)
+    asm volatile("ds_read_b64_tr_b16 %0, %1\ns_waitcnt lgkmcnt(0)"
+                 : "=&v"(out[0])
+                 : "v"(a[0])
+                 : "memory");
+  else if constexpr (K == 2)
+    asm volatile("ds_read_b64_tr_b16 %0, %2\nds_read_b64_tr_b16 %1, %3\ns_waitcnt lgkmcnt(0)"
+                 : "=&v"(out[0]), "=&v"(out[1])
+                 : "v"(a[0]), "v"(a[1])
+                 : "memory");
+  else if constexpr (K == 3)
+    asm volatile("ds_read_b64_tr_b16 %0, %3\nds_read_b64_tr_b16 %1, %4\nds_read_b64_tr_b16 %2, %5\ns_waitcnt lgkmcnt(0)"
+                 : "=&v"(out[0]), "=&v"(out[1]), "=&v"(out[2])
+                 : "v"(a[0]), "v"(a[1]), "v"(a[2])
+                 : "memory");
+  else if constexpr (K == 4)
+    asm volatile("ds_read_b64_tr_b16 %0, %4\nds_read_b64_tr_b16 %1, %5\nds_read_b64_tr_b16 %2, %6\nds_read_b64_tr_b16 %3, %7\ns_waitcnt lgkmcnt(0)"
+                 : "=&v"(out[0]), "=&v"(out[1]), "=&v"(out[2]), "=&v"(out[3])
+                 : "v"(a[0]), "v"(a[1]), "v"(a[2]), "v"(a[3])
+                 : "memory");
+  else if constexpr (K == 5)
+    asm volatile("ds_read_b64_tr_b16 %0, %5\nds_read_b64_tr_b16 %1, %6\nds_read_b64_tr_b16 %2, %7\nds_read_b64_tr_b16 %3, %8\nds_read_b64_tr_b16 %4, %9\ns_waitcnt lgkmcnt(0)"
+                 : "=&v"(out[0]), "=&v"(out[1]), "=&v"(out[2]), "=&v"(out[3]), "=&v"(out[4])
+                 : "v"(a[0]), "v"(a[1]), "v"(a[2]), "v"(a[3]), "v"(a[4])
+                 : "memory");
+  else if constexpr (K == 6)
+    asm volatile("ds_read_b64_tr_b16 %0, %6\nds_read_b64_tr_b16 %1, %7\nds_read_b64_tr_b16 %2, %8\nds_read_b64_tr_b16 %3, %9\nds_read_b64_tr_b16 %4, %10\nds_read_b64_tr_b16 %5, %11\ns_waitcnt lgkmcnt(0)"
+                 : "=&v"(out[0]), "=&v"(out[1]), "=&v"(out[2]), "=&v"(out[3]), "=&v"(out[4]), "=&v"(out[5])
+                 : "v"(a[0]), "v"(a[1]), "v"(a[2]), "v"(a[3]), "v"(a[4]), "v"(a[5])
+                 : "memory");
+  else if constexpr (K == 7)
+    asm volatile("ds_read_b64_tr_b16 %0, %7\nds_read_b64_tr_b16 %1, %8\nds_read_b64_tr_b16 %2, %9\nds_read_b64_tr_b16 %3, %10\nds_read_b64_tr_b16 %4, %11\nds_read_b64_tr_b16 %5, %12\nds_read_b64_tr_b16 %6, %13\ns_waitcnt lgkmcnt(0)"
+                 : "=&v"(out[0]), "=&v"(out[1]), "=&v"(out[2]), "=&v"(out[3]), "=&v"(out[4]), "=&v"(out[5]), "=&v"(out[6])
+                 : "v"(a[0]), "v"(a[1]), "v"(a[2]), "v"(a[3]), "v"(a[4]), "v"(a[5]), "v"(a[6])
+                 : "memory");
+  else if constexpr (K == 8)
+    asm volatile("ds_read_b64_tr_b16 %0, %8\nds_read_b64_tr_b16 %1, %9\nds_read_b64_tr_b16 %2, %10\nds_read_b64_tr_b16 %3, %11\nds_read_b64_tr_b16 %4, %12\nds_read_b64_tr_b16 %5, %13\nds_read_b64_tr_b16 %6, %14\nds_read_b64_tr_b16 %7, %15\ns_waitcnt lgkmcnt(0)"
+                 : "=&v"(out[0]), "=&v"(out[1]), "=&v"(out[2]), "=&v"(out[3]), "=&v"(out[4]), "=&v"(out[5]), "=&v"(out[6]), "=&v"(out[7])
+                 : "v"(a[0]), "v"(a[1]), "v"(a[2]), "v"(a[3]), "v"(a[4]), "v"(a[5]), "v"(a[6]), "v"(a[7])
+                 : "memory");
+  else if constexpr (K == 9)
+    asm volatile("ds_read_b64_tr_b16 %0, %9\nds_read_b64_tr_b16 %1, %10\nds_read_b64_tr_b16 %2, %11\nds_read_b64_tr_b16 %3, %12\nds_read_b64_tr_b16 %4, %13\nds_read_b64_tr_b16 %5, %14\nds_read_b64_tr_b16 %6, %15\nds_read_b64_tr_b16 %7, %16\nds_read_b64_tr_b16 %8, %17\ns_waitcnt lgkmcnt(0)"
+                 : "=&v"(out[0]), "=&v"(out[1]), "=&v"(out[2]), "=&v"(out[3]), "=&v"(out[4]), "=&v"(out[5]), "=&v"(out[6]), "=&v"(out[7]), "=&v"(out[8])
+                 : "v"(a[0]), "v"(a[1]), "v"(a[2]), "v"(a[3]), "v"(a[4]), "v"(a[5]), "v"(a[6]), "v"(a[7]), "v"(a[8])
+                 : "memory");
+  else if constexpr (K == 10)
+    asm volatile("ds_read_b64_tr_b16 %0, %10\nds_read_b64_tr_b16 %1, %11\nds_read_b64_tr_b16 %2, %12\nds_read_b64_tr_b16 %3, %13\nds_read_b64_tr_b16 %4, %14\nds_read_b64_tr_b16 %5, %15\nds_read_b64_tr_b16 %6, %16\nds_read_b64_tr_b16 %7, %17\nds_read_b64_tr_b16 %8, %18\nds_read_b64_tr_b16 %9, %19\ns_waitcnt lgkmcnt(0)"
+                 : "=&v"(out[0]), "=&v"(out[1]), "=&v"(out[2]), "=&v"(out[3]), "=&v"(out[4]), "=&v"(out[5]), "=&v"(out[6]), "=&v"(out[7]), "=&v"(out[8]), "=&v"(out[9])
+                 : "v"(a[0]), "v"(a[1]), "v"(a[2]), "v"(a[3]), "v"(a[4]), "v"(a[5]), "v"(a[6]), "v"(a[7]), "v"(a[8]), "v"(a[9])
+                 : "memory");
+}
+
 }  // namespace lla

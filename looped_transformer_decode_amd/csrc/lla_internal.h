@@ -209,6 +209,8 @@ hipError_t launch_decode_mq(const DecodeParams &p, hipStream_t s);
 hipError_t launch_encode_valu(const EncodeParams &p, int dtype, hipStream_t s);
 bool encode_mfma_supported(const EncodeParams &p, int dtype);
 hipError_t launch_encode_mfma(const EncodeParams &p, hipStream_t s);
+bool encode_stream_supported(const EncodeParams &p);
+hipError_t launch_encode_stream(const EncodeParams &p, hipStream_t s);
 bool kv_decode_supported(int32_t d, int dtype);
 int32_t kv_heads_per_group(int32_t d, int dtype);
 hipError_t launch_kv_decode(const KvParams &p, int dtype, hipStream_t s);

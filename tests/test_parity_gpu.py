@@ -381,6 +381,10 @@ ENCODE_SHAPES = [
     # enough rows for two 16-row tiles per wave and several row blocks
     ("extreme_batch_b768_ctx4k", dict(B=260, D=2, N=16)),
     ("bf16_b32_ctx4k", dict(B=70, D=2, N=16, H=4, T=1)),
+    # enough row blocks for the LDS-ring form: K = 2048 (32 chunks), and
+    # K = 128 (two chunks, fewer than the ring holds); ragged last blocks
+    ("long_recurrence_t16_ctx8k", dict(B=104, D=2, N=24)),
+    ("bf16_b32_ctx4k", dict(B=78, D=2, N=16, T=1)),
 ]
 
 
