@@ -222,20 +222,22 @@ __global__ __launch_bounds__(256) void decode_merge(DecodeParams p) {
 // read in batches of kLoadBatch independent loads.
 constexpr int kBT = 8;
 static_assert(kBT == 8, "batched_merge_lds() sizes the LDS for tiles of 8 sequences");
+constexpr int kOnePer = 8;  // partial elements per thread on the one-split path
 
 // Copies the d x rv block of W_up,v,t at wg (16-byte aligned, rows of a
 // whole number of 16-byte chunks) into LDS rows of `pitch` dwords.
-template <typename E>
+// NB: 16-byte loads a thread issues before it waits.
+template <typename E, int NB = kLoadBatch>
 __device__ __forceinline__ void w_rows_to_lds(const E *wg, int d, int rv, int pitch, uint32_t *wl,
                                               int t, int nt) {
   const u32x4_t *src = reinterpret_cast<const u32x4_t *>(wg);
   const int rc = rv * (int)sizeof(E) / 16, n = d * rc;  // 16-byte chunks per row, in all
-  for (int c0 = t; c0 < n; c0 += kLoadBatch * nt) {
-    u32x4_t v[kLoadBatch];
+  for (int c0 = t; c0 < n; c0 += NB * nt) {
+    u32x4_t v[NB];
 #pragma unroll
-    for (int u = 0; u < kLoadBatch; ++u) v[u] = src[min(c0 + u * nt, n - 1)];
+    for (int u = 0; u < NB; ++u) v[u] = src[min(c0 + u * nt, n - 1)];
 #pragma unroll
-    for (int u = 0; u < kLoadBatch; ++u) {
+    for (int u = 0; u < NB; ++u) {
       const int c = c0 + u * nt;
       if (c < n) {
         uint32_t *dst = wl + (c / rc) * pitch + 4 * (c % rc);
@@ -266,54 +268,80 @@ __global__ __launch_bounds__(256) void decode_merge_batched(DecodeParams p) {
   const E *wg = reinterpret_cast<const E *>(p.wv) + (int64_t)h * d * rv;
   const bool w_vec = p.w_lds != 0 && (rv * (int)sizeof(E)) % 16 == 0 &&
                      (reinterpret_cast<uintptr_t>(wg) & 15) == 0;
-  if (w_vec) w_rows_to_lds(wg, d, rv, lay.w_pitch, wl, tid, nt);
+  if (S == 1 && w_vec && kBT * rv <= kOnePer * nt) {
+    // One split (the usual LLA-2D case): the partials this thread needs are
+    // loaded together with the W_up,v,t rows, so the block waits for memory
+    // once instead of once per phase.  The arithmetic is the general
+    // phases' with S = 1 (weight 2^(m - m) = 1, or 0 for an empty split).
+    const int na = kBT * rv;
+    float mv[kOnePer], lv[kOnePer], av[kOnePer];
+#pragma unroll
+    for (int u = 0; u < kOnePer; ++u) {
+      const int e = min(tid + u * nt, na - 1), b = min(b0 + e / rv, p.B - 1);
+      const float *part = p.ws + (int64_t)(b * p.H + h) * (rv + 2);
+      mv[u] = part[0];
+      lv[u] = part[1];
+      av[u] = part[2 + e % rv];
+    }
+    w_rows_to_lds<E, 2 * kLoadBatch>(wg, d, rv, lay.w_pitch, wl, tid, nt);
+#pragma unroll
+    for (int u = 0; u < kOnePer; ++u) {
+      const int e = tid + u * nt;
+      if (e >= na) continue;
+      const float f = mv[u] == -INFINITY ? 0.f : exp2f(mv[u] - mv[u]);
+      const float a = fmaf(av[u], f, 0.f), L = fmaf(lv[u], f, 0.f);
+      abar[e] = b0 + e / rv < p.B ? a / L : 0.f;
+    }
+  } else {
+    if (w_vec) w_rows_to_lds(wg, d, rv, lay.w_pitch, wl, tid, nt);
 
-  // split weights 2^(m_s - M) and merged sum L of every sequence of the tile
-  for (int bl = tid; bl < kBT; bl += nt) {
-    const int b = b0 + bl;
-    if (b >= p.B) {
-      for (int s2 = 0; s2 < S; ++s2) fs[bl * S + s2] = 0.f;
-      ls[bl] = 1.f;
-      continue;
-    }
-    const float *part = p.ws + (int64_t)(b * p.H + h) * S * (rv + 2);
-    float M = -INFINITY;
+    // split weights 2^(m_s - M) and merged sum L of every sequence of the tile
+    for (int bl = tid; bl < kBT; bl += nt) {
+      const int b = b0 + bl;
+      if (b >= p.B) {
+        for (int s2 = 0; s2 < S; ++s2) fs[bl * S + s2] = 0.f;
+        ls[bl] = 1.f;
+        continue;
+      }
+      const float *part = p.ws + (int64_t)(b * p.H + h) * S * (rv + 2);
+      float M = -INFINITY;
 #pragma unroll 4
-    for (int s2 = 0; s2 < S; ++s2) M = fmaxf(M, part[s2 * (rv + 2)]);
-    float L = 0.f;
+      for (int s2 = 0; s2 < S; ++s2) M = fmaxf(M, part[s2 * (rv + 2)]);
+      float L = 0.f;
 #pragma unroll 4
-    for (int s2 = 0; s2 < S; ++s2) {
-      const float ms = part[s2 * (rv + 2)];
-      const float f = ms == -INFINITY ? 0.f : exp2f(ms - M);  // empty split: weight 0
-      fs[bl * S + s2] = f;
-      L = fmaf(part[s2 * (rv + 2) + 1], f, L);
+      for (int s2 = 0; s2 < S; ++s2) {
+        const float ms = part[s2 * (rv + 2)];
+        const float f = ms == -INFINITY ? 0.f : exp2f(ms - M);  // empty split: weight 0
+        fs[bl * S + s2] = f;
+        L = fmaf(part[s2 * (rv + 2) + 1], f, L);
+      }
+      ls[bl] = L;
     }
-    ls[bl] = L;
-  }
-  __syncthreads();
-  // averages A / L; sequences past B get zeros
-  const int na = kBT * rv;
-  for (int e0 = tid; e0 < na; e0 += kLoadBatch * nt) {
-    float a[kLoadBatch];
+    __syncthreads();
+    // averages A / L; sequences past B get zeros
+    const int na = kBT * rv;
+    for (int e0 = tid; e0 < na; e0 += kLoadBatch * nt) {
+      float a[kLoadBatch];
 #pragma unroll
-    for (int u = 0; u < kLoadBatch; ++u) a[u] = 0.f;
-    for (int s2 = 0; s2 < S; ++s2) {
-      float v[kLoadBatch];
+      for (int u = 0; u < kLoadBatch; ++u) a[u] = 0.f;
+      for (int s2 = 0; s2 < S; ++s2) {
+        float v[kLoadBatch];
 #pragma unroll
-      for (int u = 0; u < kLoadBatch; ++u) {
-        const int e = min(e0 + u * nt, na - 1), b = min(b0 + e / rv, p.B - 1);
-        v[u] = p.ws[(int64_t)(b * p.H + h) * S * (rv + 2) + s2 * (rv + 2) + 2 + e % rv];
+        for (int u = 0; u < kLoadBatch; ++u) {
+          const int e = min(e0 + u * nt, na - 1), b = min(b0 + e / rv, p.B - 1);
+          v[u] = p.ws[(int64_t)(b * p.H + h) * S * (rv + 2) + s2 * (rv + 2) + 2 + e % rv];
+        }
+#pragma unroll
+        for (int u = 0; u < kLoadBatch; ++u) {
+          const int e = min(e0 + u * nt, na - 1);
+          a[u] = fmaf(v[u], fs[(e / rv) * S + s2], a[u]);
+        }
       }
 #pragma unroll
       for (int u = 0; u < kLoadBatch; ++u) {
-        const int e = min(e0 + u * nt, na - 1);
-        a[u] = fmaf(v[u], fs[(e / rv) * S + s2], a[u]);
+        const int e = e0 + u * nt;
+        if (e < na) abar[e] = b0 + e / rv < p.B ? a[u] / ls[e / rv] : 0.f;
       }
-    }
-#pragma unroll
-    for (int u = 0; u < kLoadBatch; ++u) {
-      const int e = e0 + u * nt;
-      if (e < na) abar[e] = b0 + e / rv < p.B ? a[u] / ls[e / rv] : 0.f;
     }
   }
   __syncthreads();
