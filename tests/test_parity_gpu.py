@@ -385,6 +385,9 @@ ENCODE_SHAPES = [
     # K = 128 (two chunks, fewer than the ring holds); ragged last blocks
     ("long_recurrence_t16_ctx8k", dict(B=104, D=2, N=24)),
     ("bf16_b32_ctx4k", dict(B=78, D=2, N=16, T=1)),
+    # 33 row blocks x 2 heads x 2 axes = 132 workgroups, not a multiple of the
+    # eight XCDs: the plain workgroup numbering
+    ("extreme_batch_b768_ctx4k", dict(B=821, D=2, N=8, H=2)),
 ]
 
 
