@@ -225,19 +225,19 @@ static_assert(kBT == 8, "batched_merge_lds() sizes the LDS for tiles of 8 sequen
 constexpr int kOnePer = 8;  // partial elements per thread on the one-split path
 
 // Copies the d x rv block of W_up,v,t at wg (16-byte aligned, rows of a
-// whole number of 16-byte chunks) into LDS rows of `pitch` dwords.
-// NB: 16-byte loads a thread issues before it waits.
-template <typename E, int NB = kLoadBatch>
+// whole number of 16-byte chunks) into LDS rows of `pitch` dwords, each
+// thread issuing kBatch 16-byte loads before it waits for them.
+template <typename E, int kBatch = kLoadBatch>
 __device__ __forceinline__ void w_rows_to_lds(const E *wg, int d, int rv, int pitch, uint32_t *wl,
                                               int t, int nt) {
   const u32x4_t *src = reinterpret_cast<const u32x4_t *>(wg);
   const int rc = rv * (int)sizeof(E) / 16, n = d * rc;  // 16-byte chunks per row, in all
-  for (int c0 = t; c0 < n; c0 += NB * nt) {
-    u32x4_t v[NB];
+  for (int c0 = t; c0 < n; c0 += kBatch * nt) {
+    u32x4_t v[kBatch];
 #pragma unroll
-    for (int u = 0; u < NB; ++u) v[u] = src[min(c0 + u * nt, n - 1)];
+    for (int u = 0; u < kBatch; ++u) v[u] = src[min(c0 + u * nt, n - 1)];
 #pragma unroll
-    for (int u = 0; u < NB; ++u) {
+    for (int u = 0; u < kBatch; ++u) {
       const int c = c0 + u * nt;
       if (c < n) {
         uint32_t *dst = wl + (c / rc) * pitch + 4 * (c % rc);
