@@ -255,7 +255,12 @@ __device__ __forceinline__ float w_lds_elem(const uint32_t *row, int r) {
   return (r & 1) ? bf16_hi(row[r >> 1]) : bf16_lo(row[r >> 1]);
 }
 
-template <typename E>
+// G: sequence groups of the up-projection.  With G = 2 (d <= 128) the block
+// has 2 d threads and thread (g, i) computes output i of the kBT / 2
+// sequences of group g: twice the waves of one thread per output, which the
+// chain of LDS reads and FMAs per output needs (measured at d = 128,
+// r_v = 128: 15.0 -> 10.1 us per LLA-2D call; four groups 10.5 us).
+template <typename E, int G>
 __global__ __launch_bounds__(256) void decode_merge_batched(DecodeParams p) {
   const int h = blockIdx.x, b0 = blockIdx.y * kBT, tid = threadIdx.x, nt = blockDim.x;
   const int rv = p.rv, d = p.d, S = p.S;
@@ -346,10 +351,12 @@ __global__ __launch_bounds__(256) void decode_merge_batched(DecodeParams p) {
   }
   __syncthreads();
   const bool vec = sizeof(E) == 2 && rv % 8 == 0 && ((uintptr_t)p.wv & 15u) == 0;
-  for (int i = tid; i < d; i += nt) {
-    float acc[kBT];
+  constexpr int NBT = kBT / G;  // sequences per thread
+  const int bl0 = G > 1 ? (tid / d) * NBT : 0;
+  for (int i = G > 1 ? tid % d : tid; i < d; i += G > 1 ? d : nt) {
+    float acc[NBT];
 #pragma unroll
-    for (int bl = 0; bl < kBT; ++bl) acc[bl] = 0.f;
+    for (int bq = 0; bq < NBT; ++bq) acc[bq] = 0.f;
     const E *w = wg + (int64_t)i * rv;
     if (w_vec || vec) {
       // 8 weights of the row at a time (LDS, else one 16-byte load); the 8
@@ -372,10 +379,11 @@ __global__ __launch_bounds__(256) void decode_merge_batched(DecodeParams p) {
           }
         }
 #pragma unroll
-        for (int bl = 0; bl < kBT; ++bl) {
+        for (int bq = 0; bq < NBT; ++bq) {
+          const int bl = bl0 + bq;
           const float4 a0 = *reinterpret_cast<const float4 *>(abar + bl * rv + 8 * r8);
           const float4 a1 = *reinterpret_cast<const float4 *>(abar + bl * rv + 8 * r8 + 4);
-          float t = acc[bl];
+          float t = acc[bq];
           t = fmaf(wf[0], a0.x, t);
           t = fmaf(wf[1], a0.y, t);
           t = fmaf(wf[2], a0.z, t);
@@ -384,20 +392,22 @@ __global__ __launch_bounds__(256) void decode_merge_batched(DecodeParams p) {
           t = fmaf(wf[5], a1.y, t);
           t = fmaf(wf[6], a1.z, t);
           t = fmaf(wf[7], a1.w, t);
-          acc[bl] = t;
+          acc[bq] = t;
         }
       }
     } else {
       for (int r = 0; r < rv; ++r) {
         const float wf = load_elem(w, r);
 #pragma unroll
-        for (int bl = 0; bl < kBT; ++bl) acc[bl] = fmaf(wf, abar[bl * rv + r], acc[bl]);
+        for (int bq = 0; bq < NBT; ++bq) acc[bq] = fmaf(wf, abar[(bl0 + bq) * rv + r], acc[bq]);
       }
     }
     const float mu = p.muv[(int64_t)h * d + i];
 #pragma unroll
-    for (int bl = 0; bl < kBT; ++bl)
-      if (b0 + bl < p.B) p.out[((int64_t)(b0 + bl) * p.H + h) * d + i] = acc[bl] + mu;
+    for (int bq = 0; bq < NBT; ++bq) {
+      const int b = b0 + bl0 + bq;
+      if (b < p.B) p.out[((int64_t)b * p.H + h) * d + i] = acc[bq] + mu;
+    }
   }
 }
 
@@ -752,20 +762,32 @@ hipError_t launch_decode_valu(const DecodeParams &p, int dtype, hipStream_t st) 
 
 hipError_t launch_decode_merge_batched(const DecodeParams &p, int dtype, hipStream_t st) {
   dim3 grid(p.H, (p.B + kBT - 1) / kBT);
-  const int threads = p.d >= 256 ? 256 : (p.d + 63) / 64 * 64;
+  const bool two = p.d <= 128;  // two sequence groups, 2 d threads
+  const int threads = two ? 2 * p.d : p.d >= 256 ? 256 : (p.d + 63) / 64 * 64;
   const BatchedMergeLds lay = batched_merge_lds(p.d, p.rv, p.S, dtype == LLA_DT_F32 ? 4 : 2);
   DecodeParams q = p;
   q.w_lds = lay.with_w <= kBatchedMergeWLdsMax ? 1 : 0;  // else W_up,v,t is read from HBM
   const size_t sm = q.w_lds ? lay.with_w : lay.base;
   if (sm > 160 * 1024) return hipErrorInvalidValue;
-  const void *fn = dtype == LLA_DT_F32 ? reinterpret_cast<const void *>(decode_merge_batched<float>)
-                                       : reinterpret_cast<const void *>(decode_merge_batched<bf16_t>);
+  const void *fn =
+      dtype == LLA_DT_F32
+          ? (two ? reinterpret_cast<const void *>(decode_merge_batched<float, 2>)
+                 : reinterpret_cast<const void *>(decode_merge_batched<float, 1>))
+          : (two ? reinterpret_cast<const void *>(decode_merge_batched<bf16_t, 2>)
+                 : reinterpret_cast<const void *>(decode_merge_batched<bf16_t, 1>));
   const hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)sm);
   if (e != hipSuccess) return e;
-  if (dtype == LLA_DT_F32)
-    hipLaunchKernelGGL(decode_merge_batched<float>, grid, dim3(threads), sm, st, q);
-  else
-    hipLaunchKernelGGL(decode_merge_batched<bf16_t>, grid, dim3(threads), sm, st, q);
+  if (dtype == LLA_DT_F32) {
+    if (two)
+      hipLaunchKernelGGL((decode_merge_batched<float, 2>), grid, dim3(threads), sm, st, q);
+    else
+      hipLaunchKernelGGL((decode_merge_batched<float, 1>), grid, dim3(threads), sm, st, q);
+  } else {
+    if (two)
+      hipLaunchKernelGGL((decode_merge_batched<bf16_t, 2>), grid, dim3(threads), sm, st, q);
+    else
+      hipLaunchKernelGGL((decode_merge_batched<bf16_t, 1>), grid, dim3(threads), sm, st, q);
+  }
   return hipGetLastError();
 }
 
