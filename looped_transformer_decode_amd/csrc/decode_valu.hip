@@ -460,72 +460,103 @@ __global__ __launch_bounds__(256, 4) void decode_merge_inflight(DecodeParams p, 
   const int first = min(max(p.pos[b], 0), p.N);
   const bool act = t < d;
 
-  // W_up,v,t of head h into LDS, 16-byte loads (used when its rows allow them)
+  // Every global load of the first phase goes out before any is waited
+  // for: the split maxima and sums of the store partials, the in-flight
+  // values, the RoPE operands of the in-flight keys and queries, then
+  // W_up,v,t, whose copy into LDS waits for all of them at once (measured
+  // with the matrix-core sum below: 30.8 -> 29.2 us per long-recurrence call
+  // for this phase, 25.8 us with both).
   const E *wg = reinterpret_cast<const E *>(p.wv) + (int64_t)h * d * rv;
   const int row_bytes = rv * (int)sizeof(E);
   const bool w_vec =
       p.w_lds != 0 && row_bytes % 16 == 0 && (reinterpret_cast<uintptr_t>(wg) & 15) == 0;
-  if (w_vec) w_rows_to_lds(wg, d, rv, lay.w_pitch, wl, t, nt);
-
-  // The in-flight values of the first kVAhead tokens, fetched now (they
-  // replace the keys in LDS once the scores are done) so that their memory
-  // latency overlaps the phases in between.
+  const float *part_t = p.ws + (int64_t)((b * nq + min(t, nq - 1)) * H + h) * S * (rv + 2);
+  constexpr int kSPre = 2;  // splits whose (m, l) a thread holds in registers
+  float pm[kSPre], pl[kSPre];
+#pragma unroll
+  for (int s2 = 0; s2 < kSPre; ++s2) {
+    const int sc2 = min(s2, S - 1);
+    pm[s2] = part_t[sc2 * (rv + 2)];
+    pl[s2] = part_t[sc2 * (rv + 2) + 1];
+  }
+  // The in-flight values of the first kVAhead tokens (they replace the keys
+  // in LDS once the scores are done).
   constexpr int kVAhead = 16;
   float vah[kVAhead];
 #pragma unroll
   for (int j = 0; j < kVAhead; ++j)
     vah[j] = v_new[((int64_t)(b * nq + min(j, nq - 1)) * H + h) * d + (act ? t : 0)];
-  // rotate-half RoPE of the in-flight keys and the queries at pos0 + m
-  if (act) {
-    const int u = t < half ? t : t - half;   // pair index
-    const int pt = t < half ? t + half : u;  // the other element of the pair
-    for (int m0 = 0; m0 < nq; m0 += kLoadBatch) {
-      float xk[kLoadBatch], yk[kLoadBatch], xq[kLoadBatch], yq[kLoadBatch], c[kLoadBatch],
-          s[kLoadBatch];
+  // rotate-half RoPE of the in-flight keys and the queries at pos0 + m:
+  // thread (token slot ms, pair u) forms elements u and u + d/2 of tokens
+  // ms, ms + tpp, ... (kRPass of them per batch)
+  constexpr int kRPass = 4;
+  const int tpp = nt / half;  // tokens per pass
+  const int u = t % half, ms = t / half;
+  const bool ract = ms < tpp;
+  float xk[kRPass], yk[kRPass], xq[kRPass], yq[kRPass], cc[kRPass], ss[kRPass];
+  auto rope_load = [&](int m0) {
 #pragma unroll
-      for (int j = 0; j < kLoadBatch; ++j) {
-        const int m = min(m0 + j, nq - 1);
-        const int64_t row = ((int64_t)(b * nq + m) * H + h) * d;
-        const float *cs = p.rope_f32 + (int64_t)min(first + m, p.N - 1) * d;  // [d/2][2]
-        xk[j] = k_new[row + t];
-        yk[j] = k_new[row + pt];
-        xq[j] = p.q[row + t];
-        yq[j] = p.q[row + pt];
-        c[j] = cs[2 * u];
-        s[j] = cs[2 * u + 1];
-      }
+    for (int j = 0; j < kRPass; ++j) {
+      const int m = min(m0 + ms + j * tpp, nq - 1);
+      const int64_t row = ((int64_t)(b * nq + m) * H + h) * d;
+      const float *cs = p.rope_f32 + (int64_t)min(first + m, p.N - 1) * d;  // [d/2][2]
+      xk[j] = k_new[row + u];
+      yk[j] = k_new[row + u + half];
+      xq[j] = p.q[row + u];
+      yq[j] = p.q[row + u + half];
+      cc[j] = cs[2 * u];
+      ss[j] = cs[2 * u + 1];
+    }
+  };
+  auto rope_store = [&](int m0) {
 #pragma unroll
-      for (int j = 0; j < kLoadBatch; ++j) {
-        const int m = m0 + j;
-        if (m < nq) {
-          float rk, rq;
-          if (t < half) {
-            rk = xk[j] * c[j] - yk[j] * s[j];
-            rq = xq[j] * c[j] - yq[j] * s[j];
-          } else {
-            rk = xk[j] * c[j] + yk[j] * s[j];
-            rq = xq[j] * c[j] + yq[j] * s[j];
-          }
-          kr[m * d + t] = rk;
-          qr[m * d + t] = rq * p.scale_log2;
-        }
+    for (int j = 0; j < kRPass; ++j) {
+      const int m = m0 + ms + j * tpp;
+      if (ract && m < nq) {
+        kr[m * d + u] = xk[j] * cc[j] - yk[j] * ss[j];
+        kr[m * d + u + half] = yk[j] * cc[j] + xk[j] * ss[j];
+        qr[m * d + u] = (xq[j] * cc[j] - yq[j] * ss[j]) * p.scale_log2;
+        qr[m * d + u + half] = (yq[j] * cc[j] + xq[j] * ss[j]) * p.scale_log2;
       }
     }
+  };
+  rope_load(0);
+  if (w_vec) w_rows_to_lds(wg, d, rv, lay.w_pitch, wl, t, nt);
+  rope_store(0);
+  for (int m0 = kRPass * tpp; m0 < nq; m0 += kRPass * tpp) {
+    rope_load(m0);
+    rope_store(m0);
   }
   // store partials of every query, merged over the splits: the split
   // weights 2^(m_s - M) of every query (the numerators follow the scores)
   for (int i = t; i < nq; i += nt) {
     const float *part = p.ws + (int64_t)((b * nq + i) * H + h) * S * (rv + 2);
     float M = -INFINITY;
+    if (i == t && S <= kSPre) {
+#pragma unroll
+      for (int s2 = 0; s2 < kSPre; ++s2) M = s2 < S ? fmaxf(M, pm[s2]) : M;
+    } else {
 #pragma unroll 4
-    for (int s2 = 0; s2 < S; ++s2) M = fmaxf(M, part[s2 * (rv + 2)]);
+      for (int s2 = 0; s2 < S; ++s2) M = fmaxf(M, part[s2 * (rv + 2)]);
+    }
     float L = 0.f;
+    if (i == t && S <= kSPre) {
+#pragma unroll
+      for (int s2 = 0; s2 < kSPre; ++s2) {
+        if (s2 < S) {
+          const float w = pm[s2] == -INFINITY ? 0.f : exp2f(pm[s2] - M);
+          wsp[i * S + s2] = w;
+          L = fmaf(pl[s2], w, L);
+        }
+      }
+    } else {
 #pragma unroll 4
-    for (int s2 = 0; s2 < S; ++s2) {
-      const float ms = part[s2 * (rv + 2)];
-      const float w = ms == -INFINITY ? 0.f : exp2f(ms - M);
-      wsp[i * S + s2] = w;
-      L = fmaf(part[s2 * (rv + 2) + 1], w, L);
+      for (int s2 = 0; s2 < S; ++s2) {
+        const float msv = part[s2 * (rv + 2)];
+        const float w = msv == -INFINITY ? 0.f : exp2f(msv - M);  // empty split: weight 0
+        wsp[i * S + s2] = w;
+        L = fmaf(part[s2 * (rv + 2) + 1], w, L);
+      }
     }
     st[4 * i] = M;
     st[4 * i + 1] = L;
@@ -685,16 +716,29 @@ __global__ __launch_bounds__(256, 4) void decode_merge_inflight(DecodeParams p, 
             acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[ks], bw, acc, 0, 0, 0);
             acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(alo[ks], bw, acc, 0, 0, 0);
           }
+          // sum_m w_m v_m for the tile's 16 queries and 16 elements on the
+          // matrix cores (v_mfma_f32_16x16x4_f32: fp32 operands, exact
+          // products): A = the weights (query l % 16, token 4 s + l / 16), B =
+          // the values (token 4 s + l / 16, element l % 16); tokens past nq
+          // enter as zeros.  Two LDS reads per lane and k-step, where a loop
+          // per output element read both operands for every token.
+          f32x4_t mix = {0.f, 0.f, 0.f, 0.f};
+          {
+            const int qa = min(16 * qt + l16, nq - 1);
+            for (int m0 = 0; m0 < nq; m0 += 4) {
+              const int m = m0 + g;
+              const float wa = m < nq ? sc[qa * nq + min(m, nq - 1)] : 0.f;
+              const float vb = m < nq ? kr[min(m, nq - 1) * d + el] : 0.f;
+              mix = __builtin_amdgcn_mfma_f32_16x16x4f32(wa, vb, mix, 0, 0, 0);
+            }
+          }
           // [fs (W_up,v,t A + mu_v,t L_s) + sum_m w_m v_m] / den, w_m = 0 for m > i
           const float mu = mus[j];
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
             const int q = 16 * qt + 4 * g + i;
             if (q < nq) {
-              float num = fmaf(st[4 * q], acc[i], st[4 * q + 1] * mu);
-              const float *wq = sc + q * nq;
-#pragma unroll 8
-              for (int m = 0; m < nq; ++m) num = fmaf(wq[m], kr[m * d + el], num);
+              const float num = fmaf(st[4 * q], acc[i], st[4 * q + 1] * mu) + mix[i];
               p.out[((int64_t)(b * nq + q) * H + h) * d + el] = num / st[4 * q + 2];
             }
           }
