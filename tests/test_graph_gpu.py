@@ -17,7 +17,9 @@ pytestmark = pytest.mark.gpu
     ("extreme_batch_b768_ctx4k", dict(B=3, D=2, N=300)),
     ("lla2d_b256_ctx4k", dict(B=2, D=2, N=170)),
     ("bf16_b32_ctx4k", dict(B=3, D=2, N=700, H=8)),      # several splits + merge
-], ids=["per_head", "lla2d", "per_head_split"])
+    # 400 appended rows: enough row blocks for the LDS-ring encode
+    ("extreme_batch_b768_ctx4k", dict(B=400, D=2, N=16)),
+], ids=["per_head", "lla2d", "per_head_split", "per_head_streamed_encode"])
 def test_graph_replay_matches_eager(device, tmpl, kw):
     w = WORKLOADS[tmpl].scaled(**kw)
     vals = host_store(w)
@@ -38,7 +40,8 @@ def test_graph_replay_matches_eager(device, tmpl, kw):
         xs = [to_device(x[a].reshape(w.B, 1, w.H, K), w.dtype, device) for a in "kv"]
         mus = [to_device(codec.mu(a, 0), "f32", device) for a in "kv"]
         wds = [to_device(codec.w_down(a, 0), w.dtype, device) for a in "kv"]
-    pos = torch.tensor([w.N - 1, 41, 200][:w.B], dtype=torch.int32, device=device)
+    pos = torch.tensor(np.resize([w.N - 1, min(41, w.N - 1), min(200, w.N - 1)], w.B),
+                       dtype=torch.int32, device=device)
     start = torch.full((w.B,), w.N - 1, dtype=torch.int32, device=device)
     out = torch.empty((w.B, w.H, w.d), dtype=torch.float32, device=device)
     ws = L.workspace(store)
