@@ -13,7 +13,9 @@
 // Work split.  A workgroup of four waves owns (row block, stored head, axis,
 // column group); each wave owns MT tiles of 16 rows (rows = (sequence, new
 // token)).  With few row blocks (LLA-2D, small batches) the variant at the
-// end of this file splits the contraction over the waves instead.  The
+// end of this file splits the contraction over the waves instead; with many
+// rows the form in encode_stream.hip (x and W_down through an LDS ring)
+// takes over.  The
 // stacked length K is walked in chunks of 128.  Rows of x stream from HBM
 // straight into registers: within a chunk, lane group g = lane/16 reads 64
 // contiguous bytes of its row, and the contraction index is permuted
