@@ -648,6 +648,24 @@ def run_mfma_ceiling(args, torch):
         log(f"[bench] mfma ceiling: {waves_per_simd} wave(s)/SIMD, {ms * 1e3:.1f} us: "
             f"{results[waves_per_simd][1]:.1f} TFLOP/s")
     best = max(results, key=lambda k: results[k][1])
+    # How far the matrix cores and the vector ALU of one SIMD overlap: one
+    # MFMA-only and one FMA-only wave per SIMD, each alone and together.
+    from synth.device import mfma_valu_overlap
+    blocks, it = 256, 8192
+    sink = torch.empty(blocks * 512, dtype=torch.float32, device=dev)
+    ovl = {}
+    for mode, name in ((1, "mfma_only"), (2, "valu_only"), (3, "both")):
+        mfma_valu_overlap(blocks, 64, mode, sink)
+        torch.cuda.synchronize()
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+        ev[0].record()
+        mfma_valu_overlap(blocks, it, mode, sink)
+        ev[1].record()
+        torch.cuda.synchronize()
+        ovl[name] = round(ev[0].elapsed_time(ev[1]) * 1e3, 1)
+    ovl["hidden_share_of_shorter"] = round(
+        (ovl["mfma_only"] + ovl["valu_only"] - ovl["both"]) / min(ovl["mfma_only"], ovl["valu_only"]), 3)
+    log(f"[bench] mfma/valu overlap (us): {ovl}")
     print(json.dumps({"metric": "bf16 MFMA TFLOP/s (register-only 32x32x16 chains, context for "
                                 "the LLA-2D roofline fraction)",
                       "value": round(results[best][1], 1), "unit": "TFLOP/s",
@@ -655,7 +673,8 @@ def run_mfma_ceiling(args, torch):
                       "frac": round(results[best][1] / MFMA_BF16_PEAK_TFLOPS, 4),
                       "kernel": "mfma_spin (synth/fill.hip)", "waves_per_simd": best,
                       "sweep": {str(k): {"us": round(v[0] * 1e3, 1), "TFLOPs": round(v[1], 1)}
-                                for k, v in results.items()}}), flush=True)
+                                for k, v in results.items()},
+                      "mfma_valu_overlap_us": ovl}), flush=True)
 
 
 def main():

@@ -26,6 +26,9 @@ def _load():
         L.synth_mfma_spin.argtypes = [ctypes.c_int32, ctypes.c_int32, ctypes.c_void_p,
                                       ctypes.c_void_p]
         L.synth_mfma_spin.restype = ctypes.c_int
+        L.synth_mfma_valu_overlap.argtypes = [ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
+                                              ctypes.c_void_p, ctypes.c_void_p]
+        L.synth_mfma_valu_overlap.restype = ctypes.c_int
         _lib = L
     return _lib
 
@@ -63,3 +66,15 @@ def mfma_spin(blocks: int, iters: int, sink: torch.Tensor) -> None:
                                   torch.cuda.current_stream(sink.device).cuda_stream)
     if err != 0:
         raise RuntimeError(f"synth_mfma_spin failed: hipError {err}")
+
+
+def mfma_valu_overlap(blocks: int, iters: int, mode: int, sink: torch.Tensor) -> None:
+    """Launch the two-pipe overlap kernel: blocks x 8 waves; mode 1 = MFMA
+    waves only, 2 = vector-ALU waves only, 3 = both (one of each per SIMD);
+    sink: float32, at least blocks * 512 values."""
+    if sink.numel() < blocks * 512 or sink.dtype != torch.float32:
+        raise ValueError("sink too small")
+    err = _load().synth_mfma_valu_overlap(blocks, iters, mode, sink.data_ptr(),
+                                          torch.cuda.current_stream(sink.device).cuda_stream)
+    if err != 0:
+        raise RuntimeError(f"synth_mfma_valu_overlap failed: hipError {err}")

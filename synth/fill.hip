@@ -8,7 +8,8 @@
 // Also here, for the benchmark's context figures: a plain streaming-read
 // kernel (synth_read_stream) and a register-only matrix-core kernel
 // (synth_mfma_spin), the practical HBM and bf16 MFMA ceilings the decode
-// kernels are compared with.
+// kernels are compared with, and a kernel that measures how far the matrix
+// cores and the vector ALU of one SIMD overlap (synth_mfma_valu_overlap).
 #include <cstdint>
 
 #include <hip/hip_runtime.h>
@@ -111,7 +112,59 @@ __global__ __launch_bounds__(256) void mfma_spin(int iters, float *sink) {
 #endif
 }
 
+// Overlap of the two pipes of a SIMD: 512-thread workgroups, waves w and
+// w + 4 share a SIMD.  mode bit 0: waves 0-3 run the register-only MFMA
+// rounds of mfma_spin; mode bit 1: waves 4-7 run 32 fp32 FMAs per round
+// (eight independent chains, one wave64 v_fma per instruction).
+__global__ __launch_bounds__(512) void mfma_valu_overlap(int iters, int mode, float *sink) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  float t = 0.f;
+  if ((mode & 1) && wave < 4) {
+    bf16x8_v a, b;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      a[e] = (short)(0x3F80 + ((lane + e) & 7));
+      b[e] = (short)(0x3C00 + ((lane * 3 + e) & 7));
+    }
+    f32x16_v c0 = {}, c1 = {}, c2 = {}, c3 = {};
+    for (int i = 0; i < iters; ++i) {
+      c0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c0, 0, 0, 0);
+      c1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(b, a, c1, 0, 0, 0);
+      c2 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, a, c2, 0, 0, 0);
+      c3 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(b, b, c3, 0, 0, 0);
+    }
+#pragma unroll
+    for (int k = 0; k < 16; ++k) t += c0[k] + c1[k] + c2[k] + c3[k];
+  }
+  if ((mode & 2) && wave >= 4) {
+    float x[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) x[e] = 1.0f + 1e-7f * (float)(lane + e);
+    for (int i = 0; i < iters; ++i) {
+#pragma unroll
+      for (int rep = 0; rep < 4; ++rep)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) x[e] = __builtin_fmaf(x[e], 0.999999f, 1e-7f);
+    }
+#pragma unroll
+    for (int e = 0; e < 8; ++e) t += x[e];
+  }
+  if (t == 1234.5f) sink[blockIdx.x * 512 + threadIdx.x] = t;
+#endif
+}
+
 }  // namespace
+
+// Launches the overlap kernel: `blocks` workgroups of eight waves; see
+// mfma_valu_overlap for `mode`.  sink holds blocks * 512 floats.
+extern "C" int synth_mfma_valu_overlap(int32_t blocks, int32_t iters, int32_t mode, float *sink,
+                                       hipStream_t stream) {
+  if (blocks <= 0 || iters <= 0 || mode < 1 || mode > 3) return (int)hipErrorInvalidValue;
+  hipLaunchKernelGGL(mfma_valu_overlap, dim3((unsigned)blocks), dim3(512), 0, stream, iters, mode,
+                     sink);
+  return (int)hipGetLastError();
+}
 
 // Launches the matrix-core ceiling kernel: `blocks` workgroups of four waves,
 // each wave 4 * iters MFMAs of 32x32x16 (32768 flop each).
