@@ -55,6 +55,7 @@ namespace {
 constexpr int kT = 64;        // GEMM output tile
 constexpr int kBK = 16;       // GEMM k-chunk
 constexpr int kThreads = 256;
+constexpr size_t kMaxLds = 160 * 1024;  // dynamic LDS one gfx950 workgroup may use
 
 // Operands of the tiled GEMM, element (g, row, col).
 struct MatF32 {
@@ -337,191 +338,308 @@ __global__ __launch_bounds__(kThreads) void start_block(float *Q, int64_t n) {
 }
 
 // out[g][i][j] = sum_k P[g][k][i] * R[g][k][j] in fp64 (P, R: [K][m] fp32).
-// Block = (16 x 16 output tile, g); k in chunks of 64 through LDS.
-__global__ __launch_bounds__(kThreads) void small_gram64(const float *P, const float *R, int K,
-                                                         int m, double *out) {
-  __shared__ float Ps[64][17], Rs[64][17];
-  const int g = blockIdx.z, i0 = blockIdx.y * 16, j0 = blockIdx.x * 16;
-  const int tid = threadIdx.x, ti = tid / 16, tj = tid % 16;
+// Block = (32 x 32 output tile, g), eight waves: wave w multiplies quadrant
+// w % 4 over half w / 4 of every chunk of 64 k, one v_mfma_f64_16x16x4f64
+// per four k (fp32 products are exact in fp64, the sums are fp64); the two
+// halves are added through LDS at the end.  Chunks are staged in LDS as
+// whole 128-byte rows, the next chunk loaded into registers while the
+// current one is multiplied.  With sym (P == R) only tiles on and above the
+// diagonal run, and each entry i <= j is also written at (j, i), so that the
+// result is exactly symmetric.
+// Operand lanes: A row l % 16 and B column l % 16 of the quadrant at
+// k = 4 s + l / 16; accumulator entry e: row l / 16 + 4 e, column l % 16 (the
+// f64 form interleaves its rows, unlike the f32 16x16x4 form's 4 (l / 16) + e).
+typedef double f64x4_t __attribute__((ext_vector_type(4)));
+constexpr int kSgThreads = 512;
+constexpr int kSgT = 32;   // output tile
+constexpr int kSgK = 64;   // k per chunk
+constexpr int kSgPer = kSgK * kSgT / kSgThreads;  // elements per thread, operand and chunk
+__global__ __launch_bounds__(kSgThreads) void small_gram64(const float *P, const float *R, int K,
+                                                           int m, int sym, double *out) {
+  if (sym && blockIdx.y > blockIdx.x) return;
+  __shared__ float As[2][kSgK][kSgT + 1], Bs[2][kSgK][kSgT + 1];
+  __shared__ double part[4][4][64];
+  const int g = blockIdx.z, i0 = blockIdx.y * kSgT, j0 = blockIdx.x * kSgT;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, kl = lane >> 4;
+  const int qi = (wave >> 1) & 1, qj = wave & 1, kh = wave >> 2;
   const float *Pg = P + (int64_t)g * K * m, *Rg = R + (int64_t)g * K * m;
-  double acc = 0.0;
-  for (int k0 = 0; k0 < K; k0 += 64) {
-    for (int e = tid; e < 64 * 16; e += kThreads) {
-      const int kk = e / 16, c = e % 16, k = k0 + kk;
-      Ps[kk][c] = (k < K && i0 + c < m) ? Pg[(int64_t)k * m + i0 + c] : 0.f;
-      Rs[kk][c] = (k < K && j0 + c < m) ? Rg[(int64_t)k * m + j0 + c] : 0.f;
+  float ra[kSgPer], rb[kSgPer];
+  auto fetch = [&](int k0) {
+#pragma unroll
+    for (int q = 0; q < kSgPer; ++q) {
+      const int e = tid + kSgThreads * q, kk = k0 + e / kSgT, c = e % kSgT;
+      ra[q] = kk < K && i0 + c < m ? Pg[(int64_t)kk * m + i0 + c] : 0.f;
+      rb[q] = kk < K && j0 + c < m ? Rg[(int64_t)kk * m + j0 + c] : 0.f;
     }
+  };
+  auto stage = [&](int buf) {
+#pragma unroll
+    for (int q = 0; q < kSgPer; ++q) {
+      const int e = tid + kSgThreads * q;
+      As[buf][e / kSgT][e % kSgT] = ra[q];
+      Bs[buf][e / kSgT][e % kSgT] = rb[q];
+    }
+  };
+  f64x4_t acc = {0.0, 0.0, 0.0, 0.0};
+  fetch(0);
+  stage(0);
+  __syncthreads();
+  int buf = 0;
+  for (int k0 = 0; k0 < K; k0 += kSgK) {
+    const bool more = k0 + kSgK < K;
+    if (more) fetch(k0 + kSgK);
+#pragma unroll
+    for (int s = 0; s < kSgK / 8; ++s) {
+      const int kk = kh * (kSgK / 2) + 4 * s + kl;
+      acc = __builtin_amdgcn_mfma_f64_16x16x4f64((double)As[buf][kk][qi * 16 + (lane & 15)],
+                                                 (double)Bs[buf][kk][qj * 16 + (lane & 15)], acc,
+                                                 0, 0, 0);
+    }
+    if (more) stage(buf ^ 1);
     __syncthreads();
-#pragma unroll 8
-    for (int kk = 0; kk < 64; ++kk) acc = fma((double)Ps[kk][ti], (double)Rs[kk][tj], acc);
-    __syncthreads();
+    buf ^= 1;
   }
-  if (i0 + ti < m && j0 + tj < m) out[((int64_t)g * m + i0 + ti) * m + j0 + tj] = acc;
+  if (kh)
+    for (int e = 0; e < 4; ++e) part[wave & 3][e][lane] = acc[e];
+  __syncthreads();
+  if (!kh) {
+    const int j = j0 + qj * 16 + (lane & 15);
+    for (int e = 0; e < 4; ++e) {
+      const int i = i0 + qi * 16 + kl + 4 * e;
+      const double v = acc[e] + part[wave][e][lane];
+      if (i >= m || j >= m) continue;
+      if (!sym) {
+        out[((int64_t)g * m + i) * m + j] = v;
+      } else if (i <= j) {
+        out[((int64_t)g * m + i) * m + j] = v;
+        out[((int64_t)g * m + j) * m + i] = v;
+      }
+    }
+  }
 }
 
-// Cholesky A = L L^T of one codec's m x m matrix (fp64, in LDS, with a tiny
-// diagonal shift so that a rank-deficient block cannot break it), then
-// Rinv = (L^T)^-1, the factor that makes Y Rinv orthonormal.
-// Factorisation step j: every thread forms the pivot itself and updates its
-// (row, column) share of the trailing lower triangle, scaling column j on the
-// fly; after the step's one barrier the column is stored scaled (the next
-// step reads none of it).
-__global__ __launch_bounds__(kThreads) void chol_inv(const double *A, int m, float *Rinv) {
-  extern __shared__ double L[];  // [m][m]
-  const int g = blockIdx.x, tid = threadIdx.x, ty = tid / 16, tx = tid % 16;
+// Cholesky A = L L^T of one codec's m x m matrix (fp64, with a tiny diagonal
+// shift so that a rank-deficient block cannot break it), then
+// Rinv = (L^T)^-1 = X^T with X = L^-1, the factor that makes Y Rinv
+// orthonormal.  The array M holds L in its lower triangle and X transposed
+// in its strict upper one (X[i][c] at (c, i); X starts as the identity).
+// Thread (ty, tx) of a 16 x 16 block keeps the entries (r, col) with
+// r = ty + 16 a and col = tx + 16 b (a, b < Q, 16 Q >= m) in registers.
+// Step j: the owners of column j publish it to LDS (one barrier, two
+// buffers); every thread reads the pivot and the entries of its rows and
+// columns at once, forms 1 / d = 1 / sqrt(M[j][j]) itself (hardware
+// reciprocal square root, two Newton steps) and w = column j / d,
+// w[j] = 1 / d: column j of L scaled below the diagonal, row j of X above
+// it.  Forward elimination of L (trailing update l_rj l_colj) and of the
+// identity (X[col][r] -= l_colj X[j][r], r <= j) are then one update
+// M[r][col] -= w[r] w[col], col > j.  It also reaches the upper entries
+// j < r < col, which are not yet X's; row j is zeroed before its update, so
+// those start from zero when they become X's, and L's rows left of the
+// diagonal, no longer read once their column is published, may hold
+// anything.  The owners of column j then store w there (final: 1 / d on the
+// diagonal, which is Rinv's).
+constexpr int kCholThreads = 256;
+constexpr int kCholT = 16;  // kCholT x kCholT threads
+template <int Q>
+__global__ __launch_bounds__(kCholThreads) void chol_inv(const double *A, int m, float *Rinv) {
+  __shared__ double buf[2][Q * kCholT];
+  const int g = blockIdx.x, tid = threadIdx.x, ty = tid / kCholT, tx = tid % kCholT;
   const double *Ag = A + (int64_t)g * m * m;
-  for (int e = tid; e < m * m; e += kThreads) L[e] = Ag[e];
-  __syncthreads();
+  double v[Q][Q];
   double dmax = 0.0;
-  for (int i = 0; i < m; ++i) dmax = fmax(dmax, L[i * m + i]);
+  for (int i = 0; i < m; ++i) dmax = fmax(dmax, Ag[(int64_t)i * m + i]);
   const double shift = 1e-13 * dmax + 1e-300;
-  for (int j = 0; j < m; ++j) {
-    const double djj = sqrt(fmax(L[j * m + j] + shift, shift));
-    const double inv = 1.0 / djj;
-    for (int i = j + 1 + ty; i < m; i += 16) {
-      const double lij = L[i * m + j] * inv;
-      for (int k = j + 1 + tx; k <= i; k += 16) L[i * m + k] -= lij * (L[k * m + j] * inv);
+#pragma unroll
+  for (int a = 0; a < Q; ++a)
+#pragma unroll
+    for (int b = 0; b < Q; ++b) {
+      const int r = ty + kCholT * a, col = tx + kCholT * b;
+      v[a][b] = r < m && col <= r ? Ag[(int64_t)r * m + col] : 0.0;
     }
-    __syncthreads();
-    for (int i = j + tid; i < m; i += kThreads) L[i * m + j] = i == j ? djj : L[i * m + j] * inv;
-  }
-  __syncthreads();
-  // Linv (lower triangular) goes into the unused upper triangle, transposed:
-  // Linv[i][c] (i > c) at [c][i]; thread c forms column c from the rows of L
-  // and its own earlier entries, all in LDS.
-  float *Rg = Rinv + (int64_t)g * m * m;
-  for (int c = tid; c < m; c += kThreads) {
-    const double inv_cc = 1.0 / L[c * m + c];
-    Rg[(int64_t)c * m + c] = (float)inv_cc;
-    const double *Lc = L + c * m;  // this column's Linv entries, at [c][k]
-    for (int i = c + 1; i < m; ++i) {
-      const double *Li = L + i * m;
-      // four independent partial sums: the LDS reads of one step need not
-      // wait for the previous step's sum
-      double s0 = Li[c] * inv_cc, s1 = 0.0, s2 = 0.0, s3 = 0.0;
-      int k = c + 1;
-      for (; k + 3 < i; k += 4) {
-        s0 += Li[k] * Lc[k];
-        s1 += Li[k + 1] * Lc[k + 1];
-        s2 += Li[k + 2] * Lc[k + 2];
-        s3 += Li[k + 3] * Lc[k + 3];
+  // j = 16 jo + jl: the block jo is a constant in each unrolled copy, so the
+  // owners' slots are known and the finished column blocks b < jo (w = 0)
+  // are skipped
+#pragma unroll
+  for (int jo = 0; jo < Q; ++jo) {
+#pragma unroll 1
+    for (int jl = 0; jl < kCholT; ++jl) {
+      const int j = kCholT * jo + jl;
+      if (j >= m) break;
+      double *bj = buf[j & 1];
+      const bool owner = tx == jl;
+      if (owner) {
+#pragma unroll
+        for (int a = 0; a < Q; ++a)
+          if (ty + kCholT * a < m) bj[ty + kCholT * a] = v[a][jo];
       }
-      for (; k < i; ++k) s0 += Li[k] * Lc[k];
-      const double v = -((s0 + s1) + (s2 + s3)) / Li[i];
-      L[c * m + i] = v;
-      Rg[(int64_t)c * m + i] = (float)v;  // Rinv[c][i] = Linv[i][c]
+      __syncthreads();
+      const double piv = bj[j];
+      double br[Q], bc[Q];
+#pragma unroll
+      for (int q = 0; q < Q; ++q) {
+        br[q] = bj[min(ty + kCholT * q, m - 1)];
+        bc[q] = bj[min(tx + kCholT * q, m - 1)];
+      }
+      const double x = fmax(piv + shift, shift);
+      double inv = __builtin_amdgcn_rsq(x);
+#pragma unroll
+      for (int it = 0; it < 2; ++it) inv = fma(0.5 * inv, fma(-x * inv, inv, 1.0), inv);
+      double wr[Q], wc[Q];
+#pragma unroll
+      for (int q = 0; q < Q; ++q) {
+        wr[q] = q == jo && ty == jl ? inv : br[q] * inv;
+        wc[q] = q > jo || (q == jo && tx > jl) ? bc[q] * inv : 0.0;
+      }
+      if (ty == jl) {
+#pragma unroll
+        for (int b = jo; b < Q; ++b) v[jo][b] = 0.0;
+      }
+#pragma unroll
+      for (int a = 0; a < Q; ++a)
+#pragma unroll
+        for (int b = jo; b < Q; ++b) v[a][b] = fma(-wr[a], wc[b], v[a][b]);
+      if (owner) {
+#pragma unroll
+        for (int a = 0; a < Q; ++a) v[a][jo] = wr[a];
+      }
     }
-    for (int i = 0; i < c; ++i) Rg[(int64_t)c * m + i] = 0.f;
   }
+  // Rinv[c][i] = X[i][c]: M[c][i] above the diagonal, 1 / l_cc on it
+  float *Rg = Rinv + (int64_t)g * m * m;
+#pragma unroll
+  for (int a = 0; a < Q; ++a)
+#pragma unroll
+    for (int b = 0; b < Q; ++b) {
+      const int r = ty + kCholT * a, col = tx + kCholT * b;
+      if (r < m && col < m) Rg[(int64_t)r * m + col] = col >= r ? (float)v[a][b] : 0.f;
+    }
 }
 
 // Symmetric eigenproblem of one codec's m x m matrix B (fp64, in LDS) by
 // cyclic Jacobi rotations; disjoint pairs of a round-robin schedule rotate in
-// parallel.  Writes the eigenvectors (columns of U, fp64, global), the
-// eigenvalues and the order that sorts them descending.
-__global__ __launch_bounds__(kThreads) void jacobi(const double *B, int m, int sweeps, double *U,
-                                                   double *evals, int *order) {
-  extern __shared__ double S[];  // [m][m], rotations [mp/2][2], sums [2][256], pairs [mp/2][2]
+// parallel.  One round applies B <- J^T B J and U <- U J in a single pass:
+// the entries in rows (a, b) of one pair and columns (a', b') of another
+// depend only on those four entries and the two rotations, so each thread
+// takes such 2 x 2 blocks (rows first, then columns, as two sequential
+// passes would) and its column pair's slice of U.  B is zero-padded to an
+// even order; the odd player's pair rotates by the identity.  U sits in LDS
+// when both matrices fit (kLdsU), else in the workspace.  Writes the
+// eigenvalues, the order that sorts them descending (ties by index), and
+// Usel[k][j] = U[k][order[j]] (j < r, fp32) for the final GEMM.
+constexpr int kJacThreads = 512;
+constexpr int kJacWaves = kJacThreads / 64;
+__host__ __device__ constexpr size_t jacobi_lds(int m, bool lds_u) {
+  return (size_t)(m + (m & 1)) * (m + (m & 1)) * 8 + (lds_u ? (size_t)m * m * 8 : 0) +
+         (size_t)(m + (m & 1)) * 8 + (size_t)2 * kJacWaves * 8 + (size_t)(m + (m & 1)) * 4;
+}
+template <bool kLdsU>
+__global__ __launch_bounds__(kJacThreads) void jacobi(const double *B, int m, int sweeps,
+                                                      double *Uws, double *evals, int *order,
+                                                      int r, float *Usel) {
+  // S [mp][mp], U [m][m] (kLdsU), rotations cs [npair][2], wave sums
+  // [2][kJacWaves], pairs pr [npair][2] (at the end: the order)
+  extern __shared__ double S[];
   const int g = blockIdx.x, tid = threadIdx.x;
-  const int mp = m + (m & 1);  // players; index m (odd m) sits the round out
+  const int mp = m + (m & 1);  // players; index m (odd m) is the zero pad
   const int npair = mp / 2;
-  double *cs = S + m * m;
+  double *U = kLdsU ? S + mp * mp : Uws + (int64_t)g * m * m;
+  double *cs = S + mp * mp + (kLdsU ? m * m : 0);
   double *red = cs + 2 * npair;
-  int *pr = reinterpret_cast<int *>(red + 2 * kThreads);
+  int *pr = reinterpret_cast<int *>(red + 2 * kJacWaves);
   const double *Bg = B + (int64_t)g * m * m;
-  double *Ug = U + (int64_t)g * m * m;
-  for (int e = tid; e < m * m; e += kThreads) {
-    const int i = e / m, j = e % m;
-    S[e] = 0.5 * (Bg[e] + Bg[j * m + i]);  // exact symmetry
-    Ug[e] = i == j ? 1.0 : 0.0;
+  for (int e = tid; e < mp * mp; e += kJacThreads) {
+    const int i = e / mp, j = e % mp;
+    S[e] = i < m && j < m ? 0.5 * (Bg[i * m + j] + Bg[j * m + i]) : 0.0;  // exact symmetry
   }
+  for (int e = tid; e < m * m; e += kJacThreads) U[e] = e / m == e % m ? 1.0 : 0.0;
+  // this thread's column pair, and its first row pair / row of U
+  const int rpp = kJacThreads / npair;
+  const bool active = tid < rpp * npair;
+  const int k2 = tid % npair, r0 = tid / npair;
   __syncthreads();
   for (int sw = 0; sw < sweeps; ++sw) {
     for (int rd = 0; rd < mp - 1; ++rd) {
-      for (int k = tid; k < npair; k += kThreads) {
-        int a = (rd + k) % (mp - 1), b = k == 0 ? mp - 1 : (rd + mp - 1 - k) % (mp - 1);
+      if (tid < npair) {
+        const int a = (rd + tid) % (mp - 1), b = tid == 0 ? mp - 1 : (rd + mp - 1 - tid) % (mp - 1);
         double c = 1.0, s = 0.0;
-        if (a < m && b < m) {
-          const double app = S[a * m + a], aqq = S[b * m + b], apq = S[a * m + b];
+        if (b < m) {
+          const double app = S[a * mp + a], aqq = S[b * mp + b], apq = S[a * mp + b];
           if (fabs(apq) > 1e-300 && fabs(apq) > 1e-18 * (fabs(app) + fabs(aqq))) {
             const double tau = (aqq - app) / (2.0 * apq);
             const double t = (tau >= 0.0 ? 1.0 : -1.0) / (fabs(tau) + sqrt(1.0 + tau * tau));
             c = 1.0 / sqrt(1.0 + t * t);
             s = t * c;
           }
-        } else {
-          a = b = -1;
         }
-        cs[2 * k] = c;
-        cs[2 * k + 1] = s;
-        pr[2 * k] = a;
-        pr[2 * k + 1] = b;
+        cs[2 * tid] = c;
+        cs[2 * tid + 1] = s;
+        pr[2 * tid] = a;
+        pr[2 * tid + 1] = b;
       }
       __syncthreads();
-      for (int e = tid; e < npair * m; e += kThreads) {  // rows: B <- J^T B
-        const int k = e / m, j = e % m, a = pr[2 * k], b = pr[2 * k + 1];
-        if (a < 0) continue;
-        const double c = cs[2 * k], s = cs[2 * k + 1];
-        const double xa = S[a * m + j], xb = S[b * m + j];
-        S[a * m + j] = c * xa - s * xb;
-        S[b * m + j] = s * xa + c * xb;
-      }
-      __syncthreads();
-      for (int e = tid; e < npair * m; e += kThreads) {  // columns: B <- B J, U <- U J
-        const int k = e / m, i = e % m, a = pr[2 * k], b = pr[2 * k + 1];
-        if (a < 0) continue;
-        const double c = cs[2 * k], s = cs[2 * k + 1];
-        const double xa = S[i * m + a], xb = S[i * m + b];
-        S[i * m + a] = c * xa - s * xb;
-        S[i * m + b] = s * xa + c * xb;
-        const double ua = Ug[(int64_t)i * m + a], ub = Ug[(int64_t)i * m + b];
-        Ug[(int64_t)i * m + a] = c * ua - s * ub;
-        Ug[(int64_t)i * m + b] = s * ua + c * ub;
+      if (active) {
+        const int a2 = pr[2 * k2], b2 = pr[2 * k2 + 1];
+        const double c2 = cs[2 * k2], s2 = cs[2 * k2 + 1];
+        for (int k = r0; k < npair; k += rpp) {
+          const int a = pr[2 * k], b = pr[2 * k + 1];
+          const double c = cs[2 * k], s = cs[2 * k + 1];
+          double *Sa = S + a * mp, *Sb = S + b * mp;
+          const double xaa = Sa[a2], xab = Sa[b2], xba = Sb[a2], xbb = Sb[b2];
+          const double yaa = c * xaa - s * xba, yab = c * xab - s * xbb;  // rows
+          const double yba = s * xaa + c * xba, ybb = s * xab + c * xbb;
+          Sa[a2] = c2 * yaa - s2 * yab;  // columns
+          Sa[b2] = s2 * yaa + c2 * yab;
+          Sb[a2] = c2 * yba - s2 * ybb;
+          Sb[b2] = s2 * yba + c2 * ybb;
+        }
+        if (b2 < m) {
+          for (int i = r0; i < m; i += rpp) {
+            const double ua = U[i * m + a2], ub = U[i * m + b2];
+            U[i * m + a2] = c2 * ua - s2 * ub;
+            U[i * m + b2] = s2 * ua + c2 * ub;
+          }
+        }
       }
       __syncthreads();
     }
     // stop once the off-diagonal part is negligible against the diagonal
     double off = 0.0, dia = 0.0;
-    for (int e = tid; e < m * m; e += kThreads) {
+    for (int e = tid; e < mp * mp; e += kJacThreads) {
       const double v = S[e] * S[e];
-      if (e / m == e % m) dia += v; else off += v;
+      if (e / mp == e % mp) dia += v; else off += v;
     }
-    red[tid] = off;
-    red[kThreads + tid] = dia;
+    for (int o = 32; o > 0; o >>= 1) {
+      off += __shfl_xor(off, o);
+      dia += __shfl_xor(dia, o);
+    }
+    if ((tid & 63) == 0) {
+      red[tid >> 6] = off;
+      red[kJacWaves + (tid >> 6)] = dia;
+    }
     __syncthreads();
-    for (int h = kThreads / 2; h > 0; h >>= 1) {
-      if (tid < h) {
-        red[tid] += red[tid + h];
-        red[kThreads + tid] += red[kThreads + tid + h];
-      }
-      __syncthreads();
+    off = dia = 0.0;
+    for (int w = 0; w < kJacWaves; ++w) {
+      off += red[w];
+      dia += red[kJacWaves + w];
     }
-    const bool done = red[0] <= 1e-24 * red[kThreads];
-    __syncthreads();
-    if (done) break;
+    if (off <= 1e-24 * dia) break;  // the same decision in every thread
   }
-  if (tid == 0) {
-    for (int i = 0; i < m; ++i) order[(int64_t)g * m + i] = i;
-    for (int i = 0; i < m; ++i) {  // selection sort, descending
-      int best = i;
-      for (int j = i + 1; j < m; ++j)
-        if (S[order[(int64_t)g * m + j] * (m + 1)] > S[order[(int64_t)g * m + best] * (m + 1)])
-          best = j;
-      const int t = order[(int64_t)g * m + i];
-      order[(int64_t)g * m + i] = order[(int64_t)g * m + best];
-      order[(int64_t)g * m + best] = t;
+  // rank of each eigenvalue, descending, ties (and NaN, ranked last) by index
+  for (int i = tid; i < m; i += kJacThreads) {
+    const double li = S[i * (mp + 1)], ki = li == li ? li : -INFINITY;
+    int rank = 0;
+    for (int j = 0; j < m; ++j) {
+      const double lj = S[j * (mp + 1)], kj = lj == lj ? lj : -INFINITY;
+      rank += kj > ki || (kj == ki && j < i);
     }
-    for (int i = 0; i < m; ++i) evals[(int64_t)g * m + i] = S[i * (m + 1)];
+    pr[rank] = i;  // no thread reads the pairs any more
+    order[(int64_t)g * m + rank] = i;
+    evals[(int64_t)g * m + i] = li;
   }
-}
-
-// Usel[g][k][j] = U[g][k][order[j]], j < r (fp32 for the final GEMM).
-__global__ __launch_bounds__(kThreads) void select_vectors(const double *U, const int *order, int m,
-                                                           int r, float *Usel) {
-  const int g = blockIdx.x;
-  for (int e = threadIdx.x; e < m * r; e += kThreads) {
+  __syncthreads();
+  for (int e = tid; e < m * r; e += kJacThreads) {
     const int k = e / r, j = e % r;
-    Usel[((int64_t)g * m + k) * r + j] = (float)U[((int64_t)g * m + k) * m + order[(int64_t)g * m + j]];
+    Usel[((int64_t)g * m + k) * r + j] = (float)U[k * m + pr[j]];
   }
 }
 
@@ -628,23 +746,30 @@ static hipError_t run(const SvdParams &p, hipStream_t st) {
                      dim3(kThreads), 0, st, Q, qn);
   LLA_TRY(hipGetLastError());
 
-  const size_t chol_lds = (size_t)m * m * 8;
-  const size_t jac_lds = (size_t)m * m * 8 + (size_t)(m + 1) * 8 + (size_t)2 * kThreads * 8 +
-                         (size_t)(m + 1) * 4;
-  // both fit the 160 KB a gfx950 workgroup may use (m <= 128)
-  LLA_TRY(hipFuncSetAttribute(reinterpret_cast<const void *>(chol_inv),
-                              hipFuncAttributeMaxDynamicSharedMemorySize, (int)chol_lds));
-  LLA_TRY(hipFuncSetAttribute(reinterpret_cast<const void *>(jacobi),
-                              hipFuncAttributeMaxDynamicSharedMemorySize, (int)jac_lds));
-  const dim3 sg_grid((m + 15) / 16, (m + 15) / 16, G);
+  // U joins the matrix in LDS while both fit the 160 KB of a gfx950
+  // workgroup (m <= 100); the matrix alone fits up to m = 128
+  const bool jac_u_lds = jacobi_lds(m, true) <= kMaxLds;
+  const size_t jac_lds = jacobi_lds(m, jac_u_lds);
+  const void *jac = jac_u_lds ? reinterpret_cast<const void *>(jacobi<true>)
+                              : reinterpret_cast<const void *>(jacobi<false>);
+  LLA_TRY(hipFuncSetAttribute(jac, hipFuncAttributeMaxDynamicSharedMemorySize, (int)jac_lds));
+  const dim3 sg_grid((m + kSgT - 1) / kSgT, (m + kSgT - 1) / kSgT, G);
   // C is symmetric: its rows are read as columns (coalesced)
   const MatF32 Ct = mat(C, (int64_t)K * K, 1, K, K, K);
   auto orthonormalise = [&](float *src, float *dst) -> hipError_t {
     // CholeskyQR: dst = src R^-1 with src^T src = R^T R
-    hipLaunchKernelGGL(small_gram64, sg_grid, dim3(kThreads), 0, st, src, src, K, m, Sm);
+    hipLaunchKernelGGL(small_gram64, sg_grid, dim3(kSgThreads), 0, st, src, src, K, m, 1, Sm);
     hipError_t e2 = hipGetLastError();
     if (e2 != hipSuccess) return e2;
-    hipLaunchKernelGGL(chol_inv, dim3(G), dim3(kThreads), chol_lds, st, Sm, m, Rinv);
+    const int q = (m + kCholT - 1) / kCholT;  // m <= 128
+    if (q <= 2)
+      hipLaunchKernelGGL(chol_inv<2>, dim3(G), dim3(kCholThreads), 0, st, Sm, m, Rinv);
+    else if (q <= 4)
+      hipLaunchKernelGGL(chol_inv<4>, dim3(G), dim3(kCholThreads), 0, st, Sm, m, Rinv);
+    else if (q <= 6)
+      hipLaunchKernelGGL(chol_inv<6>, dim3(G), dim3(kCholThreads), 0, st, Sm, m, Rinv);
+    else
+      hipLaunchKernelGGL(chol_inv<8>, dim3(G), dim3(kCholThreads), 0, st, Sm, m, Rinv);
     if ((e2 = hipGetLastError()) != hipSuccess) return e2;
     return launch_gemm(mat(src, (int64_t)K * m, m, 1, K, m), mat(Rinv, (int64_t)m * m, m, 1, m, m),
                        dst, (int64_t)K * m, m, G, K, m, m, st);
@@ -661,11 +786,14 @@ static hipError_t run(const SvdParams &p, hipStream_t st) {
   }
   // Rayleigh-Ritz: B = Q^T C Q, B = U diag(lambda) U^T, W = Q U[:, leading r]
   LLA_TRY(launch_gemm(Ct, mat(Q, (int64_t)K * m, m, 1, K, m), Y, (int64_t)K * m, m, G, K, m, K, st));
-  hipLaunchKernelGGL(small_gram64, sg_grid, dim3(kThreads), 0, st, Q, Y, K, m, Sm);
+  hipLaunchKernelGGL(small_gram64, sg_grid, dim3(kSgThreads), 0, st, Q, Y, K, m, 0, Sm);
   LLA_TRY(hipGetLastError());
-  hipLaunchKernelGGL(jacobi, dim3(G), dim3(kThreads), jac_lds, st, Sm, m, p.sweeps, U, ev, order);
-  LLA_TRY(hipGetLastError());
-  hipLaunchKernelGGL(select_vectors, dim3(G), dim3(kThreads), 0, st, U, order, m, r, Usel);
+  if (jac_u_lds)
+    hipLaunchKernelGGL(jacobi<true>, dim3(G), dim3(kJacThreads), jac_lds, st, Sm, m, p.sweeps, U, ev,
+                       order, r, Usel);
+  else
+    hipLaunchKernelGGL(jacobi<false>, dim3(G), dim3(kJacThreads), jac_lds, st, Sm, m, p.sweeps, U,
+                       ev, order, r, Usel);
   LLA_TRY(hipGetLastError());
   LLA_TRY(launch_gemm(mat(Q, (int64_t)K * m, m, 1, K, m), mat(Usel, (int64_t)m * r, r, 1, m, r), W,
                       (int64_t)K * r, r, G, K, r, m, st));
