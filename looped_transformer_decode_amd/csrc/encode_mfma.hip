@@ -222,7 +222,7 @@ __device__ __forceinline__ void encode_body(const EncodeParams &p, int axis, int
       const int row = row0 + mt * 16 + 4 * g + i;
       if (row >= M) continue;
       const int b = row / p.n_new, jn = row % p.n_new;
-      const int slot = p.start[b] + jn;
+      const int64_t slot = (int64_t)p.start[b] + jn;  // start is caller data
       if (slot < 0 || slot >= p.N) continue;
       uint16_t *dst = st + ((((int64_t)b * p.D + p.layer) * p.N + slot) * p.Hs + hs) * p.R + koff;
 #pragma unroll
@@ -398,7 +398,7 @@ __global__ __launch_bounds__(64 * kSkWaves) void encode_mfma_splitk(EncodeParams
     const int r = (int)blockIdx.x * 16 + 4 * g + i;
     if (r >= M) continue;
     const int b = r / p.n_new, jn = r % p.n_new;
-    const int slot = p.start[b] + jn;
+    const int64_t slot = (int64_t)p.start[b] + jn;  // start is caller data
     if (slot < 0 || slot >= p.N) continue;
     st[((((int64_t)b * p.D + p.layer) * p.N + slot) * p.Hs + hs) * p.R + koff + rr] =
         f32_to_bf16_bits(a - bias);

@@ -294,7 +294,7 @@ __device__ __forceinline__ void body(const EncodeParams &p, int axis, int hs, in
       const int row = row0 + 32 * wave + 16 * mt + 4 * g + i;
       if (row >= M) continue;
       const int b = row / p.n_new, jn = row % p.n_new;
-      const int slot = p.start[b] + jn;
+      const int64_t slot = (int64_t)p.start[b] + jn;  // start is caller data
       if (slot < 0 || slot >= p.N) continue;
       uint16_t *dst = st + ((((int64_t)b * p.D + p.layer) * p.N + slot) * p.Hs + hs) * p.R + koff;
 #pragma unroll

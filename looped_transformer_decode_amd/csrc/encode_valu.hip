@@ -74,7 +74,7 @@ __global__ __launch_bounds__(kThreads) void encode_valu(EncodeParams p) {
     const int row = row0 + rr;
     if (row >= M) continue;
     const int b = row / p.n_new, jn = row % p.n_new;
-    const int slot = p.start[b] + jn;
+    const int64_t slot = (int64_t)p.start[b] + jn;  // start is caller data
     if (slot < 0 || slot >= p.N) continue;
     const int64_t off = ((((int64_t)b * p.D + p.layer) * p.N + slot) * p.Hs + hs) * p.R +
                         (axis ? p.rk : 0) + k;

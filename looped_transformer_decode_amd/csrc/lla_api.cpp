@@ -318,7 +318,7 @@ lla::KvParams kv_params(const lla_kv_cache_t *c, int32_t layer, int32_t cache_lo
 }
 
 // ---- SVD codec initialisation -----------------------------------------------
-constexpr int32_t kSvdMaxBlock = 128;   // iterated block m (Jacobi / Cholesky in LDS)
+constexpr int32_t kSvdMaxBlock = 128;   // iterated block m (Jacobi in LDS, Cholesky in registers)
 constexpr int32_t kSvdOversample = 16;
 constexpr int32_t kSvdDefaultIters = 16;
 constexpr int32_t kSvdSweeps = 10;
