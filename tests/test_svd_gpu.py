@@ -144,6 +144,35 @@ def test_edge_cases(device, n, K, r):
     assert np.abs(sig[0][:k] - osig[:k]).max() <= 1e-4 * osig[0]
 
 
+@pytest.mark.parametrize("r", [101, 79], ids=["block_117_odd", "block_95_odd"])
+def test_large_odd_block(device, r):
+    """Iterated blocks of odd order beyond what the small cases reach:
+    m = r + 16 = 117 (the eigenvector matrix no longer fits LDS beside the
+    Rayleigh-Ritz matrix, 8 x 8 registers per thread in the Cholesky step)
+    and m = 95 (6 x 6).  The leading r singular values are distinct but close
+    and the rest well below, so only the subspace is unique: compared are mu,
+    sigma, orthonormality and the codec error against the optimum."""
+    G, T, width, n = 2, 2, 80, 600
+    K = T * width
+    sv = np.concatenate([np.linspace(50.0, 20.0, r), np.full(K - r, 0.5)])
+    x = np.stack([spectrum_rows(900 + g + r, n, K, sv) for g in range(G)], axis=1)
+    x = gen.as_storage(x, "f32")[1]
+    say(f"[svd] large odd block G={G} K={K} r={r} m={r + 16} n={n}")
+    mu, wd, wu, sig = run_init(x, "f32", G, T, width, r, device)
+    for g in range(G):
+        omu, oW, oUp, osig = O.svd_init(x[:, g], T, width, r)
+        assert np.abs(mu[g] - omu).max() <= 1e-5 * (np.abs(omu).max() + 1e-3)
+        assert np.abs(wd[g].T @ wd[g] - np.eye(r)).max() < 1e-3
+        for t in range(T):
+            assert np.array_equal(wu[t, g], wd[g][t * width:(t + 1) * width])
+        assert np.abs(sig[g] - osig).max() <= 1e-4 * osig[0]
+        e_gpu = O.codec_error(x[:, g], mu[g], wd[g],
+                              [wd[g][t * width:(t + 1) * width] for t in range(T)])
+        e_opt = O.codec_error(x[:, g], omu, oW, oUp)
+        say(f"    codec {g}: error {e_gpu:.4e} (optimum {e_opt:.4e})")
+        assert e_gpu <= e_opt * (1 + 1e-4) + 1e-7
+
+
 def test_deterministic(device):
     G, T, width, r, n = 2, 4, 16, 8, 256
     K = T * width
