@@ -144,6 +144,109 @@ __global__ __launch_bounds__(kThreads) void gemm(LA A, LB B, float *C, int64_t c
   }
 }
 
+// C[g][i][j] = sum_k X[g][k][i] Y[g][k][j] for a narrow right-hand side
+// (Nn <= 32 NB columns), both operands k-major with rows of 16-byte vectors:
+// the subspace iteration's C Q (C symmetric, so its rows serve as X's) and
+// the Rayleigh-Ritz product.  A block takes 128 rows and every column; wave
+// w multiplies rows 32 w .. 32 w + 31 against the NB column tiles, so each
+// A fragment read from LDS feeds NB independent v_mfma_f32_32x32x2_f32
+// chains.  Chunks of 32 k are staged in LDS as 16-byte vectors, the next
+// chunk loaded into registers while the current one is multiplied.
+typedef float f32x4_v __attribute__((ext_vector_type(4)));
+constexpr int kTnRows = 128;
+constexpr int kTnK = 32;
+template <int NB>
+struct TnCfg {
+  static constexpr int NC = 32 * NB;                       // columns of the block
+  // LDS row pitches (floats), 32 banks apart modulo 64: the two k rows one
+  // operand read touches (lanes 0-31, 32-63) fall in disjoint banks
+  static constexpr int AP = kTnRows + 32, BP = NC + (NC % 64 == 32 ? 0 : 32);
+  static constexpr int AV = kTnK * kTnRows / 4 / kThreads; // A vectors per thread and chunk
+  static constexpr int BV = (kTnK * NC / 4 + kThreads - 1) / kThreads;
+  static constexpr int LDS = 2 * kTnK * (AP + BP) * 4;
+  static_assert(AV * kThreads * 4 == kTnK * kTnRows, "A load split");
+};
+template <int NB>
+__global__ __launch_bounds__(kThreads) void gemm_tn(const float *X, int64_t x_sg, int ldx,
+                                                    const float *Y, int64_t y_sg, int ldy,
+                                                    float *C, int64_t c_sg, int ldc, int M,
+                                                    int Nn, int Kd) {
+  using T = TnCfg<NB>;
+  extern __shared__ __align__(16) float tn[];
+  float *As = tn;                          // [2][kTnK][AP]
+  float *Bs = tn + 2 * kTnK * T::AP;       // [2][kTnK][BP]
+  const int g = blockIdx.y, i0 = blockIdx.x * kTnRows;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const float *Xg = X + g * x_sg, *Yg = Y + g * y_sg;
+  f32x4_v ra[T::AV], rb[T::BV];
+  auto fetch = [&](int k0) {
+#pragma unroll
+    for (int q = 0; q < T::AV; ++q) {
+      const int e = tid + kThreads * q, kk = e / (kTnRows / 4), c4 = 4 * (e % (kTnRows / 4));
+      const bool ok = k0 + kk < Kd && i0 + c4 < M;
+      ra[q] = ok ? *reinterpret_cast<const f32x4_v *>(Xg + (int64_t)(k0 + kk) * ldx + i0 + c4)
+                 : f32x4_v{0.f, 0.f, 0.f, 0.f};
+    }
+#pragma unroll
+    for (int q = 0; q < T::BV; ++q) {
+      const int e = tid + kThreads * q, kk = e / (T::NC / 4), c4 = 4 * (e % (T::NC / 4));
+      const bool ok = e < kTnK * T::NC / 4 && k0 + kk < Kd && c4 < Nn;
+      rb[q] = ok ? *reinterpret_cast<const f32x4_v *>(Yg + (int64_t)(k0 + kk) * ldy + c4)
+                 : f32x4_v{0.f, 0.f, 0.f, 0.f};
+    }
+  };
+  auto stage = [&](int buf) {
+#pragma unroll
+    for (int q = 0; q < T::AV; ++q) {
+      const int e = tid + kThreads * q, kk = e / (kTnRows / 4), c4 = 4 * (e % (kTnRows / 4));
+      *reinterpret_cast<f32x4_v *>(As + (buf * kTnK + kk) * T::AP + c4) = ra[q];
+    }
+#pragma unroll
+    for (int q = 0; q < T::BV; ++q) {
+      const int e = tid + kThreads * q, kk = e / (T::NC / 4), c4 = 4 * (e % (T::NC / 4));
+      if (e < kTnK * T::NC / 4)
+        *reinterpret_cast<f32x4_v *>(Bs + (buf * kTnK + kk) * T::BP + c4) = rb[q];
+    }
+  };
+  f32x16_t acc[NB];
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb) acc[nb] = f32x16_t{};
+  fetch(0);
+  stage(0);
+  __syncthreads();
+  int buf = 0;
+  for (int k0 = 0; k0 < Kd; k0 += kTnK) {
+    const bool more = k0 + kTnK < Kd;
+    if (more) fetch(k0 + kTnK);
+    const float *Ab = As + buf * kTnK * T::AP + 32 * wave + (lane & 31);
+    const float *Bb = Bs + buf * kTnK * T::BP + (lane & 31);
+#pragma unroll
+    for (int kk = 0; kk < kTnK; kk += 2) {
+      // A: row 32 wave + lane % 32, k = kk + lane / 32;  B: column 32 nb + lane % 32
+      const int kr = kk + (lane >> 5);
+      const float a = Ab[kr * T::AP];
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb)
+        acc[nb] = __builtin_amdgcn_mfma_f32_32x32x2f32(a, Bb[kr * T::BP + 32 * nb], acc[nb], 0, 0,
+                                                       0);
+    }
+    if (more) stage(buf ^ 1);
+    __syncthreads();
+    buf ^= 1;
+  }
+  // accumulator r: row 8 (r / 4) + 4 (lane / 32) + r % 4, column lane % 32
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb) {
+    const int j = 32 * nb + (lane & 31);
+    if (j >= Nn) continue;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int i = i0 + 32 * wave + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+      if (i < M) C[g * c_sg + (int64_t)i * ldc + j] = acc[nb][r];
+    }
+  }
+}
+
 // Gram matrix of the centred calibration rows, C[g] = Xc^T Xc with
 // Xc[n][f] = x[n][g][f] - mu[g][f], on the fp32 matrix cores.  C is
 // symmetric: only the 128 x 128 tiles (ti, tj) with ti <= tj are computed,
@@ -699,6 +802,29 @@ hipError_t launch_gemm(const LA &A, const LB &B, float *C, int64_t c_sg, int ldc
   return hipGetLastError();
 }
 
+template <int NB>
+hipError_t launch_gemm_tn_nb(const float *X, int64_t x_sg, int ldx, const float *Y, int64_t y_sg,
+                             int ldy, float *C, int64_t c_sg, int ldc, int G, int M, int Nn,
+                             int Kd, hipStream_t st) {
+  const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(gemm_tn<NB>),
+                                           hipFuncAttributeMaxDynamicSharedMemorySize,
+                                           TnCfg<NB>::LDS);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(gemm_tn<NB>, dim3((M + kTnRows - 1) / kTnRows, G), dim3(kThreads),
+                     TnCfg<NB>::LDS, st, X, x_sg, ldx, Y, y_sg, ldy, C, c_sg, ldc, M, Nn, Kd);
+  return hipGetLastError();
+}
+// Needs M, Nn, ldx, ldy multiples of 4, 16-byte aligned X and Y, Nn <= 128.
+hipError_t launch_gemm_tn(const float *X, int64_t x_sg, int ldx, const float *Y, int64_t y_sg,
+                          int ldy, float *C, int64_t c_sg, int ldc, int G, int M, int Nn, int Kd,
+                          hipStream_t st) {
+  const int nb = (Nn + 31) / 32;
+  if (nb <= 1) return launch_gemm_tn_nb<1>(X, x_sg, ldx, Y, y_sg, ldy, C, c_sg, ldc, G, M, Nn, Kd, st);
+  if (nb == 2) return launch_gemm_tn_nb<2>(X, x_sg, ldx, Y, y_sg, ldy, C, c_sg, ldc, G, M, Nn, Kd, st);
+  if (nb == 3) return launch_gemm_tn_nb<3>(X, x_sg, ldx, Y, y_sg, ldy, C, c_sg, ldc, G, M, Nn, Kd, st);
+  return launch_gemm_tn_nb<4>(X, x_sg, ldx, Y, y_sg, ldy, C, c_sg, ldc, G, M, Nn, Kd, st);
+}
+
 MatF32 mat(const float *p, int64_t sg, int64_t s0, int64_t s1, int n0, int n1) {
   return MatF32{p, sg, s0, s1, n0, n1};
 }
@@ -756,6 +882,16 @@ static hipError_t run(const SvdParams &p, hipStream_t st) {
   const dim3 sg_grid((m + kSgT - 1) / kSgT, (m + kSgT - 1) / kSgT, G);
   // C is symmetric: its rows are read as columns (coalesced)
   const MatF32 Ct = mat(C, (int64_t)K * K, 1, K, K, K);
+  // dst = C src (C symmetric, so its rows serve as the k-major left operand)
+  const bool tn = K % 4 == 0 && m % 4 == 0 && m <= 128 && ((uintptr_t)C & 15) == 0 &&
+                  ((uintptr_t)Q & 15) == 0 && ((uintptr_t)Y & 15) == 0;
+  auto c_times = [&](const float *src, float *dst) -> hipError_t {
+    if (!tn)
+      return launch_gemm(Ct, mat(src, (int64_t)K * m, m, 1, K, m), dst, (int64_t)K * m, m, G, K,
+                         m, K, st);
+    return launch_gemm_tn(C, (int64_t)K * K, K, src, (int64_t)K * m, m, dst, (int64_t)K * m, m, G,
+                          K, m, K, st);
+  };
   auto orthonormalise = [&](float *src, float *dst) -> hipError_t {
     // CholeskyQR: dst = src R^-1 with src^T src = R^T R
     hipLaunchKernelGGL(small_gram64, sg_grid, dim3(kSgThreads), 0, st, src, src, K, m, 1, Sm);
@@ -777,7 +913,7 @@ static hipError_t run(const SvdParams &p, hipStream_t st) {
   LLA_TRY(orthonormalise(Q, Y));
   LLA_TRY(orthonormalise(Y, Q));
   for (int it = 0; it < p.iters; ++it) {
-    LLA_TRY(launch_gemm(Ct, mat(Q, (int64_t)K * m, m, 1, K, m), Y, (int64_t)K * m, m, G, K, m, K, st));
+    LLA_TRY(c_times(Q, Y));
     LLA_TRY(orthonormalise(Y, Q));   // CholeskyQR2: twice
     LLA_TRY(orthonormalise(Q, Y));
     float *t = Q;  // the orthonormal block is now in Y
@@ -785,7 +921,7 @@ static hipError_t run(const SvdParams &p, hipStream_t st) {
     Y = t;
   }
   // Rayleigh-Ritz: B = Q^T C Q, B = U diag(lambda) U^T, W = Q U[:, leading r]
-  LLA_TRY(launch_gemm(Ct, mat(Q, (int64_t)K * m, m, 1, K, m), Y, (int64_t)K * m, m, G, K, m, K, st));
+  LLA_TRY(c_times(Q, Y));
   hipLaunchKernelGGL(small_gram64, sg_grid, dim3(kSgThreads), 0, st, Q, Y, K, m, 0, Sm);
   LLA_TRY(hipGetLastError());
   if (jac_u_lds)
