@@ -78,6 +78,9 @@ def parse():
     ap.add_argument("--copy-calibration", type=float, default=0.0, metavar="GB",
                     help="instead of the benchmark, copy a buffer of this size a few times "
                          "(reference for HBM byte counters)")
+    ap.add_argument("--write-ceiling", type=float, default=0.0, metavar="GB",
+                    help="instead of the decode step: time a plain streaming write and a plain "
+                         "copy of a buffer of this size (the ceilings of the write-bound kernels)")
     ap.add_argument("--read-ceiling", type=float, default=0.0, metavar="GB",
                     help="instead of the benchmark, time a plain streaming-read kernel over a "
                          "buffer of this size (the practical HBM read ceiling)")
@@ -623,6 +626,67 @@ def run_read_ceiling(args, torch):
           flush=True)
 
 
+def run_write_ceiling(args, torch):
+    """A plain streaming write, and a plain copy, of a buffer larger than the
+    caches: workgroups of 256 threads taking 32 KB chunks in turn (those in
+    flight neighbours in memory), eight 16-byte stores per thread in flight.
+    The copy's bytes count its reads and its writes."""
+    from synth.device import write_stream
+    dev = torch.device("cuda:0")
+    n = int(args.write_ceiling * 1e9) // (16 * 2048) * (16 * 2048)
+    dst = torch.empty(n // 4, dtype=torch.int32, device=dev)
+    src = torch.zeros(n // 4, dtype=torch.int32, device=dev)
+    out = {}
+    for mode, s_arg, nbytes in (("write", None, n), ("copy", src, 2 * n)):
+        results = {}
+        for blocks in (2048, 8192, 32768):
+            for _ in range(3):
+                write_stream(dst, blocks, s_arg)
+            torch.cuda.synchronize()
+            ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+            reps = max(args.steps, 5)
+            ev[0].record()
+            for _ in range(reps):
+                write_stream(dst, blocks, s_arg)
+            ev[1].record()
+            torch.cuda.synchronize()
+            ms = ev[0].elapsed_time(ev[1]) / reps
+            results[blocks] = (ms, nbytes / (ms / 1e3) / 1e9)
+            log(f"[bench] {mode} ceiling: {blocks} workgroups, {nbytes / 1e9:.2f} GB in "
+                f"{ms * 1e3:.1f} us: {results[blocks][1]:.1f} GB/s")
+        best = max(results, key=lambda b: results[b][1])
+        # torch's own fill and copy kernels of the same buffers, beside it
+        lib_fn = (lambda: dst.fill_(7)) if s_arg is None else (lambda: dst.copy_(src))
+        for _ in range(3):
+            lib_fn()
+        torch.cuda.synchronize()
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+        reps = max(args.steps, 5)
+        ev[0].record()
+        for _ in range(reps):
+            lib_fn()
+        ev[1].record()
+        torch.cuda.synchronize()
+        lib_ms = ev[0].elapsed_time(ev[1]) / reps
+        lib_gbs = nbytes / (lib_ms / 1e3) / 1e9
+        log(f"[bench] {mode} ceiling: torch {'fill_' if s_arg is None else 'copy_'} "
+            f"{lib_ms * 1e3:.1f} us: {lib_gbs:.1f} GB/s")
+        top = max(results[best][1], lib_gbs)
+        out[mode] = {"GBps": round(top, 1), "frac": round(top / HBM_PEAK_GBS, 4),
+                     "kernel": "write_stream" if results[best][1] >= lib_gbs else
+                               ("torch fill_" if s_arg is None else "torch copy_"),
+                     "write_stream": {"workgroups": best, "GBps": round(results[best][1], 1)},
+                     "torch": {"launch_us": round(lib_ms * 1e3, 2), "GBps": round(lib_gbs, 1)},
+                     "sweep": {str(b): {"launch_us": round(v[0] * 1e3, 2), "GBps": round(v[1], 1)}
+                               for b, v in results.items()}}
+    print(json.dumps({"metric": "streaming-write GB/s (best plain write: write_stream of "
+                                "synth/fill.hip or torch fill_; the plain copy beside it, reads "
+                                "plus writes), context for the write-bound kernels",
+                      "value": out["write"]["GBps"], "unit": "GB/s", "peak": HBM_PEAK_GBS,
+                      "frac": out["write"]["frac"], "bytes": n, "write": out["write"],
+                      "copy": out["copy"]}), flush=True)
+
+
 def run_mfma_ceiling(args, torch):
     """Register-only v_mfma_f32_32x32x16_bf16 chains (four independent
     accumulators per wave) at one to four waves per SIMD: the bf16
@@ -714,6 +778,9 @@ def main():
 
     if args.read_ceiling > 0:
         run_read_ceiling(args, torch)
+        return
+    if args.write_ceiling > 0:
+        run_write_ceiling(args, torch)
         return
     if args.mfma_ceiling:
         run_mfma_ceiling(args, torch)

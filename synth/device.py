@@ -23,6 +23,9 @@ def _load():
         L.synth_read_stream.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32,
                                         ctypes.c_void_p, ctypes.c_void_p]
         L.synth_read_stream.restype = ctypes.c_int
+        L.synth_write_stream.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64,
+                                         ctypes.c_int32, ctypes.c_void_p]
+        L.synth_write_stream.restype = ctypes.c_int
         L.synth_mfma_spin.argtypes = [ctypes.c_int32, ctypes.c_int32, ctypes.c_void_p,
                                       ctypes.c_void_p]
         L.synth_mfma_spin.restype = ctypes.c_int
@@ -55,6 +58,20 @@ def read_stream(src: torch.Tensor, sink: torch.Tensor, blocks: int) -> None:
                                     torch.cuda.current_stream(src.device).cuda_stream)
     if err != 0:
         raise RuntimeError(f"synth_read_stream failed: hipError {err}")
+
+
+def write_stream(dst: torch.Tensor, blocks: int, src: torch.Tensor = None) -> None:
+    """Launch the streaming-write kernel over all of dst (bytes a multiple of
+    16) with `blocks` workgroups: a fixed pattern, or a copy of src (the same
+    size) when given."""
+    nbytes = dst.numel() * dst.element_size()
+    if src is not None and src.numel() * src.element_size() != nbytes:
+        raise ValueError("src and dst sizes differ")
+    err = _load().synth_write_stream(None if src is None else src.data_ptr(), dst.data_ptr(),
+                                     nbytes, blocks,
+                                     torch.cuda.current_stream(dst.device).cuda_stream)
+    if err != 0:
+        raise RuntimeError(f"synth_write_stream failed: hipError {err}")
 
 
 def mfma_spin(blocks: int, iters: int, sink: torch.Tensor) -> None:

@@ -84,6 +84,31 @@ __global__ __launch_bounds__(256) void read_stream(const u32x4_v *src, int64_t n
     sink[(int64_t)blockIdx.x * 256 + threadIdx.x] = u32x4_v{a0, a1, a2, a3};
 }
 
+// Streaming write (src null) or copy of n16 16-byte words in chunks of
+// 2048 words (one unrolled round of a workgroup): workgroup g takes chunks
+// g, g + grid, g + 2 grid, ..., so that the chunks in flight at any time are
+// neighbours in memory; eight 16-byte stores per thread in flight (loads of
+// a copy nontemporal).  The write and read-plus-write ceilings the
+// write-bound kernels are compared with.
+__global__ __launch_bounds__(256) void write_stream(const u32x4_v *src, u32x4_v *dst,
+                                                     int64_t n16) {
+  const u32x4_v pat = {0x3F803F80u, 0x3F803F80u, (uint32_t)blockIdx.x, threadIdx.x};
+  const int64_t chunk = 256 * kReadUnroll;
+  for (int64_t c0 = (int64_t)blockIdx.x * chunk; c0 < n16; c0 += (int64_t)gridDim.x * chunk) {
+    const int64_t i = c0 + threadIdx.x;
+    if (c0 + chunk <= n16) {
+      u32x4_v v[kReadUnroll];
+#pragma unroll
+      for (int u = 0; u < kReadUnroll; ++u)
+        v[u] = src ? __builtin_nontemporal_load(src + i + u * 256) : pat;
+#pragma unroll
+      for (int u = 0; u < kReadUnroll; ++u) dst[i + u * 256] = v[u];
+    } else {
+      for (int64_t k = i; k < n16; k += 256) dst[k] = src ? src[k] : pat;
+    }
+  }
+}
+
 // Matrix-core ceiling: every wave runs `iters` rounds of four independent
 // v_mfma_f32_32x32x16_bf16 accumulations on operands held in registers (no
 // memory traffic), then writes its sum only if it equals a fixed pattern.
@@ -186,6 +211,17 @@ extern "C" int synth_read_stream(const void *src, int64_t bytes, int32_t blocks,
   const int64_t per = ((n16 + blocks - 1) / blocks + round - 1) / round * round;
   hipLaunchKernelGGL(read_stream, dim3((unsigned)blocks), dim3(256), 0, stream,
                      (const u32x4_v *)src, n16, per, (u32x4_v *)sink);
+  return (int)hipGetLastError();
+}
+
+// Writes `bytes` (a multiple of 16) to dst, copied from src or, with src
+// null, a fixed pattern, with `blocks` workgroups of 256 threads.  Returns a
+// hipError_t value.
+extern "C" int synth_write_stream(const void *src, void *dst, int64_t bytes, int32_t blocks,
+                                  hipStream_t stream) {
+  if (!dst || bytes <= 0 || bytes % 16 != 0 || blocks <= 0) return (int)hipErrorInvalidValue;
+  hipLaunchKernelGGL(write_stream, dim3((unsigned)blocks), dim3(256), 0, stream,
+                     (const u32x4_v *)src, (u32x4_v *)dst, bytes / 16);
   return (int)hipGetLastError();
 }
 
