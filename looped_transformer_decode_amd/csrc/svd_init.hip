@@ -247,25 +247,46 @@ __global__ __launch_bounds__(kThreads) void gemm_tn(const float *X, int64_t x_sg
   }
 }
 
-// Gram matrix of the centred calibration rows, C[g] = Xc^T Xc with
-// Xc[n][f] = x[n][g][f] - mu[g][f], on the fp32 matrix cores.  C is
-// symmetric: only the 128 x 128 tiles (ti, tj) with ti <= tj are computed,
-// and those off the diagonal are also written transposed (through LDS, so
-// that both stores are coalesced).  Four waves, each a 64 x 64 quarter of
-// the tile as 2 x 2 blocks of v_mfma_f32_32x32x2_f32.  Samples are staged in
-// LDS in chunks of 32, centred and in fp32, feature-contiguous; the next
-// chunk is loaded into registers while the current one is multiplied.
+// Gram matrix tiles: 128 x 128 outputs, samples staged in chunks of 32.
 constexpr int kGT = 128;  // output tile
 constexpr int kGN = 32;   // samples per chunk
 typedef uint32_t u32x4_v __attribute__((ext_vector_type(4)));
-constexpr int kGP = kGT + 4;
-constexpr int kGramLds = 2 * 2 * kGN * kGP * 4;  // [buf][operand][n][feature] fp32
-static_assert(kGT * (kGT + 1) * 4 <= kGramLds, "the transposed store reuses the staging LDS");
+
+// Gram matrix of the centred calibration rows, C[g] = Xc^T Xc with
+// Xc[n][f] = x[n][g][f] - mu[g][f], on the bf16 matrix cores to fp32
+// accuracy.  Every centred value y = x - mu (fp32) is split exactly into
+// three bf16 parts, y = h + m + l (8 significant bits each: h = bf16(y),
+// m = bf16(y - h), l = bf16(y - h - m)), and a product y_a y_b is formed from
+// the six partial products whose size reaches 2^-24 |y_a y_b|: hh, hm, mh,
+// mm, hl, lh (the dropped ml, lm, ll are below it, as an fp32 product's own
+// rounding is); products are exact and sums fp32.  Six
+// v_mfma_f32_32x32x16_bf16 take the place of eight v_mfma_f32_32x32x2_f32 per
+// 32 x 32 block and 16 samples, at 32 against 64 cycles each.
+// C is symmetric: only the 128 x 128 tiles (ti, tj) with ti <= tj are
+// computed, those off the diagonal also written transposed; four waves, each
+// a 64 x 64 quarter of the tile as 2 x 2 blocks of 32 x 32.  The
+// operands want 8 consecutive samples of one feature per lane, so chunks of
+// 32 samples are staged feature-major, one plane per part, in one buffer
+// (two workgroups per CU; the next chunk waits in registers); a thread loads
+// the 8 features of its 16-byte vector for two adjacent samples and writes
+// each feature's pair as one 4-byte word.  Feature f of the tile sits in LDS
+// row (f % 8) 16 + f / 8, so that the rows one such write touches across a
+// wave fall in distinct banks; the tile goes out through LDS, where the
+// permutation is undone and both stores are coalesced.
+constexpr int kG3P = kGN + 8;                             // bf16 per LDS row (80 bytes)
+constexpr int kG3Plane = kGT * kG3P;                      // bf16 per plane
+// one staging buffer [operand][part][row][sample] (two workgroups per CU),
+// or the output tile [kGT][kGT + 1] fp32, whichever is larger
+constexpr int kGram3Lds = 2 * 3 * kG3Plane * 2 > kGT * (kGT + 1) * 4 ? 2 * 3 * kG3Plane * 2
+                                                                     : kGT * (kGT + 1) * 4;
+__device__ __forceinline__ int g3_row(int f) { return (f & 7) * (kGT / 8) + (f >> 3); }
+__device__ __forceinline__ int g3_feature(int r) { return (r % (kGT / 8)) * 8 + r / (kGT / 8); }
+typedef __attribute__((__vector_size__(8 * sizeof(short)))) short g3_bf16x8_t;
 
 template <typename E>
-__global__ __launch_bounds__(kThreads) void gram(const E *x, const float *mu, int G, int N, int K,
-                                                  float *C) {
-  extern __shared__ __align__(16) float gs[];
+__global__ __launch_bounds__(kThreads) void gram3(const E *x, const float *mu, int G, int N, int K,
+                                                   float *C) {
+  extern __shared__ __align__(16) uint16_t g3[];
   const int T = (K + kGT - 1) / kGT;
   int t = blockIdx.x, ti = 0;
   while (t >= T - ti) {  // upper-triangle tile (ti, tj), ti <= tj
@@ -277,11 +298,8 @@ __global__ __launch_bounds__(kThreads) void gram(const E *x, const float *mu, in
   const bool diag = ti == tj;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wi = wave >> 1, wj = wave & 1;
-  // This thread loads features f8 .. f8 + 7 of the tile (one 16-byte vector
-  // of bf16, or two of fp32) of chunk rows nr and nr + 16.  Loads are never
-  // conditional (indices are clamped, values past N or K zeroed afterwards),
-  // so that they all go out before the first is waited for.
-  const int f8 = (tid % (kGT / 8)) * 8, nr = tid / (kGT / 8);
+  // features f8 .. f8 + 7 of the tile, samples 2 np and 2 np + 1 of a chunk
+  const int f8 = (tid % (kGT / 8)) * 8, np = tid / (kGT / 8);
   const int fa = i0 + f8, fb = j0 + f8;
   float mua[8], mub[8];
 #pragma unroll
@@ -291,21 +309,19 @@ __global__ __launch_bounds__(kThreads) void gram(const E *x, const float *mu, in
   }
   const bool fa_ok = fa < K, fb_ok = fb < K;  // K % 8 == 0: whole vectors in or out
   const int fa_c = fa_ok ? fa : 0, fb_c = fb_ok ? fb : 0;
-  // raw 16-byte vectors of the two rows (bf16: one per row, fp32: two),
-  // converted and centred only when staged, after the chunk's products
   constexpr int NV = sizeof(E) == 2 ? 1 : 2;
   u32x4_v ra[2][NV], rb[2][NV];
   auto fetch = [&](int n0) {
 #pragma unroll
     for (int q = 0; q < 2; ++q) {
-      const int n = min(n0 + nr + 16 * q, N - 1);
+      const int n = min(n0 + 2 * np + q, N - 1);
       const int64_t row = ((int64_t)n * G + g) * K;
       const u32x4_v *pa = reinterpret_cast<const u32x4_v *>(x + row + fa_c);
       const u32x4_v *pb = reinterpret_cast<const u32x4_v *>(x + row + (diag ? fa_c : fb_c));
 #pragma unroll
       for (int v = 0; v < NV; ++v) {
         ra[q][v] = pa[v];
-        rb[q][v] = pb[v];  // on the diagonal a second copy of the same features (unused)
+        rb[q][v] = pb[v];
       }
     }
   };
@@ -321,28 +337,37 @@ __global__ __launch_bounds__(kThreads) void gram(const E *x, const float *mu, in
       for (int e = 0; e < 8; ++e) dst[e] = __uint_as_float(raw[e / 4][e % 4]);
     }
   };
-  auto stage = [&](int buf, int n0) {
-    float *sa = gs + (buf * 2) * kGN * kGP, *sb = sa + kGN * kGP;
+  // the two samples' centred values of 8 features -> three planes of pairs
+  auto put = [&](uint16_t *plane0, const float (&y0)[8], const float (&y1)[8]) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const float h0 = bf16_bits_to_f32(f32_to_bf16_bits(y0[e]));
+      const float h1 = bf16_bits_to_f32(f32_to_bf16_bits(y1[e]));
+      const float r0 = y0[e] - h0, r1 = y1[e] - h1;
+      const float m0 = bf16_bits_to_f32(f32_to_bf16_bits(r0));
+      const float m1 = bf16_bits_to_f32(f32_to_bf16_bits(r1));
+      uint32_t *w = reinterpret_cast<uint32_t *>(plane0 + g3_row(f8 + e) * kG3P + 2 * np);
+      w[0] = pack_bf16x2(h0, h1);
+      w[kG3Plane / 2] = pack_bf16x2(m0, m1);
+      w[kG3Plane] = pack_bf16x2(r0 - m0, r1 - m1);
+    }
+  };
+  auto stage = [&](int n0) {
+    uint16_t *pa = g3, *pb = pa + 3 * kG3Plane;
+    float va[2][8], vb[2][8];
 #pragma unroll
     for (int q = 0; q < 2; ++q) {
-      const bool nok = n0 + nr + 16 * q < N;
-      float va[8], vb[8];
-      unpack(ra[q], va);
-      unpack(rb[q], vb);
+      const bool nok = n0 + 2 * np + q < N;
+      unpack(ra[q], va[q]);
+      unpack(rb[q], vb[q]);
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
-        va[e] = nok && fa_ok ? va[e] - mua[e] : 0.f;
-        vb[e] = nok && fb_ok ? vb[e] - mub[e] : 0.f;
-      }
-      float *da = sa + (nr + 16 * q) * kGP + f8;
-      *reinterpret_cast<float4 *>(da) = make_float4(va[0], va[1], va[2], va[3]);
-      *reinterpret_cast<float4 *>(da + 4) = make_float4(va[4], va[5], va[6], va[7]);
-      if (!diag) {
-        float *db = sb + (nr + 16 * q) * kGP + f8;
-        *reinterpret_cast<float4 *>(db) = make_float4(vb[0], vb[1], vb[2], vb[3]);
-        *reinterpret_cast<float4 *>(db + 4) = make_float4(vb[4], vb[5], vb[6], vb[7]);
+        va[q][e] = nok && fa_ok ? va[q][e] - mua[e] : 0.f;
+        vb[q][e] = nok && fb_ok ? vb[q][e] - mub[e] : 0.f;
       }
     }
+    put(pa, va[0], va[1]);
+    if (!diag) put(pb, vb[0], vb[1]);
   };
   f32x16_t acc[2][2];
 #pragma unroll
@@ -350,39 +375,53 @@ __global__ __launch_bounds__(kThreads) void gram(const E *x, const float *mu, in
 #pragma unroll
     for (int b = 0; b < 2; ++b) acc[a][b] = f32x16_t{};
   fetch(0);
-  stage(0, 0);
+  stage(0);
   __syncthreads();
-  int buf = 0;
   for (int n0 = 0; n0 < N; n0 += kGN) {
     const bool more = n0 + kGN < N;
     if (more) fetch(n0 + kGN);
     __builtin_amdgcn_sched_barrier(0);  // the loads go out before the products
-    const float *sa = gs + (buf * 2) * kGN * kGP;
-    const float *sb = diag ? sa : sa + kGN * kGP;
+    const uint16_t *pa = g3;
+    const uint16_t *pb = diag ? pa : pa + 3 * kG3Plane;
 #pragma unroll
-    for (int kk = 0; kk < kGN; kk += 2) {
-      const int r = (kk + (lane >> 5)) * kGP + (lane & 31);
-      float av[2], bv[2];
+    for (int ks = 0; ks < kGN / 16; ++ks) {
+      // lane: row (feature slot) lane % 32 of its block, samples 16 ks + 8 (lane / 32) ..
+      const int off = (lane & 31) * kG3P + 16 * ks + 8 * (lane >> 5);
+      g3_bf16x8_t A[2][3], B[2][3];
 #pragma unroll
-      for (int a = 0; a < 2; ++a) av[a] = sa[r + wi * 64 + 32 * a];
+      for (int pt = 0; pt < 3; ++pt) {
 #pragma unroll
-      for (int b = 0; b < 2; ++b) bv[b] = sb[r + wj * 64 + 32 * b];
+        for (int a = 0; a < 2; ++a)
+          A[a][pt] = *reinterpret_cast<const g3_bf16x8_t *>(
+              pa + pt * kG3Plane + (wi * 64 + 32 * a) * kG3P + off);
+#pragma unroll
+        for (int b = 0; b < 2; ++b)
+          B[b][pt] = *reinterpret_cast<const g3_bf16x8_t *>(
+              pb + pt * kG3Plane + (wj * 64 + 32 * b) * kG3P + off);
+      }
 #pragma unroll
       for (int a = 0; a < 2; ++a)
 #pragma unroll
-        for (int b = 0; b < 2; ++b)
-          acc[a][b] = __builtin_amdgcn_mfma_f32_32x32x2f32(av[a], bv[b], acc[a][b], 0, 0, 0);
+        for (int b = 0; b < 2; ++b) {
+          f32x16_t c = acc[a][b];
+          c = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A[a][0], B[b][2], c, 0, 0, 0);  // h l
+          c = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A[a][2], B[b][0], c, 0, 0, 0);  // l h
+          c = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A[a][1], B[b][1], c, 0, 0, 0);  // m m
+          c = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A[a][0], B[b][1], c, 0, 0, 0);  // h m
+          c = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A[a][1], B[b][0], c, 0, 0, 0);  // m h
+          c = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A[a][0], B[b][0], c, 0, 0, 0);  // h h
+          acc[a][b] = c;
+        }
     }
     __builtin_amdgcn_sched_barrier(0);  // and are waited for only after them
-    if (more) stage(buf ^ 1, n0 + kGN);
+    __syncthreads();                    // every wave is done with this chunk
+    if (more) stage(n0 + kGN);
     __syncthreads();
-    buf ^= 1;
   }
-  // tile rows i (features of the first operand), columns j: accumulator r of
-  // block (a, b) is row 64 wi + 32 a + 8 (r / 4) + 4 (lane / 32) + r % 4,
-  // column 64 wj + 32 b + lane % 32
-  float *Cg = C + (int64_t)g * K * K;
-  float *tr = gs;  // [kGT][kGT + 1]: the tile, for the transposed store
+  // accumulator r of block (a, b): LDS rows 64 wi + 32 a + 8 (r / 4) +
+  // 4 (lane / 32) + r % 4 and 64 wj + 32 b + lane % 32, i.e. the features
+  // g3_feature() of those; the tile [fi][fj] goes through LDS
+  float *tr = reinterpret_cast<float *>(g3);  // [kGT][kGT + 1]
 #pragma unroll
   for (int a = 0; a < 2; ++a)
 #pragma unroll
@@ -391,16 +430,21 @@ __global__ __launch_bounds__(kThreads) void gram(const E *x, const float *mu, in
       for (int r = 0; r < 16; ++r) {
         const int il = 64 * wi + 32 * a + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
         const int jl = 64 * wj + 32 * b + (lane & 31);
-        if (i0 + il < K && j0 + jl < K) Cg[(int64_t)(i0 + il) * K + j0 + jl] = acc[a][b][r];
-        if (!diag) tr[il * (kGT + 1) + jl] = acc[a][b][r];
+        tr[g3_feature(il) * (kGT + 1) + g3_feature(jl)] = acc[a][b][r];
       }
-  if (diag) return;  // workgroup-uniform
   __syncthreads();
+  float *Cg = C + (int64_t)g * K * K;
+  for (int e = tid; e < kGT * kGT; e += kThreads) {
+    const int il = e / kGT, jl = e % kGT;  // C[i][j], consecutive j per lane
+    if (i0 + il < K && j0 + jl < K) Cg[(int64_t)(i0 + il) * K + j0 + jl] = tr[il * (kGT + 1) + jl];
+  }
+  if (diag) return;  // workgroup-uniform
   for (int e = tid; e < kGT * kGT; e += kThreads) {
     const int jl = e / kGT, il = e % kGT;  // C[j][i] = tile[i][j], consecutive i per lane
     if (j0 + jl < K && i0 + il < K) Cg[(int64_t)(j0 + jl) * K + i0 + il] = tr[il * (kGT + 1) + jl];
   }
 }
+
 
 // mu[g][f] = (1/N) sum_n x[n][g][f] in fp64: a block covers 32 features;
 // its 8 row groups (n = r, r + 8, ...) sum in parallel and are added in a
@@ -858,10 +902,10 @@ static hipError_t run(const SvdParams &p, hipStream_t st) {
   // Gram matrix of the centred rows: C = Xc^T Xc  (K x K, contraction over N)
   if (K % 8 == 0 && ((uintptr_t)x & 15u) == 0) {  // whole 16-byte feature vectors
     const int T = (K + kGT - 1) / kGT;
-    LLA_TRY(hipFuncSetAttribute(reinterpret_cast<const void *>(gram<E>),
-                                hipFuncAttributeMaxDynamicSharedMemorySize, kGramLds));
-    hipLaunchKernelGGL(gram<E>, dim3((unsigned)(T * (T + 1) / 2), G), dim3(kThreads), kGramLds, st,
-                       x, p.mu, G, N, K, C);
+    LLA_TRY(hipFuncSetAttribute(reinterpret_cast<const void *>(gram3<E>),
+                                hipFuncAttributeMaxDynamicSharedMemorySize, kGram3Lds));
+    hipLaunchKernelGGL(gram3<E>, dim3((unsigned)(T * (T + 1) / 2), G), dim3(kThreads), kGram3Lds,
+                       st, x, p.mu, G, N, K, C);
     LLA_TRY(hipGetLastError());
   } else {
     LLA_TRY(launch_gemm(Centred<E, true>{x, p.mu, G, N, K}, Centred<E, false>{x, p.mu, G, N, K},
