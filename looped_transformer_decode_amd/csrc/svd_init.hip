@@ -25,6 +25,9 @@
 namespace lla {
 namespace svd {
 inline size_t align256_(size_t v) { return (v + 255) / 256 * 256; }
+// The small fp64 Gram products are formed in this many row ranges, whose
+// partial m x m matrices their consumers add as they load them.
+constexpr int kSmallGramParts = 4;
 }  // namespace svd
 
 SvdLayout svd_layout(int32_t G, int32_t K, int32_t m, int32_t r) {
@@ -38,7 +41,7 @@ SvdLayout svd_layout(int32_t G, int32_t K, int32_t m, int32_t r) {
   L.gram = take((size_t)G * K * K * 4);
   L.q = take((size_t)G * K * m * 4);
   L.y = take((size_t)G * K * m * 4);
-  L.small = take((size_t)G * m * m * 8);
+  L.small = take((size_t)G * m * m * 8 * svd::kSmallGramParts);
   L.rinv = take((size_t)G * m * m * 4);
   L.u = take((size_t)G * m * m * 8);
   L.evals = take((size_t)G * m * 8);
@@ -484,8 +487,10 @@ __global__ __launch_bounds__(kThreads) void start_block(float *Q, int64_t n) {
     Q[i] = start_value((uint64_t)i);
 }
 
-// out[g][i][j] = sum_k P[g][k][i] * R[g][k][j] in fp64 (P, R: [K][m] fp32).
-// Block = (32 x 32 output tile, g), eight waves: wave w multiplies quadrant
+// out[part][g][i][j] = sum over the part's rows k of P[g][k][i] * R[g][k][j]
+// in fp64 (P, R: [K][m] fp32; parts of kSmallGramParts row ranges, so that
+// a few codecs still fill the GPU; the consumers add the parts in order).
+// Block = (32 x 32 output tile, g and part), eight waves: wave w multiplies quadrant
 // w % 4 over half w / 4 of every chunk of 64 k, one v_mfma_f64_16x16x4f64
 // per four k (fp32 products are exact in fp64, the sums are fp64); the two
 // halves are added through LDS at the end.  Chunks are staged in LDS as
@@ -506,7 +511,12 @@ __global__ __launch_bounds__(kSgThreads) void small_gram64(const float *P, const
   if (sym && blockIdx.y > blockIdx.x) return;
   __shared__ float As[2][kSgK][kSgT + 1], Bs[2][kSgK][kSgT + 1];
   __shared__ double part[4][4][64];
-  const int g = blockIdx.z, i0 = blockIdx.y * kSgT, j0 = blockIdx.x * kSgT;
+  const int g = blockIdx.z / kSmallGramParts, sp = blockIdx.z % kSmallGramParts;
+  const int i0 = blockIdx.y * kSgT, j0 = blockIdx.x * kSgT;
+  // this part's rows [kb, ke), whole chunks of kSgK (an empty range writes zeros)
+  const int span = ((K + kSmallGramParts - 1) / kSmallGramParts + kSgK - 1) / kSgK * kSgK;
+  const int kb = sp * span, ke = min(K, kb + span);
+  out += (int64_t)sp * (gridDim.z / kSmallGramParts) * m * m;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, kl = lane >> 4;
   const int qi = (wave >> 1) & 1, qj = wave & 1, kh = wave >> 2;
   const float *Pg = P + (int64_t)g * K * m, *Rg = R + (int64_t)g * K * m;
@@ -515,8 +525,8 @@ __global__ __launch_bounds__(kSgThreads) void small_gram64(const float *P, const
 #pragma unroll
     for (int q = 0; q < kSgPer; ++q) {
       const int e = tid + kSgThreads * q, kk = k0 + e / kSgT, c = e % kSgT;
-      ra[q] = kk < K && i0 + c < m ? Pg[(int64_t)kk * m + i0 + c] : 0.f;
-      rb[q] = kk < K && j0 + c < m ? Rg[(int64_t)kk * m + j0 + c] : 0.f;
+      ra[q] = kk < ke && i0 + c < m ? Pg[(int64_t)kk * m + i0 + c] : 0.f;
+      rb[q] = kk < ke && j0 + c < m ? Rg[(int64_t)kk * m + j0 + c] : 0.f;
     }
   };
   auto stage = [&](int buf) {
@@ -528,12 +538,12 @@ __global__ __launch_bounds__(kSgThreads) void small_gram64(const float *P, const
     }
   };
   f64x4_t acc = {0.0, 0.0, 0.0, 0.0};
-  fetch(0);
+  fetch(kb);
   stage(0);
   __syncthreads();
   int buf = 0;
-  for (int k0 = 0; k0 < K; k0 += kSgK) {
-    const bool more = k0 + kSgK < K;
+  for (int k0 = kb; k0 < ke; k0 += kSgK) {
+    const bool more = k0 + kSgK < ke;
     if (more) fetch(k0 + kSgK);
 #pragma unroll
     for (int s = 0; s < kSgK / 8; ++s) {
@@ -592,17 +602,32 @@ __global__ __launch_bounds__(kCholThreads) void chol_inv(const double *A, int m,
   __shared__ double buf[2][Q * kCholT];
   const int g = blockIdx.x, tid = threadIdx.x, ty = tid / kCholT, tx = tid % kCholT;
   const double *Ag = A + (int64_t)g * m * m;
+  const int64_t pst = (int64_t)gridDim.x * m * m;  // between the small Gram parts
+  auto a_at = [&](int r, int c) {
+    double v = Ag[(int64_t)r * m + c];
+#pragma unroll
+    for (int sp = 1; sp < kSmallGramParts; ++sp) v += Ag[sp * pst + (int64_t)r * m + c];
+    return v;
+  };
   double v[Q][Q];
-  double dmax = 0.0;
-  for (int i = 0; i < m; ++i) dmax = fmax(dmax, Ag[(int64_t)i * m + i]);
-  const double shift = 1e-13 * dmax + 1e-300;
 #pragma unroll
   for (int a = 0; a < Q; ++a)
 #pragma unroll
     for (int b = 0; b < Q; ++b) {
       const int r = ty + kCholT * a, col = tx + kCholT * b;
-      v[a][b] = r < m && col <= r ? Ag[(int64_t)r * m + col] : 0.0;
+      v[a][b] = r < m && col <= r ? a_at(r, col) : 0.0;
     }
+  // the diagonal, from its owners (ty == tx, a == b), for the shift
+  if (ty == tx) {
+#pragma unroll
+    for (int a = 0; a < Q; ++a)
+      if (ty + kCholT * a < m) buf[0][ty + kCholT * a] = v[a][a];
+  }
+  __syncthreads();
+  double dmax = 0.0;
+  for (int i = 0; i < m; ++i) dmax = fmax(dmax, buf[0][i]);
+  const double shift = 1e-13 * dmax + 1e-300;
+  __syncthreads();  // step 0 publishes into the same buffer
   // j = 16 jo + jl: the block jo is a constant in each unrolled copy, so the
   // owners' slots are known and the finished column blocks b < jo (w = 0)
   // are skipped
@@ -694,9 +719,16 @@ __global__ __launch_bounds__(kJacThreads) void jacobi(const double *B, int m, in
   double *red = cs + 2 * npair;
   int *pr = reinterpret_cast<int *>(red + 2 * kJacWaves);
   const double *Bg = B + (int64_t)g * m * m;
+  const int64_t pst = (int64_t)gridDim.x * m * m;  // between the small Gram parts
+  auto b_at = [&](int i, int j) {
+    double v = Bg[i * m + j];
+#pragma unroll
+    for (int sp = 1; sp < kSmallGramParts; ++sp) v += Bg[sp * pst + i * m + j];
+    return v;
+  };
   for (int e = tid; e < mp * mp; e += kJacThreads) {
     const int i = e / mp, j = e % mp;
-    S[e] = i < m && j < m ? 0.5 * (Bg[i * m + j] + Bg[j * m + i]) : 0.0;  // exact symmetry
+    S[e] = i < m && j < m ? 0.5 * (b_at(i, j) + b_at(j, i)) : 0.0;  // exact symmetry
   }
   for (int e = tid; e < m * m; e += kJacThreads) U[e] = e / m == e % m ? 1.0 : 0.0;
   // this thread's column pair, and its first row pair / row of U
@@ -923,7 +955,7 @@ static hipError_t run(const SvdParams &p, hipStream_t st) {
   const void *jac = jac_u_lds ? reinterpret_cast<const void *>(jacobi<true>)
                               : reinterpret_cast<const void *>(jacobi<false>);
   LLA_TRY(hipFuncSetAttribute(jac, hipFuncAttributeMaxDynamicSharedMemorySize, (int)jac_lds));
-  const dim3 sg_grid((m + kSgT - 1) / kSgT, (m + kSgT - 1) / kSgT, G);
+  const dim3 sg_grid((m + kSgT - 1) / kSgT, (m + kSgT - 1) / kSgT, G * kSmallGramParts);
   // C is symmetric: its rows are read as columns (coalesced)
   const MatF32 Ct = mat(C, (int64_t)K * K, 1, K, K, K);
   // dst = C src (C symmetric, so its rows serve as the k-major left operand)
