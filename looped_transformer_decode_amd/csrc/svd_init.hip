@@ -698,7 +698,7 @@ __global__ __launch_bounds__(kCholThreads) void chol_inv(const double *A, int m,
 // when both matrices fit (kLdsU), else in the workspace.  Writes the
 // eigenvalues, the order that sorts them descending (ties by index), and
 // Usel[k][j] = U[k][order[j]] (j < r, fp32) for the final GEMM.
-constexpr int kJacThreads = 512;
+constexpr int kJacThreads = 1024;
 constexpr int kJacWaves = kJacThreads / 64;
 __host__ __device__ constexpr size_t jacobi_lds(int m, bool lds_u) {
   return (size_t)(m + (m & 1)) * (m + (m & 1)) * 8 + (lds_u ? (size_t)m * m * 8 : 0) +
