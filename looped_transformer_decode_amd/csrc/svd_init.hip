@@ -452,6 +452,62 @@ __global__ __launch_bounds__(kThreads) void gram3(const E *x, const float *mu, i
 // mu[g][f] = (1/N) sum_n x[n][g][f] in fp64: a block covers 32 features;
 // its 8 row groups (n = r, r + 8, ...) sum in parallel and are added in a
 // fixed order at the end.
+// mu[g][f] = (1/N) sum_n x[n][g][f] (fp64 sums) for rows of whole 16-byte
+// vectors: a block takes 64 features of one codec; its threads read one
+// vector of a row each (the block's rows 128 contiguous bytes), row groups
+// of a block take every (256 / vectors per row)-th row, four rows in flight,
+// with one fp64 sum per feature, and the groups' sums are added through LDS
+// in a fixed order.
+constexpr int kMeanVF = 64;  // features per block
+template <typename E>
+__global__ __launch_bounds__(kThreads) void column_mean_vec(const E *x, int G, int N, int K,
+                                                            float *mu) {
+  constexpr int VEC = 16 / (int)sizeof(E);   // features per 16-byte vector
+  constexpr int VPR = kMeanVF / VEC;         // vectors per row of the block
+  constexpr int RG = kThreads / VPR;         // row groups
+  __shared__ double part[RG][kMeanVF];
+  const int g = blockIdx.y, v = threadIdx.x % VPR, rg = threadIdx.x / VPR;
+  const int f0 = blockIdx.x * kMeanVF + v * VEC;
+  const bool ok = f0 < K;  // K % VEC == 0: whole vectors in or out
+  double s[VEC];
+#pragma unroll
+  for (int e = 0; e < VEC; ++e) s[e] = 0.0;
+  auto add = [&](const u32x4_v &w) {
+    if constexpr (sizeof(E) == 2) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        s[2 * e] += (double)bf16_lo(w[e]);
+        s[2 * e + 1] += (double)bf16_hi(w[e]);
+      }
+    } else {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) s[e] += (double)__uint_as_float(w[e]);
+    }
+  };
+  if (ok) {
+    const u32x4_v *base = reinterpret_cast<const u32x4_v *>(x + (int64_t)g * K + f0);
+    const int64_t rs = (int64_t)G * K / VEC;  // 16-byte words per row
+    int n = rg;
+    for (; n + 3 * RG < N; n += 4 * RG) {
+      u32x4_v w[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) w[u] = base[(int64_t)(n + u * RG) * rs];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) add(w[u]);
+    }
+    for (; n < N; n += RG) add(base[(int64_t)n * rs]);
+  }
+#pragma unroll
+  for (int e = 0; e < VEC; ++e) part[rg][v * VEC + e] = s[e];
+  __syncthreads();
+  if (threadIdx.x < kMeanVF) {
+    const int f = blockIdx.x * kMeanVF + threadIdx.x;
+    double t = 0.0;
+    for (int r = 0; r < RG; ++r) t += part[r][threadIdx.x];
+    if (f < K) mu[(int64_t)g * K + f] = (float)(t / N);
+  }
+}
+
 constexpr int kMeanF = 32, kMeanR = kThreads / kMeanF;
 template <typename E>
 __global__ __launch_bounds__(kThreads) void column_mean(const E *x, int G, int N, int K, float *mu) {
@@ -928,8 +984,12 @@ static hipError_t run(const SvdParams &p, hipStream_t st) {
 #define LLA_TRY(call)                   \
   if ((e = (call)) != hipSuccess) return e;
 
-  hipLaunchKernelGGL(column_mean<E>, dim3((K + kMeanF - 1) / kMeanF, G), dim3(kThreads), 0, st,
-                     x, G, N, K, p.mu);
+  if (K % (16 / (int)sizeof(E)) == 0 && ((uintptr_t)x & 15u) == 0)  // rows of 16-byte vectors
+    hipLaunchKernelGGL(column_mean_vec<E>, dim3((K + kMeanVF - 1) / kMeanVF, G), dim3(kThreads), 0,
+                       st, x, G, N, K, p.mu);
+  else
+    hipLaunchKernelGGL(column_mean<E>, dim3((K + kMeanF - 1) / kMeanF, G), dim3(kThreads), 0, st,
+                       x, G, N, K, p.mu);
   LLA_TRY(hipGetLastError());
   // Gram matrix of the centred rows: C = Xc^T Xc  (K x K, contraction over N)
   if (K % 8 == 0 && ((uintptr_t)x & 15u) == 0) {  // whole 16-byte feature vectors
