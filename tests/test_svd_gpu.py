@@ -144,6 +144,26 @@ def test_edge_cases(device, n, K, r):
     assert np.abs(sig[0][:k] - osig[:k]).max() <= 1e-4 * osig[0]
 
 
+def test_bf16_stack_not_multiple_of_8(device):
+    """bf16 rows whose stack length (K = 12) is not a whole number of 16-byte
+    vectors: the column means and the Gram matrix then take their
+    element-wise forms."""
+    T, width, r, n = 2, 6, 5, 120
+    K = T * width
+    rng = np.random.default_rng(12)
+    x = gen.as_storage(rng.standard_normal((n, 1, K)) * 2 + 1, "bf16")[1]
+    say(f"[svd] bf16 K={K} r={r} n={n}")
+    mu, wd, wu, sig = run_init(x, "bf16", 1, T, width, r, device)
+    omu, oW, oUp, osig = O.svd_init(x[:, 0], T, width, r)
+    assert np.abs(mu[0] - omu).max() <= 1e-5 * (np.abs(omu).max() + 1e-3)
+    assert np.abs(wd[0].T @ wd[0] - np.eye(r)).max() < 2e-2  # bf16 W_down
+    assert np.abs(sig[0] - osig).max() <= 1e-4 * osig[0]
+    e_gpu = O.codec_error(x[:, 0], mu[0], wd[0], [wd[0][t * width:(t + 1) * width] for t in range(T)])
+    e_opt = O.codec_error(x[:, 0], omu, oW, oUp)
+    say(f"    codec error {e_gpu:.4e} (optimum {e_opt:.4e})")
+    assert e_gpu <= e_opt * (1 + 2e-2) + 1e-6  # W_down rounded to bf16
+
+
 @pytest.mark.parametrize("r", [101, 79], ids=["block_117_odd", "block_95_odd"])
 def test_large_odd_block(device, r):
     """Iterated blocks of odd order beyond what the small cases reach:
