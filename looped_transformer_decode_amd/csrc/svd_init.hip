@@ -156,25 +156,33 @@ __global__ __launch_bounds__(kThreads) void gemm(LA A, LB B, float *C, int64_t c
 // chains.  Chunks of 32 k are staged in LDS as 16-byte vectors, the next
 // chunk loaded into registers while the current one is multiplied.
 typedef float f32x4_v __attribute__((ext_vector_type(4)));
-constexpr int kTnRows = 128;
 constexpr int kTnK = 32;
-template <int NB>
+// RW row tiles of 32 per block (4, or 2 for narrow products, which then run
+// more blocks per CU); the 4 / RW waves of a row tile share its NB column
+// tiles.
+template <int NB, int RW>
 struct TnCfg {
+  static constexpr int ROWS = 32 * RW;                     // rows of the block
+  static constexpr int WPR = 4 / RW;                       // waves per row tile
+  static constexpr int NBW = NB / WPR;                     // column tiles per wave
   static constexpr int NC = 32 * NB;                       // columns of the block
   // LDS row pitches (floats), 32 banks apart modulo 64: the two k rows one
   // operand read touches (lanes 0-31, 32-63) fall in disjoint banks
-  static constexpr int AP = kTnRows + 32, BP = NC + (NC % 64 == 32 ? 0 : 32);
-  static constexpr int AV = kTnK * kTnRows / 4 / kThreads; // A vectors per thread and chunk
+  static constexpr int AP = ROWS + (ROWS % 64 == 32 ? 0 : 32), BP = NC + (NC % 64 == 32 ? 0 : 32);
+  static constexpr int AV = kTnK * ROWS / 4 / kThreads;    // A vectors per thread and chunk
   static constexpr int BV = (kTnK * NC / 4 + kThreads - 1) / kThreads;
   static constexpr int LDS = 2 * kTnK * (AP + BP) * 4;
-  static_assert(AV * kThreads * 4 == kTnK * kTnRows, "A load split");
+  static_assert(AV * kThreads * 4 == kTnK * ROWS, "A load split");
+  static_assert(NBW * WPR == NB, "column tiles split evenly over a row tile's waves");
 };
-template <int NB>
+template <int NB, int RW>
 __global__ __launch_bounds__(kThreads) void gemm_tn(const float *X, int64_t x_sg, int ldx,
                                                     const float *Y, int64_t y_sg, int ldy,
                                                     float *C, int64_t c_sg, int ldc, int M,
                                                     int Nn, int Kd) {
-  using T = TnCfg<NB>;
+  using T = TnCfg<NB, RW>;
+  constexpr int kTnRows = T::ROWS;
+  const int wr = (threadIdx.x >> 6) / T::WPR, wc = (threadIdx.x >> 6) % T::WPR;
   extern __shared__ __align__(16) float tn[];
   float *As = tn;                          // [2][kTnK][AP]
   float *Bs = tn + 2 * kTnK * T::AP;       // [2][kTnK][BP]
@@ -211,9 +219,9 @@ __global__ __launch_bounds__(kThreads) void gemm_tn(const float *X, int64_t x_sg
         *reinterpret_cast<f32x4_v *>(Bs + (buf * kTnK + kk) * T::BP + c4) = rb[q];
     }
   };
-  f32x16_t acc[NB];
+  f32x16_t acc[T::NBW];
 #pragma unroll
-  for (int nb = 0; nb < NB; ++nb) acc[nb] = f32x16_t{};
+  for (int nb = 0; nb < T::NBW; ++nb) acc[nb] = f32x16_t{};
   fetch(0);
   stage(0);
   __syncthreads();
@@ -221,15 +229,15 @@ __global__ __launch_bounds__(kThreads) void gemm_tn(const float *X, int64_t x_sg
   for (int k0 = 0; k0 < Kd; k0 += kTnK) {
     const bool more = k0 + kTnK < Kd;
     if (more) fetch(k0 + kTnK);
-    const float *Ab = As + buf * kTnK * T::AP + 32 * wave + (lane & 31);
-    const float *Bb = Bs + buf * kTnK * T::BP + (lane & 31);
+    const float *Ab = As + buf * kTnK * T::AP + 32 * wr + (lane & 31);
+    const float *Bb = Bs + buf * kTnK * T::BP + 32 * T::NBW * wc + (lane & 31);
 #pragma unroll
     for (int kk = 0; kk < kTnK; kk += 2) {
       // A: row 32 wave + lane % 32, k = kk + lane / 32;  B: column 32 nb + lane % 32
       const int kr = kk + (lane >> 5);
       const float a = Ab[kr * T::AP];
 #pragma unroll
-      for (int nb = 0; nb < NB; ++nb)
+      for (int nb = 0; nb < T::NBW; ++nb)
         acc[nb] = __builtin_amdgcn_mfma_f32_32x32x2f32(a, Bb[kr * T::BP + 32 * nb], acc[nb], 0, 0,
                                                        0);
     }
@@ -239,12 +247,12 @@ __global__ __launch_bounds__(kThreads) void gemm_tn(const float *X, int64_t x_sg
   }
   // accumulator r: row 8 (r / 4) + 4 (lane / 32) + r % 4, column lane % 32
 #pragma unroll
-  for (int nb = 0; nb < NB; ++nb) {
-    const int j = 32 * nb + (lane & 31);
+  for (int nb = 0; nb < T::NBW; ++nb) {
+    const int j = 32 * (T::NBW * wc + nb) + (lane & 31);
     if (j >= Nn) continue;
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
-      const int i = i0 + 32 * wave + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+      const int i = i0 + 32 * wr + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
       if (i < M) C[g * c_sg + (int64_t)i * ldc + j] = acc[nb][r];
     }
   }
@@ -934,16 +942,16 @@ hipError_t launch_gemm(const LA &A, const LB &B, float *C, int64_t c_sg, int ldc
   return hipGetLastError();
 }
 
-template <int NB>
+template <int NB, int RW = 4>
 hipError_t launch_gemm_tn_nb(const float *X, int64_t x_sg, int ldx, const float *Y, int64_t y_sg,
                              int ldy, float *C, int64_t c_sg, int ldc, int G, int M, int Nn,
                              int Kd, hipStream_t st) {
-  const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(gemm_tn<NB>),
-                                           hipFuncAttributeMaxDynamicSharedMemorySize,
-                                           TnCfg<NB>::LDS);
+  using T = TnCfg<NB, RW>;
+  const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(gemm_tn<NB, RW>),
+                                           hipFuncAttributeMaxDynamicSharedMemorySize, T::LDS);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(gemm_tn<NB>, dim3((M + kTnRows - 1) / kTnRows, G), dim3(kThreads),
-                     TnCfg<NB>::LDS, st, X, x_sg, ldx, Y, y_sg, ldy, C, c_sg, ldc, M, Nn, Kd);
+  hipLaunchKernelGGL((gemm_tn<NB, RW>), dim3((M + T::ROWS - 1) / T::ROWS, G), dim3(kThreads),
+                     T::LDS, st, X, x_sg, ldx, Y, y_sg, ldy, C, c_sg, ldc, M, Nn, Kd);
   return hipGetLastError();
 }
 // Needs M, Nn, ldx, ldy multiples of 4, 16-byte aligned X and Y, Nn <= 128.
@@ -952,7 +960,8 @@ hipError_t launch_gemm_tn(const float *X, int64_t x_sg, int ldx, const float *Y,
                           hipStream_t st) {
   const int nb = (Nn + 31) / 32;
   if (nb <= 1) return launch_gemm_tn_nb<1>(X, x_sg, ldx, Y, y_sg, ldy, C, c_sg, ldc, G, M, Nn, Kd, st);
-  if (nb == 2) return launch_gemm_tn_nb<2>(X, x_sg, ldx, Y, y_sg, ldy, C, c_sg, ldc, G, M, Nn, Kd, st);
+  if (nb == 2)
+    return launch_gemm_tn_nb<2, 2>(X, x_sg, ldx, Y, y_sg, ldy, C, c_sg, ldc, G, M, Nn, Kd, st);
   if (nb == 3) return launch_gemm_tn_nb<3>(X, x_sg, ldx, Y, y_sg, ldy, C, c_sg, ldc, G, M, Nn, Kd, st);
   return launch_gemm_tn_nb<4>(X, x_sg, ldx, Y, y_sg, ldy, C, c_sg, ldc, G, M, Nn, Kd, st);
 }
